@@ -1,0 +1,49 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module holds no attention arithmetic: only the random draw and the
+float32 -> bf16 encoding. Recipe: ``numpy.random.default_rng(seed)`` (PCG64),
+``standard_normal(shape, dtype=float32)`` drawn in the order Q, K, V, dO, each
+over its whole contiguous [B][H][S][D] tensor, then rounded to bf16 with
+round-to-nearest-even on the bit pattern.
+"""
+import numpy as np
+
+
+def bf16_bits(x):
+    """float32 array -> uint16 bf16 bit patterns, round to nearest even (NaN stays NaN)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = np.isnan(x)
+    out = rounded.astype(np.uint16)
+    if nan.any():
+        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return out
+
+
+def bf16_to_f32(bits):
+    """uint16 bf16 bit patterns -> float32 (exact)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def qkv(B, Hq, Hkv, S, D, seed=0, with_dout=False):
+    """Q [B,Hq,S,D], K and V [B,Hkv,S,D] (and dO like Q) as bf16 bits, iid N(0,1)."""
+    rng = np.random.default_rng(seed)
+    q = bf16_bits(rng.standard_normal((B, Hq, S, D), dtype=np.float32))
+    k = bf16_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32))
+    v = bf16_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32))
+    if not with_dout:
+        return q, k, v
+    dout = bf16_bits(rng.standard_normal((B, Hq, S, D), dtype=np.float32))
+    return q, k, v, dout
+
+
+# The workloads the benchmark and the parity tests run: (name, B, Hq, Hkv, S, D, causal, pass).
+CONFIGS = {
+    "single_head_s128_d64": dict(B=1, Hq=1, Hkv=1, S=128, D=64, causal=False, bwd=False),
+    "llama8b_causal_gqa_s4096": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, bwd=False),
+    "long_causal_gqa_s8192": dict(B=2, Hq=32, Hkv=8, S=8192, D=128, causal=True, bwd=False),
+    "mha_noncausal_s2048_d64": dict(B=8, Hq=16, Hkv=16, S=2048, D=64, causal=False, bwd=False),
+    "llama8b_causal_gqa_s4096_bwd": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, bwd=True),
+}

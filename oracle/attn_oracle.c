@@ -1,0 +1,317 @@
+/*
+ * Plain fp64 CPU oracle for scaled dot-product attention and its exact gradient.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the package's smoke() check and
+ * the CPU-baseline leg of the benchmark may load this library. The product path
+ * (the HIP kernels and their C ABI) never calls it, shares no code, header,
+ * table or helper with it, and must fail loudly when its own library is missing.
+ *
+ * What it computes follows "Scheduling Data to Compute: Hierarchical Data
+ * Pipelining for LLM Training on AMD GPUs" (Rao et al.), section 2.1, Eq. (1):
+ * O = softmax(Q K^T * scale) V, one row of Q at a time, written out naively in
+ * double precision with no tiling, no fusion and no reordering. The backward
+ * pass is the exact gradient of Eq. (1); the same section's Table 3 lists the
+ * two products it contains (dQ = dS K and dK = dS^T Q). Readings of the page
+ * where it is silent:
+ *   - scale is an argument (the page uses 1/sqrt(d));
+ *   - causal: key j is visible to query i iff j <= i (query and key lengths equal);
+ *   - grouped-query attention: query head hq reads key/value head hq / (Hq/Hkv);
+ *   - lse_i = m_i + ln(sum_j exp(s_ij - m_i)), natural log; subtracting the row
+ *     maximum m_i is an exact rescaling, not an approximation;
+ *   - dK and dV of a key/value head are summed over every query head that reads it.
+ *
+ * Layout: contiguous [B][H][S][D]; inputs are bf16 bit patterns (uint16),
+ * widened exactly to double; every output is double.
+ * All functions return 0 on success and a negative value on bad arguments.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    int B, Hq, Hkv, S, D, G, causal;
+    double scale;
+} ctx_t;
+
+static double widen(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int check_args(int B, int Hq, int Hkv, int S, int D) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return -1;
+    if (Hq % Hkv != 0) return -2;
+    return 0;
+}
+
+static size_t qrow_off(const ctx_t* c, int b, int hq, int i) {
+    return (((size_t)b * c->Hq + hq) * c->S + i) * (size_t)c->D;
+}
+static size_t kvrow_off(const ctx_t* c, int b, int hkv, int j) {
+    return (((size_t)b * c->Hkv + hkv) * c->S + j) * (size_t)c->D;
+}
+
+static double dot_bf16(const uint16_t* x, const uint16_t* y, int D) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += widen(x[d]) * widen(y[d]);
+    return s;
+}
+
+/* Number of keys query row i sees: all S, or i+1 when causal. */
+static int visible(const ctx_t* c, int i) { return c->causal ? i + 1 : c->S; }
+
+/*
+ * One query row of Eq. (1): scores s_j = scale * q_i . k_j over the visible
+ * keys, their softmax P_j, and optionally O_i = sum_j P_j v_j and
+ * lse_i = m + ln(l). If dout is set, also the row's backward quantities:
+ * dP_j = dO_i . v_j, delta_i = sum_j P_j dP_j, dS_j = P_j (dP_j - delta_i),
+ * dQ_i = scale * sum_j dS_j k_j.  `p` and `dp` are caller scratch of length S.
+ */
+static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
+                    double* o_out, double* lse_out, double* delta_out, double* dq_out) {
+    const int D = c->D, n = visible(c, i), hkv = hq / c->G;
+    const uint16_t* qi = c->q + qrow_off(c, b, hq, i);
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+        p[j] = c->scale * dot_bf16(qi, c->k + kvrow_off(c, b, hkv, j), D);
+        if (p[j] > m) m = p[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+    }
+    for (int j = 0; j < n; ++j) p[j] /= l;
+    if (lse_out) *lse_out = m + log(l);
+    if (o_out) {
+        for (int d = 0; d < D; ++d) o_out[d] = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j);
+            for (int d = 0; d < D; ++d) o_out[d] += p[j] * widen(vj[d]);
+        }
+    }
+    if (c->dout && (delta_out || dq_out)) {
+        const uint16_t* doi = c->dout + qrow_off(c, b, hq, i);
+        double delta = 0.0;
+        for (int j = 0; j < n; ++j) {
+            dp[j] = dot_bf16(doi, c->v + kvrow_off(c, b, hkv, j), D);
+            delta += p[j] * dp[j];
+        }
+        if (delta_out) *delta_out = delta;
+        if (dq_out) {
+            for (int d = 0; d < D; ++d) dq_out[d] = 0.0;
+            for (int j = 0; j < n; ++j) {
+                const double ds = p[j] * (dp[j] - delta);
+                const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j);
+                for (int d = 0; d < D; ++d) dq_out[d] += c->scale * ds * widen(kj[d]);
+            }
+        }
+    }
+}
+
+/*
+ * Gradient of one key/value row j of head group (b, hkv): for every query head
+ * hq that reads this group and every query row i that sees key j,
+ *   P_ij = exp(scale q_i.k_j - lse_i),  dP_ij = dO_i . v_j,
+ *   dV_j += P_ij dO_i,   dK_j += scale * P_ij (dP_ij - delta_i) q_i.
+ * lse and delta are the per-row values of one_row for the group's query heads,
+ * indexed [g][i] with g = hq - hkv*G.
+ */
+static void one_key(const ctx_t* c, int b, int hkv, int j, const double* lse,
+                    const double* delta, double* dk_out, double* dv_out) {
+    const int D = c->D, S = c->S;
+    const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j);
+    const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j);
+    for (int d = 0; d < D; ++d) { dk_out[d] = 0.0; dv_out[d] = 0.0; }
+    for (int g = 0; g < c->G; ++g) {
+        const int hq = hkv * c->G + g;
+        for (int i = c->causal ? j : 0; i < S; ++i) {
+            const uint16_t* qi = c->q + qrow_off(c, b, hq, i);
+            const uint16_t* doi = c->dout + qrow_off(c, b, hq, i);
+            const double pij = exp(c->scale * dot_bf16(qi, kj, D) - lse[(size_t)g * S + i]);
+            const double dpij = dot_bf16(doi, vj, D);
+            const double ds = pij * (dpij - delta[(size_t)g * S + i]);
+            for (int d = 0; d < D; ++d) {
+                dv_out[d] += pij * widen(doi[d]);
+                dk_out[d] += c->scale * ds * widen(qi[d]);
+            }
+        }
+    }
+}
+
+static void init_ctx(ctx_t* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const uint16_t* dout, int B, int Hq, int Hkv, int S, int D, int causal,
+                     double scale) {
+    c->q = q; c->k = k; c->v = v; c->dout = dout;
+    c->B = B; c->Hq = Hq; c->Hkv = Hkv; c->S = S; c->D = D; c->G = Hq / Hkv;
+    c->causal = causal ? 1 : 0;
+    c->scale = scale;
+}
+
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* Forward over every row: o [B][Hq][S][D], lse [B][Hq][S]. */
+int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* o,
+                    double* lse, int B, int Hq, int Hkv, int S, int D, int causal,
+                    double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D);
+    if (rc) return rc;
+    ctx_t c;
+    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, scale);
+    const long long rows = (long long)B * Hq * S;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 16)
+        for (long long r = 0; r < rows; ++r) {
+            const int i = (int)(r % S), bh = (int)(r / S);
+            one_row(&c, bh / Hq, bh % Hq, i, p, NULL, o + (size_t)r * D, lse + r, NULL, NULL);
+        }
+        free(p);
+    }
+    return 0;
+}
+
+/* Forward for selected rows only; rows[n] are flat indices (b*Hq + hq)*S + i.
+ * o_rows [n][D], lse_rows [n]. */
+int oracle_attn_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int64_t* rows, int64_t n, double* o_rows, double* lse_rows,
+                         int B, int Hq, int Hkv, int S, int D, int causal, double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D);
+    if (rc) return rc;
+    for (int64_t t = 0; t < n; ++t)
+        if (rows[t] < 0 || rows[t] >= (int64_t)B * Hq * S) return -3;
+    ctx_t c;
+    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, scale);
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n; ++t) {
+            const int64_t r = rows[t];
+            const int i = (int)(r % S), bh = (int)(r / S);
+            one_row(&c, bh / Hq, bh % Hq, i, p, NULL, o_rows + (size_t)t * D, lse_rows + t,
+                    NULL, NULL);
+        }
+        free(p);
+    }
+    return 0;
+}
+
+/* Per-row lse and delta for every query head of group (b, hkv): [G][S] each. */
+static void group_row_stats(const ctx_t* c, int b, int hkv, double* lse, double* delta) {
+    const int S = c->S, G = c->G;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)S);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 8)
+        for (long long r = 0; r < (long long)G * S; ++r) {
+            const int g = (int)(r / S), i = (int)(r % S);
+            one_row(c, b, hkv * G + g, i, p, dp, NULL, lse + r, delta + r, NULL);
+        }
+        free(p);
+        free(dp);
+    }
+}
+
+/* Full backward: dq [B][Hq][S][D]; dk, dv [B][Hkv][S][D] (summed over the group). */
+int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const uint16_t* dout, double* dq, double* dk, double* dv, int B, int Hq,
+                    int Hkv, int S, int D, int causal, double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D);
+    if (rc) return rc;
+    ctx_t c;
+    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, scale);
+    const int G = c.G;
+    const long long rows = (long long)B * Hq * S;
+    double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)rows);
+    if (!lse || !delta) { free(lse); free(delta); return -4; }
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)S);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 16)
+        for (long long r = 0; r < rows; ++r) {
+            const int i = (int)(r % S), bh = (int)(r / S);
+            one_row(&c, bh / Hq, bh % Hq, i, p, dp, NULL, lse + r, delta + r,
+                    dq + (size_t)r * D);
+        }
+        free(p);
+        free(dp);
+    }
+    const long long keys = (long long)B * Hkv * S;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long long r = 0; r < keys; ++r) {
+        const int j = (int)(r % S), bh = (int)(r / S);
+        const int b = bh / Hkv, hkv = bh % Hkv;
+        /* the group's query heads are hkv*G .. hkv*G+G-1, contiguous in [Hq] */
+        const size_t base = ((size_t)b * Hq + (size_t)hkv * G) * S;
+        one_key(&c, b, hkv, j, lse + base, delta + base, dk + (size_t)r * D, dv + (size_t)r * D);
+    }
+    free(lse);
+    free(delta);
+    return 0;
+}
+
+/*
+ * Backward for selected rows only. qrows[nq]: flat query rows (b*Hq+hq)*S+i,
+ * giving dq_rows [nq][D]. kvrows[nkv]: flat key rows (b*Hkv+hkv)*S+j, giving
+ * dk_rows, dv_rows [nkv][D]. Every query row of each group that a selected key
+ * belongs to is visited once for its lse and delta.
+ */
+int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, const int64_t* qrows, int64_t nq, double* dq_rows,
+                         const int64_t* kvrows, int64_t nkv, double* dk_rows, double* dv_rows,
+                         int B, int Hq, int Hkv, int S, int D, int causal, double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D);
+    if (rc) return rc;
+    for (int64_t t = 0; t < nq; ++t)
+        if (qrows[t] < 0 || qrows[t] >= (int64_t)B * Hq * S) return -3;
+    for (int64_t t = 0; t < nkv; ++t)
+        if (kvrows[t] < 0 || kvrows[t] >= (int64_t)B * Hkv * S) return -3;
+    ctx_t c;
+    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, scale);
+    const int G = c.G;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)S);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < nq; ++t) {
+            const int64_t r = qrows[t];
+            const int i = (int)(r % S), bh = (int)(r / S);
+            one_row(&c, bh / Hq, bh % Hq, i, p, dp, NULL, NULL, NULL, dq_rows + (size_t)t * D);
+        }
+        free(p);
+        free(dp);
+    }
+    if (nkv == 0) return 0;
+    double* lse = (double*)malloc(sizeof(double) * (size_t)G * S);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)G * S);
+    if (!lse || !delta) { free(lse); free(delta); return -4; }
+    /* visit groups in the order they first appear; recompute stats per group */
+    int64_t done_group = -1;
+    for (int64_t t = 0; t < nkv; ++t) {
+        const int64_t grp = kvrows[t] / S;
+        if (grp == done_group) continue;
+        const int b = (int)(grp / Hkv), hkv = (int)(grp % Hkv);
+        group_row_stats(&c, b, hkv, lse, delta);
+        done_group = grp;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t u = t; u < nkv; ++u) {
+            if (kvrows[u] / S != grp) continue;
+            one_key(&c, b, hkv, (int)(kvrows[u] % S), lse, delta, dk_rows + (size_t)u * D,
+                    dv_rows + (size_t)u * D);
+        }
+    }
+    free(lse);
+    free(delta);
+    return 0;
+}

@@ -1,0 +1,268 @@
+"""Checks that pin the fp64 oracle to facts other than its own code.
+
+Each check takes an oracle object (``oracle.Oracle``) and raises AssertionError
+when the oracle disagrees with the fact. The facts come from section 2.1 of
+Rao et al., "Scheduling Data to Compute: Hierarchical Data Pipelining for LLM
+Training on AMD GPUs" (Eq. (1): O = softmax(Q K^T / sqrt(d)) V) and from
+mathematics: an independent brute force on tiny inputs, closed forms,
+invariants, torch's float64 CPU attention and autograd as a library routine,
+and central finite differences for the gradient.
+
+The same checks run against deliberately broken copies of the oracle
+(tests/test_oracle.py) to show that each plausible mistake trips at least one.
+"""
+import math
+
+import numpy as np
+import torch
+
+from flashattention_tiled_attention_amd.inputs import bf16_bits, bf16_to_f32, qkv
+
+
+def _f64(bits):
+    return bf16_to_f32(bits).astype(np.float64)
+
+
+def _visible(causal, S, i):
+    return range(i + 1) if causal else range(S)
+
+
+def brute_force_fwd(q, k, v, causal, scale):
+    """Eq. (1) on tiny inputs in pure Python: exp(s)/sum(exp(s)) with math.fsum,
+    no max subtraction, no numpy linear algebra."""
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    B, Hq, S, D = q.shape
+    G = Hq // k.shape[1]
+    o = np.zeros((B, Hq, S, D))
+    lse = np.zeros((B, Hq, S))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i in range(S):
+                js = list(_visible(causal, S, i))
+                e = [math.exp(scale * math.fsum(qf[b, h, i, d] * kf[b, g, j, d] for d in range(D)))
+                     for j in js]
+                z = math.fsum(e)
+                lse[b, h, i] = math.log(z)
+                for d in range(D):
+                    o[b, h, i, d] = math.fsum(e[t] / z * vf[b, g, j, d] for t, j in enumerate(js))
+    return o, lse
+
+
+def _loss_py(qf, kf, vf, dof, causal, scale, G):
+    """L = sum(O * dO) of Eq. (1), float64 arrays in, pure Python out."""
+    B, Hq, S, D = qf.shape
+    total = []
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i in range(S):
+                js = list(_visible(causal, S, i))
+                s = [scale * float(np.dot(qf[b, h, i], kf[b, g, j])) for j in js]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = math.fsum(e)
+                for t, j in enumerate(js):
+                    total.append(e[t] / z * float(np.dot(vf[b, g, j], dof[b, h, i])))
+    return math.fsum(total)
+
+
+def _torch_ref(q, k, v, causal, scale, dout=None):
+    """torch float64 CPU scaled_dot_product_attention (+ autograd) as a library routine."""
+    G = q.shape[1] // k.shape[1]
+    tq = torch.from_numpy(_f64(q)).requires_grad_(dout is not None)
+    tk = torch.from_numpy(_f64(k)).requires_grad_(dout is not None)
+    tv = torch.from_numpy(_f64(v)).requires_grad_(dout is not None)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=bool(causal), scale=float(scale), enable_gqa=G > 1)
+    if dout is None:
+        return o.detach().numpy(), None
+    o.backward(torch.from_numpy(_f64(dout)))
+    return o.detach().numpy(), (tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy())
+
+
+def _close(a, b, tol, what):
+    err = float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+    assert err <= tol, "%s: max abs diff %.3e > %.1e" % (what, err, tol)
+
+
+# ---------------------------------------------------------------- forward pins
+
+def pin_brute_force(orc):
+    """Oracle forward equals the pure-Python brute force on tiny shapes."""
+    for (B, Hq, Hkv, S, D, causal, seed) in [(1, 1, 1, 5, 4, False, 1), (1, 2, 1, 7, 8, True, 2),
+                                             (2, 4, 2, 6, 3, False, 3), (1, 2, 2, 8, 5, True, 4)]:
+        q, k, v = qkv(B, Hq, Hkv, S, D, seed)
+        scale = 1.0 / math.sqrt(D)
+        o, lse = orc.fwd(q, k, v, causal, scale)
+        ob, lb = brute_force_fwd(q, k, v, causal, scale)
+        _close(o, ob, 1e-12, "O vs brute force %s" % ((B, Hq, Hkv, S, D, causal),))
+        _close(lse, lb, 1e-12, "lse vs brute force")
+
+
+def pin_torch_sdpa(orc):
+    """Oracle forward equals torch's float64 scaled_dot_product_attention."""
+    for (B, Hq, Hkv, S, D, causal, seed) in [(2, 4, 2, 33, 16, True, 5), (1, 3, 3, 40, 8, False, 6),
+                                             (1, 8, 2, 17, 64, True, 7)]:
+        q, k, v = qkv(B, Hq, Hkv, S, D, seed)
+        scale = 1.0 / math.sqrt(D)
+        o, _ = orc.fwd(q, k, v, causal, scale)
+        ot, _ = _torch_ref(q, k, v, causal, scale)
+        _close(o, ot, 1e-12, "O vs torch sdpa")
+
+
+def pin_single_key(orc):
+    """S=1: the single key gets weight 1, so O = V_0 and lse = scale * q.k_0."""
+    q, k, v = qkv(2, 4, 2, 1, 16, 11)
+    scale = 0.3
+    for causal in (False, True):
+        o, lse = orc.fwd(q, k, v, causal, scale)
+        vf = _f64(v)
+        _close(o, np.repeat(vf, 2, axis=1), 0.0, "S=1 O")
+        expect = scale * np.einsum("bhsd,bhsd->bhs", _f64(q), np.repeat(_f64(k), 2, axis=1))
+        _close(lse, expect, 1e-14, "S=1 lse")
+
+
+def pin_zero_query(orc):
+    """Q=0: all scores are 0, so O is the (prefix) mean of V and lse = ln(#visible keys)."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 9, 4
+    _, k, v = qkv(B, Hq, Hkv, S, D, 12)
+    q = np.zeros((B, Hq, S, D), np.uint16)
+    vf = _f64(v)
+    o, lse = orc.fwd(q, k, v, False, 0.125)
+    _close(o, np.broadcast_to(vf.mean(axis=2, keepdims=True), o.shape), 1e-14, "Q=0 O")
+    _close(lse, np.full(lse.shape, math.log(S)), 1e-14, "Q=0 lse")
+    o, lse = orc.fwd(q, k, v, True, 0.125)
+    prefix = np.cumsum(vf, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    _close(o, np.broadcast_to(prefix, o.shape), 1e-14, "Q=0 causal O")
+    _close(lse, np.broadcast_to(np.log(np.arange(1, S + 1.0)), lse.shape), 1e-14, "Q=0 causal lse")
+
+
+def pin_causal_first_row(orc):
+    """Causal row 0 sees only key 0: O_0 = V_0 exactly, lse_0 = scale q_0.k_0."""
+    q, k, v = qkv(1, 4, 4, 12, 8, 13)
+    o, lse = orc.fwd(q, k, v, True, 0.5)
+    _close(o[:, :, 0], _f64(v)[:, :, 0], 0.0, "causal row 0")
+    _close(lse[:, :, 0], 0.5 * np.einsum("bhd,bhd->bh", _f64(q)[:, :, 0], _f64(k)[:, :, 0]), 1e-14,
+           "causal row 0 lse")
+
+
+def pin_permutation(orc):
+    """Non-causal: permuting the key/value rows together leaves O and lse unchanged."""
+    q, k, v = qkv(1, 2, 2, 16, 8, 14)
+    perm = np.random.default_rng(0).permutation(16)
+    o1, l1 = orc.fwd(q, k, v, False, 0.35)
+    o2, l2 = orc.fwd(q, np.ascontiguousarray(k[:, :, perm]), np.ascontiguousarray(v[:, :, perm]),
+                     False, 0.35)
+    _close(o1, o2, 1e-13, "permuted O")
+    _close(l1, l2, 1e-13, "permuted lse")
+
+
+def pin_gqa_is_repeated_mha(orc):
+    """GQA with G query heads per key/value head equals MHA with each K/V head repeated
+    G times consecutively (query head h reads K/V head h // G)."""
+    q, k, v = qkv(2, 6, 2, 10, 8, 15)
+    for causal in (False, True):
+        o1, l1 = orc.fwd(q, k, v, causal, 0.4)
+        o2, l2 = orc.fwd(q, np.ascontiguousarray(np.repeat(k, 3, axis=1)),
+                         np.ascontiguousarray(np.repeat(v, 3, axis=1)), causal, 0.4)
+        _close(o1, o2, 0.0, "GQA vs repeated MHA")
+        _close(l1, l2, 0.0, "GQA lse")
+
+
+def pin_sharp_softmax(orc):
+    """A large scale with a unique maximum score concentrates all weight on its key."""
+    B, H, S, D = 1, 1, 6, 4
+    q = bf16_bits(np.array([[[[1, 0, 0, 0]] * S]], np.float32))
+    kf = np.zeros((B, H, S, D), np.float32)
+    kf[0, 0, :, 0] = [0.5, -1, 2, 0.25, 1, -2]   # key 2 has the unique largest score
+    _, _, v = qkv(B, H, H, S, D, 16)
+    o, lse = orc.fwd(q, bf16_bits(kf), v, False, 200.0)
+    _close(o[0, 0], np.broadcast_to(_f64(v)[0, 0, 2], (S, D)), 1e-30, "sharp softmax")
+    _close(lse, np.full(lse.shape, 400.0), 1e-12, "sharp lse")
+
+
+def pin_rows_match_full(orc):
+    """The sampled-row entry points agree exactly with the full ones."""
+    q, k, v, do = qkv(2, 4, 2, 24, 8, 17, with_dout=True)
+    for causal in (False, True):
+        o, lse = orc.fwd(q, k, v, causal, 0.3)
+        rows = np.array([0, 5, 23, 24, 77, 150, 191])
+        o_r, l_r = orc.fwd_rows(q, k, v, rows, causal, 0.3)
+        _close(o_r, o.reshape(-1, 8)[rows], 0.0, "fwd rows")
+        _close(l_r, lse.reshape(-1)[rows], 0.0, "fwd rows lse")
+        dq, dk, dv = orc.bwd(q, k, v, do, causal, 0.3)
+        kvr = np.array([0, 3, 23, 30, 47, 60, 95, 94])
+        dq_r, dk_r, dv_r = orc.bwd_rows(q, k, v, do, rows, kvr, causal, 0.3)
+        _close(dq_r, dq.reshape(-1, 8)[rows], 1e-15, "dq rows")
+        _close(dk_r, dk.reshape(-1, 8)[kvr], 1e-15, "dk rows")
+        _close(dv_r, dv.reshape(-1, 8)[kvr], 1e-15, "dv rows")
+
+
+# ---------------------------------------------------------------- backward pins
+
+def pin_finite_differences(orc):
+    """Analytic gradients equal central differences of L = sum(O * dO), where O comes
+    from an independent pure-Python forward evaluated at perturbed float64 inputs."""
+    h = 1e-6
+    for (B, Hq, Hkv, S, D, causal, seed) in [(1, 2, 1, 5, 3, True, 21), (1, 2, 2, 4, 3, False, 22)]:
+        q, k, v, do = qkv(B, Hq, Hkv, S, D, seed, with_dout=True)
+        scale = 0.7
+        dq, dk, dv = orc.bwd(q, k, v, do, causal, scale)
+        G = Hq // Hkv
+        base = [_f64(q), _f64(k), _f64(v)]
+        dof = _f64(do)
+        for which, grad in enumerate((dq, dk, dv)):
+            for idx in np.ndindex(*base[which].shape):
+                plus = [a.copy() for a in base]
+                minus = [a.copy() for a in base]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                fd = (_loss_py(*plus, dof, causal, scale, G) - _loss_py(*minus, dof, causal, scale, G)) / (2 * h)
+                assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), \
+                    "finite difference %s%s: fd %.9f analytic %.9f" % ("qkv"[which], idx, fd, grad[idx])
+
+
+def pin_torch_autograd(orc):
+    """Oracle gradients equal torch float64 autograd of scaled_dot_product_attention
+    (dK, dV summed over the query heads of each group)."""
+    for (B, Hq, Hkv, S, D, causal, seed) in [(2, 4, 2, 29, 16, True, 23), (1, 3, 3, 20, 8, False, 24),
+                                             (1, 8, 2, 13, 64, True, 25)]:
+        q, k, v, do = qkv(B, Hq, Hkv, S, D, seed, with_dout=True)
+        scale = 1.0 / math.sqrt(D)
+        dq, dk, dv = orc.bwd(q, k, v, do, causal, scale)
+        _, (tq, tk, tv) = _torch_ref(q, k, v, causal, scale, do)
+        _close(dq, tq, 1e-12, "dQ vs torch autograd")
+        _close(dk, tk, 1e-12, "dK vs torch autograd")
+        _close(dv, tv, 1e-12, "dV vs torch autograd")
+
+
+def pin_backward_invariants(orc):
+    """Rows of P sum to 1, so sum_j dV_j = sum of dO over the group's heads and rows;
+    rows of dS sum to 0, so sum_j dK_j = 0; causal row 0 has dQ = 0."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 19, 8
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 26, with_dout=True)
+    for causal in (False, True):
+        dq, dk, dv = orc.bwd(q, k, v, do, causal, 0.35)
+        dof = _f64(do).reshape(B, Hkv, Hq // Hkv, S, D)
+        _close(dv.sum(axis=2), dof.sum(axis=(2, 3)), 1e-12, "sum dV")
+        _close(dk.sum(axis=2), np.zeros((B, Hkv, D)), 1e-12, "sum dK")
+        if causal:
+            _close(dq[:, :, 0], np.zeros((B, Hq, D)), 1e-15, "causal dQ row 0")
+
+
+def pin_equal_keys(orc):
+    """With every key equal, scores do not depend on Q, so dQ = 0."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 7, 4
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 27, with_dout=True)
+    k = np.ascontiguousarray(np.broadcast_to(k[:, :, :1], k.shape))
+    for causal in (False, True):
+        dq, _, _ = orc.bwd(q, k, v, do, causal, 0.5)
+        _close(dq, np.zeros_like(dq), 1e-14, "equal keys dQ")
+
+
+FORWARD_PINS = [pin_brute_force, pin_torch_sdpa, pin_single_key, pin_zero_query,
+                pin_causal_first_row, pin_permutation, pin_gqa_is_repeated_mha, pin_sharp_softmax,
+                pin_rows_match_full]
+BACKWARD_PINS = [pin_finite_differences, pin_torch_autograd, pin_backward_invariants, pin_equal_keys]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS

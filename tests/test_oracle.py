@@ -1,0 +1,50 @@
+"""The fp64 oracle against its pins, and the pins against planted mistakes (CPU only)."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(oracle.default())
+
+
+# Plausible mistakes planted in a copy of the oracle source: (name, original text, replacement).
+# Each must make at least one pin fail; none reads or writes out of bounds.
+MUTATIONS = [
+    ("dropped_scale", "p[j] = c->scale * dot_bf16(", "p[j] = dot_bf16("),
+    ("causal_sees_next_key", "return c->causal ? i + 1 : c->S;",
+     "return c->causal ? (i + 1 < c->S ? i + 2 : c->S) : c->S;"),
+    ("gqa_interleaved_map", "hkv = hq / c->G;", "hkv = hq % c->Hkv;"),
+    ("lse_log2", "*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    ("unnormalised_p", "for (int j = 0; j < n; ++j) p[j] /= l;", ""),
+    ("ds_sign_flipped", "const double ds = p[j] * (dp[j] - delta);",
+     "const double ds = p[j] * (delta - dp[j]);"),
+    ("dp_uses_k_not_v", "dp[j] = dot_bf16(doi, c->v + kvrow_off", "dp[j] = dot_bf16(doi, c->k + kvrow_off"),
+    ("dq_missing_scale", "dq_out[d] += c->scale * ds * widen(kj[d]);", "dq_out[d] += ds * widen(kj[d]);"),
+    ("dk_missing_scale", "dk_out[d] += c->scale * ds * widen(qi[d]);", "dk_out[d] += ds * widen(qi[d]);"),
+    ("dk_dv_first_head_only", "for (int g = 0; g < c->G; ++g) {", "for (int g = 0; g < 1; ++g) {"),
+    ("dv_uses_q_not_do", "dv_out[d] += pij * widen(doi[d]);", "dv_out[d] += pij * widen(qi[d]);"),
+    ("delta_missing_p", "delta += p[j] * dp[j];", "delta += dp[j];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: %r" % old
+    mutated = tmp_path / ("oracle_%s.c" % name)
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.build(src=str(mutated), out=str(tmp_path / ("liboracle_%s.so" % name)))
+    broken = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(broken)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "planted mistake %s passed every pin" % name
