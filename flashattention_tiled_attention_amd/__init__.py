@@ -1,0 +1,169 @@
+"""MI355X (gfx950) fused attention: thin Python binding over the C ABI in include/attn.h.
+
+The binding only marshals arguments: torch tensors are used for device memory
+and streams, their data pointers and the current HIP stream go to the C entry
+points, and every step of the computation runs in the library's HIP kernels.
+There is no fallback: if ``libattn.so`` is missing, every call raises.
+
+Entry points with the C names (``attn_fwd``, ``attn_bwd``,
+``attn_bwd_workspace_bytes``, ``attn_status_str``) take caller-allocated
+tensors; ``fwd`` and ``bwd`` allocate their outputs with torch.
+"""
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+# attn_status codes (include/attn.h)
+ATTN_OK = 0
+ATTN_ERR_NULL = 1
+ATTN_ERR_SHAPE = 2
+ATTN_ERR_GQA = 3
+ATTN_ERR_UNSUPPORTED_D = 4
+ATTN_ERR_ALIGN = 5
+ATTN_ERR_WORKSPACE = 6
+ATTN_ERR_SCALE = 7
+ATTN_ERR_HIP = 8
+ATTN_ERR_DEVICE = 9
+
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__("%s: %s (status %d)" % (where, attn_status_str(code), code))
+
+
+def load_library(path=None):
+    """Load libattn.so (built by ``flashattention_tiled_attention_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libattn.so not found at %s: run flashattention_tiled_attention_amd/build.py "
+                           "(or __graft_entry__.build()) first" % p)
+    lib = ctypes.CDLL(p)
+    V = ctypes.c_void_p
+    I = ctypes.c_int
+    F = ctypes.c_float
+    Z = ctypes.c_size_t
+    lib.attn_fwd.argtypes = [V, V, V, V, V, I, I, I, I, I, I, F, V]
+    lib.attn_fwd.restype = I
+    lib.attn_bwd.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, F, V, Z, V]
+    lib.attn_bwd.restype = I
+    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_bwd_workspace_bytes.restype = Z
+    lib.attn_status_str.argtypes = [I]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def attn_status_str(code):
+    return load_library().attn_status_str(int(code)).decode()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape):
+    import torch
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise TypeError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B][H][S][D]")
+    B, Hq, S, D = q.shape
+    return B, Hq, k.shape[1], S, D
+
+
+def attn_fwd(q, k, v, o, lse, causal, scale, stream=None):
+    """C attn_fwd on torch tensors: q [B,Hq,S,D], k/v [B,Hkv,S,D] bf16; writes o (bf16) and lse (fp32)."""
+    import torch
+    B, Hq, Hkv, S, D = _dims(q, k)
+    _check(q, "q", torch.bfloat16, (B, Hq, S, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
+    _check(o, "o", torch.bfloat16, (B, Hq, S, D))
+    _check(lse, "lse", torch.float32, (B, Hq, S))
+    rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, D,
+                                 int(bool(causal)), float(scale), _stream(stream))
+    if rc:
+        raise AttnError(rc, "attn_fwd")
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal):
+    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, int(bool(causal))))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
+    """C attn_bwd on torch tensors; dq/dk/dv are fp32; workspace is a uint8 GPU tensor."""
+    import torch
+    B, Hq, Hkv, S, D = _dims(q, k)
+    for t, n, dt, sh in ((q, "q", torch.bfloat16, (B, Hq, S, D)), (k, "k", torch.bfloat16, (B, Hkv, S, D)),
+                         (v, "v", torch.bfloat16, (B, Hkv, S, D)), (o, "o", torch.bfloat16, (B, Hq, S, D)),
+                         (lse, "lse", torch.float32, (B, Hq, S)), (dout, "dout", torch.bfloat16, (B, Hq, S, D)),
+                         (dq, "dq", torch.float32, (B, Hq, S, D)), (dk, "dk", torch.float32, (B, Hkv, S, D)),
+                         (dv, "dv", torch.float32, (B, Hkv, S, D))):
+        _check(t, n, dt, sh)
+    if workspace.device.type != "cuda":
+        raise TypeError("workspace must be a GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), float(scale),
+                                 _ptr(workspace), nbytes, _stream(stream))
+    if rc:
+        raise AttnError(rc, "attn_bwd")
+
+
+def fwd(q, k, v, causal=False, scale=None):
+    """Allocate o and lse and run attn_fwd. scale defaults to 1/sqrt(D)."""
+    import torch
+    B, Hq, Hkv, S, D = _dims(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None):
+    """Allocate dq/dk/dv (fp32) and the workspace and run attn_bwd."""
+    import torch
+    B, Hq, Hkv, S, D = _dims(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=q.device)
+    ws = torch.empty((attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal),), dtype=torch.uint8,
+                     device=q.device)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, ws)
+    return dq, dk, dv

@@ -1,0 +1,156 @@
+// C ABI of the attention library: argument validation, per-device set-up and
+// kernel launch on the caller's stream. Declarations and the contract of each
+// entry point are in include/attn.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "attn.h"
+#include "kernels.h"
+
+namespace attn {
+hipError_t fwd_setup_device();
+hipError_t bwd_setup_device();
+}  // namespace attn
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_status[kMaxDevices];
+
+// Once per device: check that it is a gfx950 GPU and raise the kernels'
+// dynamic-LDS limit. Returns an attn_status.
+int setup_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return ATTN_ERR_HIP;
+    }
+    if (dev >= kMaxDevices) return ATTN_ERR_DEVICE;
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            g_dev_status[dev] = ATTN_ERR_HIP;
+            return;
+        }
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            g_dev_status[dev] = ATTN_ERR_DEVICE;
+            return;
+        }
+        if (attn::fwd_setup_device() != hipSuccess || attn::bwd_setup_device() != hipSuccess) {
+            (void)hipGetLastError();
+            g_dev_status[dev] = ATTN_ERR_HIP;
+            return;
+        }
+        g_dev_status[dev] = ATTN_OK;
+    });
+    return g_dev_status[dev];
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+int check_sizes(int B, int Hq, int Hkv, int S, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1) return ATTN_ERR_SHAPE;
+    const double elems = (double)B * Hq * S * D;
+    if (elems >= 1099511627776.0) return ATTN_ERR_SHAPE;  // 2^40
+    // grid size: B * Hq * ceil(S / 128) work groups must fit a 32-bit grid
+    if ((double)B * Hq * ((S + 127) / 128) >= 2147483647.0) return ATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_GQA;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
+    return ATTN_OK;
+}
+
+size_t delta_bytes(int B, int Hq, int S) {
+    return (((size_t)B * Hq * S * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "B, Hq, Hkv, S and D must be >= 1 and B*Hq*S*D < 2^40";
+        case ATTN_ERR_GQA: return "Hq must be a multiple of Hkv";
+        case ATTN_ERR_UNSUPPORTED_D: return "head dimension D must be 64 or 128";
+        case ATTN_ERR_ALIGN: return "tensor and workspace pointers must be 16-byte aligned";
+        case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
+        case ATTN_ERR_SCALE: return "scale must be finite";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+        case ATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+        default: return "unknown attn status";
+    }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int S, int D, int causal, float scale, void* stream) {
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    int rc = check_sizes(B, Hq, Hkv, S, D);
+    if (rc) return rc;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+        return ATTN_ERR_ALIGN;
+    if ((rc = setup_current_device())) return rc;
+
+    attn::FwdArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.o = (uint16_t*)o;
+    a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.G = Hq / Hkv;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+    a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
+    if (attn::launch_fwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal) {
+    (void)causal;
+    if (check_sizes(B, Hq, Hkv, S, D) != ATTN_OK) return 0;
+    return delta_bytes(B, Hq, S);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
+             int D, int causal, float scale, void* workspace, size_t workspace_bytes,
+             void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    int rc = check_sizes(B, Hq, Hkv, S, D);
+    if (rc) return rc;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal))
+        return ATTN_ERR_WORKSPACE;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
+        misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
+        misaligned(workspace))
+        return ATTN_ERR_ALIGN;
+    if ((rc = setup_current_device())) return rc;
+
+    attn::BwdArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.o = (const uint16_t*)o;
+    a.lse = lse;
+    a.dout = (const uint16_t*)dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = (float*)workspace;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.G = Hq / Hkv;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (attn::launch_bwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Device helpers for the gfx950 attention kernels: MFMA operand types, bf16
+// packing, LDS transpose loads and cross-half-wave reductions.
+//
+// MFMA lane layouts used throughout (v_mfma_f32_32x32x16_bf16, wave64, lane l,
+// half h = l / 32):
+//   A (32 x 16): lane l holds A[l % 32][8h + e], e = 0..7
+//   B (16 x 32): lane l holds B[8h + e][l % 32], e = 0..7
+//   C (32 x 32): lane l, register r holds C[8 (r / 4) + 4h + (r % 4)][l % 32]
+// A 32x32 accumulator therefore gives every lane one output column and 16 of
+// its rows; used as the B operand of a following product, its rows become the
+// contraction index in the order "k-slot 8h + e  <->  row 8 (e / 4) + 4h + e % 4"
+// (for the first 16 rows; rows 16..31 likewise with r = 8..15). The matching A
+// operand is read with that same row order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                        float a6, float a7) {
+    bf16x8 r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+__device__ __forceinline__ bf16x4 pack4(float a0, float a1, float a2, float a3) {
+    bf16x4 r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ds_read_b64_tr_b16. Each group of 16 lanes reads a 4-row x 16-column block of
+// 16-bit elements: local lane 4r + c passes the address of row r, columns
+// 4c..4c+3; local lane j receives column j, rows 0..3 as elements 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* lds_elem) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+    auto p = (ATTN_LDS v4bf*)((ATTN_LDS __bf16*)(lds_elem));
+    v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 lds_read8(const __bf16* lds_elem) {
+    return *(const bf16x8*)lds_elem;
+}
+
+// Combine a value with the same register of the lane 32 away (v_permlane32_swap).
+__device__ __forceinline__ float halves_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace attn

@@ -1,0 +1,41 @@
+// Internal interface between the C ABI (attn_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    int B, Hq, Hkv, S, G;
+    int causal;
+    float scale_log2;    // |scale| * log2(e)
+    uint32_t q_sign;     // 0x80008000 when scale < 0 (Q is negated on load), else 0
+};
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const float* lse;
+    const uint16_t* dout;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* delta;        // workspace: [B][Hq][S]
+    int B, Hq, Hkv, S, G;
+    int causal;
+    float scale;         // signed scale
+    float scale_log2;    // scale * log2(e) (signed)
+};
+
+// Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
+hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream);
+
+}  // namespace attn

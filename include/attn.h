@@ -1,0 +1,105 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention library.
+ *
+ * The operation is scaled dot-product attention as stated in Rao et al.,
+ * "Scheduling Data to Compute: Hierarchical Data Pipelining for LLM Training on
+ * AMD GPUs", section 2.1, Eq. (1): O = softmax(Q K^T * scale) V, computed the
+ * way that section's Algorithm 0 describes: K/V blocks stream through on-chip
+ * memory while the online-softmax state (running max m, running sum l) and the
+ * output accumulator stay on chip. The backward pass is the exact gradient of
+ * Eq. (1), recomputing P from the saved log-sum-exp; its products are the ones
+ * the same section's Table 3 lists (dQ = dS K, dK = dS^T Q) plus dV = P^T dO.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer on the current HIP device, in
+ *    contiguous [B][H][S][D] layout (row-major; D fastest), 16-byte aligned.
+ *    q, o, dout, dq: H = Hq.  k, v, dk, dv: H = Hkv.  lse: [B][Hq][S].
+ *  - bf16 tensors are passed as raw 16-bit storage (const void*).
+ *  - Grouped-query attention: query head hq reads key/value head hq / (Hq/Hkv)
+ *    (consecutive query heads share a key/value head). Hq % Hkv must be 0.
+ *  - causal != 0: query row i sees key rows j <= i (query and key lengths are
+ *    both S). causal == 0: every row sees all S keys.
+ *  - scale: any finite float; the usual value is 1/sqrt(D).
+ *  - D must be 64 or 128. S, B, Hq, Hkv >= 1, and B*Hq*S*D < 2^40.
+ *  - stream: a hipStream_t passed as void*; NULL means the null stream.
+ *    Calls are asynchronous: ATTN_OK means the kernels were enqueued. A device
+ *    fault surfaces at the caller's next synchronisation.
+ *  - The caller owns every buffer (inputs, outputs, workspace) and keeps it
+ *    alive until the stream has finished the call. The library allocates no
+ *    device memory and keeps no per-call state.
+ *  - Outputs must not alias inputs or each other. Every output element is
+ *    overwritten; none needs to be cleared beforehand.
+ *  - Arguments are validated before any HIP call; on an error nothing is
+ *    launched and nothing is written.
+ */
+#ifndef MI355_ATTN_H
+#define MI355_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,          /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = 2,         /* B, Hq, Hkv, S or D < 1, or B*Hq*S*D >= 2^40 */
+    ATTN_ERR_GQA = 3,           /* Hq is not a multiple of Hkv */
+    ATTN_ERR_UNSUPPORTED_D = 4, /* D is neither 64 nor 128 */
+    ATTN_ERR_ALIGN = 5,         /* a tensor or workspace pointer is not 16-byte aligned */
+    ATTN_ERR_WORKSPACE = 6,     /* workspace is NULL or smaller than attn_bwd_workspace_bytes() */
+    ATTN_ERR_SCALE = 7,         /* scale is NaN or infinite */
+    ATTN_ERR_HIP = 8,           /* the HIP runtime failed (no device, launch error) */
+    ATTN_ERR_DEVICE = 9         /* the current device is not a gfx950 GPU */
+};
+
+/*
+ * Forward pass, Eq. (1) with Algorithm 0's streaming (section 2.1).
+ *   q    [B][Hq][S][D]  bf16, read
+ *   k, v [B][Hkv][S][D] bf16, read
+ *   o    [B][Hq][S][D]  bf16, written: softmax(q k^T * scale) v, accumulated in
+ *                       fp32 and rounded to nearest even once at the end
+ *   lse  [B][Hq][S]     fp32, written: natural-log log-sum-exp of each row's
+ *                       scaled scores, ln(sum_j exp(scale * q_i . k_j))
+ * Returns an attn_status.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int S, int D, int causal, float scale, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for these sizes (the per-row
+ * delta_i = sum_d dO_id * O_id, fp32, plus alignment). Returns 0 when the
+ * sizes are invalid (attn_bwd would reject them).
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal);
+
+/*
+ * Backward pass: exact gradient of Eq. (1) (section 2.1; Table 3 lists its
+ * dQ and dK products), with P recomputed from lse.
+ *   q, k, v        as in attn_fwd, read
+ *   o              [B][Hq][S][D] bf16, read: attn_fwd's output for the same inputs
+ *   lse            [B][Hq][S] fp32, read: attn_fwd's lse for the same inputs
+ *   dout           [B][Hq][S][D] bf16, read: gradient of the loss w.r.t. o
+ *   dq             [B][Hq][S][D] fp32, written
+ *   dk, dv         [B][Hkv][S][D] fp32, written; each key/value head's gradient
+ *                  is summed over the Hq/Hkv query heads that read it
+ *   workspace      device scratch of at least attn_bwd_workspace_bytes() bytes,
+ *                  16-byte aligned; its contents on entry do not matter and on
+ *                  return are unspecified
+ * Calls that share a workspace must be ordered on one stream.
+ * Returns an attn_status.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv,
+             int B, int Hq, int Hkv, int S, int D, int causal, float scale,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_ATTN_H */

@@ -1,0 +1,111 @@
+"""Forward parity on the GPU: the HIP kernel through the C ABI against the fp64 oracle."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import flashattention_tiled_attention_amd as fa
+from flashattention_tiled_attention_amd.inputs import CONFIGS, qkv
+from tests.gpu_util import TOL_LSE, assert_close, bf16_dev_to_f64, f32_dev_to_f64, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, causal, scale):
+    import torch
+    o, lse = fa.fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return bf16_dev_to_f64(o), f32_dev_to_f64(lse)
+
+
+def check_full(B, Hq, Hkv, S, D, causal, seed=0, scale=None):
+    print("case B=%d Hq=%d Hkv=%d S=%d D=%d causal=%d seed=%d scale=%s" % (B, Hq, Hkv, S, D, causal, seed, scale),
+          flush=True)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q, k, v = qkv(B, Hq, Hkv, S, D, seed)
+    o, lse = run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal, scale)
+    assert_close(o, o_ref, "O")
+    assert_close(lse, lse_ref, "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)
+
+
+def test_single_head_s128_d64():
+    c = CONFIGS["single_head_s128_d64"]
+    check_full(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], c["causal"], seed=0)
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 63, 64, 65, 127, 128, 129, 200, 383])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(S, D, causal):
+    check_full(1, 2, 1, S, D, causal, seed=S)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (8, 2), (8, 1), (16, 16)])
+def test_gqa_groups(Hq, Hkv):
+    check_full(2, Hq, Hkv, 300, 128, True, seed=Hq * 10 + Hkv)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal", [
+    (2, 8, 2, 1024, 128, True),     # several tiles, GQA, (B*Hkv) % 8 != 0
+    (1, 16, 8, 777, 128, True),     # groups spread over all 8 XCDs, ragged tail
+    (3, 4, 4, 640, 64, False),
+    (2, 8, 8, 1000, 64, True),
+])
+def test_multi_tile(B, Hq, Hkv, S, D, causal):
+    check_full(B, Hq, Hkv, S, D, causal, seed=B + S)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0884, 0.5, -1.3])
+def test_scales(scale):
+    check_full(1, 4, 2, 257, 128, True, seed=3, scale=scale)
+    check_full(1, 2, 2, 130, 64, False, seed=4, scale=scale)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_seeds_small(seed):
+    check_full(1, 8, 2, 512, 128, True, seed=seed)
+
+
+@pytest.mark.parametrize("name", ["llama8b_causal_gqa_s4096", "long_causal_gqa_s8192", "mha_noncausal_s2048_d64"])
+def test_full_size_sampled(name):
+    """Full-size workloads in the launch configuration the benchmark times; the oracle
+    recomputes a sample of rows (every head's first/last rows, tile boundaries, random)."""
+    c = CONFIGS[name]
+    B, Hq, Hkv, S, D, causal = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], c["causal"]
+    print("case %s" % name, flush=True)
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = qkv(B, Hq, Hkv, S, D, 0)
+    o, lse = run_fwd(q, k, v, causal, scale)
+    rows = sample_rows(B, Hq, S, 600, seed=1)
+    o_ref, lse_ref = oracle.fwd_rows(q, k, v, rows, causal, scale)
+    assert_close(o.reshape(-1, D)[rows], o_ref, "O (%d sampled rows)" % rows.size)
+    assert_close(lse.reshape(-1)[rows], lse_ref, "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_deterministic():
+    import torch
+    q, k, v = qkv(1, 8, 2, 1024, 128, 5)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    o1, l1 = fa.fwd(dq, dk, dv, causal=True)
+    o2, l2 = fa.fwd(dq, dk, dv, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_zero_query_gives_prefix_mean():
+    """Closed form checked directly on GPU output: Q=0 gives the prefix mean of V."""
+    B, H, S, D = 1, 2, 700, 128
+    _, k, v = qkv(B, H, H, S, D, 9)
+    q = np.zeros((B, H, S, D), np.uint16)
+    o, lse = run_fwd(q, k, v, True, 0.0884)
+    from flashattention_tiled_attention_amd.inputs import bf16_to_f32
+    vf = bf16_to_f32(v).astype(np.float64)
+    prefix = np.cumsum(vf, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    assert_close(o, prefix, "Q=0 prefix mean")
+    assert_close(lse, np.broadcast_to(np.log(np.arange(1, S + 1.0)), lse.shape), "Q=0 lse",
+                 tol_max=TOL_LSE, tol_mean=TOL_LSE)
