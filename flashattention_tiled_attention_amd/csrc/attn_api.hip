@@ -149,6 +149,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     a.causal = causal ? 1 : 0;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
+    // Peaky softmax (score spread > 2 for unit-variance inputs): bf16 rounding of
+    // P, dS and the stored O would dominate, so every tile takes the exact path.
+    a.precise_all = fabsf(scale) * sqrtf((float)D) > 2.0f ? 1 : 0;
     if (attn::launch_bwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
 }

@@ -1,8 +1,548 @@
-// Backward attention kernels for gfx950 (placeholder until the kernels land).
+// Backward attention kernels for gfx950 (MI355X).
+//
+// Exact gradient of Eq. (1) of Rao et al., "Scheduling Data to Compute:
+// Hierarchical Data Pipelining for LLM Training on AMD GPUs", section 2.1,
+// with P recomputed from the forward's log-sum-exp. With
+//   P = exp(scale Q K^T - lse),  dP = dO V^T,  delta = rowsum(dO * O),
+//   dS = P * (dP - delta),
+// the products are dQ = scale dS K and dK = scale dS^T Q (the two backward rows
+// of that section's Table 3) and dV = P^T dO. Both Table 3 rows with a
+// transposed operand read it with the gfx950 transpose load
+// (ds_read_b64_tr_b16) from the row-major tile in LDS.
+//
+// Two kernels, ordered on the caller's stream, no atomics (deterministic):
+//   dq_kernel   one workgroup per (b, hq, 128-row query tile), K/V tiles streamed
+//               through double-buffered LDS as in the forward. It also computes
+//               delta for its rows and stores it in the workspace.
+//   dkv_kernel  one workgroup per (b, kv head, 64-key tile). K and V stay in
+//               registers; query/dO tiles of every query head of the group are
+//               streamed through LDS. Two wave pairs split the (head, query tile)
+//               iterations and their dK/dV partial sums are added in LDS at the
+//               end, so the grouped-query sum never leaves the chip.
+//
+// Rows whose visible keys all lie in the first 128 keys (the first query tile
+// of a causal problem, or every row when S <= 128) can carry probabilities near
+// 1, where bf16 rounding of P and dS and the rounding of the stored O inside
+// delta are largest. For those rows delta is recomputed exactly as
+// sum_j P_ij dP_ij in fp32, and the P and dS operands are split into a bf16 high
+// part plus a bf16 remainder (two MFMAs each). When |scale| * sqrt(D) > 2 the
+// scores of unit-variance inputs spread wide enough for any row to concentrate
+// on a few keys, and the host asks for this treatment on every tile.
 #include "device.h"
 #include "kernels.h"
 
 namespace attn {
-hipError_t bwd_setup_device() { return hipSuccess; }
-hipError_t launch_bwd(const BwdArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPreciseRows = 128;
+
+// ---------------------------------------------------------------------------
+// dQ (+ delta) kernel
+// ---------------------------------------------------------------------------
+constexpr int kDqBQ = 128;
+constexpr int kDqBK = 64;
+constexpr int kDqThreads = 256;
+
+template <int D>
+struct DqTile {
+    static constexpr int KP = D + 8;
+    static constexpr int VP = D + 8;
+    static constexpr int KTILE = kDqBK * KP;
+    static constexpr int VTILE = kDqBK * VP;
+    static constexpr int STAGE = KTILE + VTILE;
+    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static constexpr int CH = D / 8;
+    static constexpr int NLD = kDqBK * CH / kDqThreads;
+};
+
+__device__ __forceinline__ void decode_q_item(int bid, int nQ, int B, int Hkv, int G, bool causal,
+                                              int& b, int& hq, int& qt) {
+    const int C = B * Hkv;
+    int rank, c, g;
+    if ((C & 7) == 0) {
+        const int x = bid & 7, s = bid >> 3, per = (C >> 3) * G;
+        rank = s / per;
+        const int rem = s - rank * per;
+        c = (rem / G) * 8 + x;
+        g = rem % G;
+    } else {
+        const int per = C * G;
+        rank = bid / per;
+        const int rem = bid - rank * per;
+        c = rem / G;
+        g = rem % G;
+    }
+    qt = causal ? nQ - 1 - rank : rank;
+    b = c / Hkv;
+    hq = (c % Hkv) * G + g;
+}
+
+__device__ __forceinline__ float bf_lo(float x) { return x - (float)(__bf16)x; }
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) dq_kernel(BwdArgs a) {
+    using T = DqTile<D>;
+    constexpr int DK = D / 16;
+    constexpr int DB = D / 32;
+    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int S = a.S;
+    const int nQ = (S + kDqBQ - 1) / kDqBQ;
+    int b, hq, qt;
+    decode_q_item(blockIdx.x, nQ, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
+    const int hkv = hq / a.G;
+    const size_t rowbase = ((size_t)b * a.Hq + hq) * (size_t)S;
+    const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
+    const uint16_t* Kp = a.k + kvbase;
+    const uint16_t* Vp = a.v + kvbase;
+    const int q0 = qt * kDqBQ;
+    const int qrow = q0 + 32 * wave + l32;
+    const bool live = qrow < S;
+    const float c = a.scale_log2;
+    const bool precise = a.precise_all || ((qt == 0) && (CAUSAL || S <= kPreciseRows));
+
+    // Q and dO rows as B operands; delta = rowsum(dO * O) from the stored O.
+    bf16x8 qf[DK], df[DK];
+    float dpart = 0.0f;
+    if (live) {
+        const size_t off = (rowbase + qrow) * D + 8 * h;
+        const u32x4* qs = (const u32x4*)(a.q + off);
+        const u32x4* ds = (const u32x4*)(a.dout + off);
+        const u32x4* os = (const u32x4*)(a.o + off);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            qf[dk] = __builtin_bit_cast(bf16x8, qs[2 * dk]);
+            df[dk] = __builtin_bit_cast(bf16x8, ds[2 * dk]);
+            const bf16x8 ov = __builtin_bit_cast(bf16x8, os[2 * dk]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dpart += (float)df[dk][e] * (float)ov[e];
+        }
+    } else {
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            qf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+            df[dk] = qf[dk];
+        }
+    }
+    float delta = halves_sum(dpart);
+    const float lse2 = live ? a.lse[rowbase + qrow] * kLog2e : INFINITY;
+
+    const int nK = (S + kDqBK - 1) / kDqBK;
+    const int jend = CAUSAL ? min(nK, (q0 + kDqBQ - 1) / kDqBK + 1) : nK;
+    int wjend = CAUSAL ? min(jend, (q0 + 32 * wave + 31) / kDqBK + 1) : jend;
+    if (q0 + 32 * wave >= S) wjend = 0;
+
+    u32x4 kst[T::NLD], vst[T::NLD];
+    auto gload = [&](int j) {
+        const int k0 = j * kDqBK;
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int ch = tid + kDqThreads * i, row = ch / T::CH, col = (ch % T::CH) * 8;
+            const int key = k0 + row;
+            if (key < S) {
+                kst[i] = *(const u32x4*)(Kp + (size_t)key * D + col);
+                vst[i] = *(const u32x4*)(Vp + (size_t)key * D + col);
+            } else {
+                kst[i] = u32x4{0, 0, 0, 0};
+                vst[i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto lstore = [&](int stage) {
+        __bf16* Ks = smem + stage * T::STAGE;
+        __bf16* Vs = Ks + T::KTILE;
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int ch = tid + kDqThreads * i, row = ch / T::CH, col = (ch % T::CH) * 8;
+            *(u32x4*)(Ks + row * T::KP + col) = kst[i];
+            *(u32x4*)(Vs + row * T::VP + col) = vst[i];
+        }
+    };
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero16();
+
+    // Pass 0 (precise tiles only) accumulates the exact delta; the last pass
+    // forms dS and accumulates dQ^T += K^T dS^T.
+    for (int pass = precise ? 0 : 1; pass < 2; ++pass) {
+        float dacc = 0.0f;
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int j = 0; j < jend; ++j) {
+            if (j + 1 < jend) gload(j + 1);
+            if (j < wjend) {
+                const __bf16* Ks = smem + (j & 1) * T::STAGE;
+                const __bf16* Vs = Ks + T::KTILE;
+                const int k0 = j * kDqBK;
+                const bool need_mask = CAUSAL && (k0 + kDqBK - 1 > q0 + 32 * wave);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+                    for (int dk = 0; dk < DK; ++dk) {
+                        const bf16x8 kf = lds_read8(Ks + (kb * 32 + l32) * T::KP + dk * 16 + 8 * h);
+                        const bf16x8 vf = lds_read8(Vs + (kb * 32 + l32) * T::VP + dk * 16 + 8 * h);
+                        s = mfma32(kf, qf[dk], s);
+                        dp = mfma32(vf, df[dk], dp);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = fast_exp2(fmaf(s[r], c, -lse2));
+                        if (need_mask) {
+                            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            p = key <= qrow ? p : 0.0f;
+                        }
+                        if (pass == 0) dacc += p * dp[r];
+                        s[r] = p * (dp[r] - delta);
+                    }
+                    if (pass == 0) continue;
+                    // dQ^T += K^T dS^T over two 16-key steps; K^T via transpose loads.
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const int r0 = 8 * t2;
+                        const bf16x8 hi = pack8(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4],
+                                                s[r0 + 5], s[r0 + 6], s[r0 + 7]);
+                        bf16x8 lo;
+                        if (precise)
+                            lo = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
+                                       bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]), bf_lo(s[r0 + 7]));
+                        const __bf16* krow = Ks + (kb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2)) * T::KP +
+                                             16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+                        for (int db = 0; db < DB; ++db) {
+                            const bf16x8 kt = concat(lds_read_tr(krow + db * 32),
+                                                     lds_read_tr(krow + db * 32 + 8 * T::KP));
+                            dq[db] = mfma32(kt, hi, dq[db]);
+                            if (precise) dq[db] = mfma32(kt, lo, dq[db]);
+                        }
+                    }
+                }
+            }
+            if (j + 1 < jend) lstore((j + 1) & 1);
+            __syncthreads();
+        }
+        if (pass == 0) delta = halves_sum(dacc);
+    }
+
+    if (live) {
+        if (h == 0) a.delta[rowbase + qrow] = delta;
+        float* dst = a.dq + (rowbase + qrow) * D;
+        const float sc = a.scale;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v;
+                v[0] = dq[db][4 * g4] * sc;
+                v[1] = dq[db][4 * g4 + 1] * sc;
+                v[2] = dq[db][4 * g4 + 2] * sc;
+                v[3] = dq[db][4 * g4 + 3] * sc;
+                *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * h) = v;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel
+// ---------------------------------------------------------------------------
+constexpr int kKvBK = 64;    // keys per workgroup (2 waves x 32)
+constexpr int kKvBQ = 64;    // query rows per streamed tile
+constexpr int kKvThreads = 256;
+
+template <int D>
+struct KvTile {
+    static constexpr int QP = D + 8;                       // Q / dO row pitch (b128 and transpose reads)
+    static constexpr int QTILE = kKvBQ * QP;               // elements
+    static constexpr int STAGE_BYTES = 2 * QTILE * 2 + 2 * kKvBQ * 4;  // Q, dO, lse*log2e, delta
+    static constexpr int PAIR_BYTES = 2 * STAGE_BYTES;     // double buffered
+    static constexpr int XCHG_BYTES = 2 * 2 * (D / 32) * 16 * 64 * 4;  // 2 waves x dK,dV partials
+    static constexpr int LDS_BYTES = (2 * PAIR_BYTES > XCHG_BYTES) ? 2 * PAIR_BYTES : XCHG_BYTES;
+    static constexpr int CH = D / 8;
+    static constexpr int NLD = kKvBQ * CH / 128;           // chunks per thread of a pair, per tensor
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
+    using T = KvTile<D>;
+    constexpr int DK = D / 16;
+    constexpr int DB = D / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int pair = wave >> 1, w2 = wave & 1, ptid = tid & 127;
+    const int S = a.S, G = a.G;
+    const int nQB = (S + kKvBQ - 1) / kKvBQ;
+
+    // work item: (b, hkv, key tile); causal tiles issued longest (lowest) first,
+    // groups dealt to XCDs as in the forward.
+    int b, hkv, kt;
+    {
+        const int C = a.B * a.Hkv, bid = blockIdx.x;
+        int rank, cgrp;
+        if ((C & 7) == 0) {
+            const int x = bid & 7, s = bid >> 3, per = C >> 3;
+            rank = s / per;
+            cgrp = (s - rank * per) * 8 + x;
+        } else {
+            rank = bid / C;
+            cgrp = bid - rank * C;
+        }
+        kt = rank;  // ascending key tile = most query tiles first when causal
+        b = cgrp / a.Hkv;
+        hkv = cgrp % a.Hkv;
+    }
+    const int kv0 = kt * kKvBK;
+    const int kw0 = kv0 + 32 * w2;  // this wave's first key
+    const int key = kw0 + l32;      // this lane's key (column of S, dP)
+    const size_t kvrow = ((size_t)b * a.Hkv + hkv) * (size_t)S;
+    const float c = a.scale_log2;
+    const bool precise_problem = CAUSAL || S <= kPreciseRows;
+
+    // K and V rows of this lane's key as B operands (zero past the end).
+    bf16x8 kf[DK], vf[DK];
+    if (key < S) {
+        const u32x4* ks = (const u32x4*)(a.k + (kvrow + key) * D + 8 * h);
+        const u32x4* vs = (const u32x4*)(a.v + (kvrow + key) * D + 8 * h);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            kf[dk] = __builtin_bit_cast(bf16x8, ks[2 * dk]);
+            vf[dk] = __builtin_bit_cast(bf16x8, vs[2 * dk]);
+        }
+    } else {
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            kf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+            vf[dk] = kf[dk];
+        }
+    }
+
+    // Iterations: (g, query tile qi) for qi >= first visible tile; pair p takes
+    // iterations p, p+2, ...
+    const int qi_first = CAUSAL ? kv0 / kKvBQ : 0;
+    const int per_g = nQB - qi_first;
+    const int total = G * per_g;
+    const int steps = (total + 1) / 2;
+
+    unsigned char* pair_base = lds_raw + pair * T::PAIR_BYTES;
+    auto stage_q = [&](int st) { return (__bf16*)(pair_base + st * T::STAGE_BYTES); };
+    auto stage_do = [&](int st) { return (__bf16*)(pair_base + st * T::STAGE_BYTES) + T::QTILE; };
+    auto stage_lse = [&](int st) { return (float*)(pair_base + st * T::STAGE_BYTES + 2 * T::QTILE * 2); };
+    auto stage_dl = [&](int st) { return stage_lse(st) + kKvBQ; };
+
+    u32x4 qst[T::NLD], dst_[T::NLD];
+    float lst = 0.f, dlst = 0.f;
+    auto gload = [&](int step) {
+        const int it = 2 * step + pair;
+        if (it >= total) return;
+        const int g = it / per_g, qi = qi_first + it % per_g;
+        const int hq = hkv * G + g;
+        const size_t rb = ((size_t)b * a.Hq + hq) * (size_t)S;
+        const int qr0 = qi * kKvBQ;
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int ch = ptid + 128 * i, row = ch / T::CH, col = (ch % T::CH) * 8;
+            const int qr = qr0 + row;
+            if (qr < S) {
+                qst[i] = *(const u32x4*)(a.q + (rb + qr) * D + col);
+                dst_[i] = *(const u32x4*)(a.dout + (rb + qr) * D + col);
+            } else {
+                qst[i] = u32x4{0, 0, 0, 0};
+                dst_[i] = u32x4{0, 0, 0, 0};
+            }
+        }
+        if (ptid < kKvBQ) {
+            const int qr = qr0 + ptid;
+            lst = qr < S ? a.lse[rb + qr] * kLog2e : INFINITY;
+            dlst = qr < S ? a.delta[rb + qr] : 0.0f;
+        }
+    };
+    auto lstore = [&](int step) {
+        const int it = 2 * step + pair;
+        if (it >= total) return;
+        const int st = step & 1;
+        __bf16* Qs = stage_q(st);
+        __bf16* Ds = stage_do(st);
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int ch = ptid + 128 * i, row = ch / T::CH, col = (ch % T::CH) * 8;
+            *(u32x4*)(Qs + row * T::QP + col) = qst[i];
+            *(u32x4*)(Ds + row * T::QP + col) = dst_[i];
+        }
+        if (ptid < kKvBQ) {
+            stage_lse(st)[ptid] = lst;
+            stage_dl(st)[ptid] = dlst;
+        }
+    };
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dk[db] = zero16();
+        dv[db] = zero16();
+    }
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int step = 0; step < steps; ++step) {
+        if (step + 1 < steps) gload(step + 1);
+        const int it = 2 * step + pair;
+        if (it < total) {
+            const int st = step & 1;
+            const __bf16* Qs = stage_q(st);
+            const __bf16* Ds = stage_do(st);
+            const float* Ls = stage_lse(st);
+            const float* Dl = stage_dl(st);
+            const int qi = qi_first + it % per_g;
+            const int qr0 = qi * kKvBQ;
+            const bool precise = a.precise_all || (precise_problem && qr0 < kPreciseRows);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int qs0 = qr0 + 32 * qb;
+                if (CAUSAL && qs0 + 31 < kw0) continue;  // every query precedes every key
+                if (qs0 >= S) continue;
+                const bool need_mask = CAUSAL && qs0 < kw0 + 31;
+                f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+                for (int dd = 0; dd < DK; ++dd) {
+                    const bf16x8 qa = lds_read8(Qs + (qb * 32 + l32) * T::QP + dd * 16 + 8 * h);
+                    const bf16x8 da = lds_read8(Ds + (qb * 32 + l32) * T::QP + dd * 16 + 8 * h);
+                    s = mfma32(qa, kf[dd], s);
+                    dp = mfma32(da, vf[dd], dp);
+                }
+                // rows of s/dp are queries qb*32 + 8(r/4) + 4h + r%4; the column is this lane's key
+                float pv[16];
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const f32x4 l4 = *(const f32x4*)(Ls + qb * 32 + 8 * rg + 4 * h);
+                    const f32x4 d4 = *(const f32x4*)(Dl + qb * 32 + 8 * rg + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * rg + e;
+                        float p = fast_exp2(fmaf(s[r], c, -l4[e]));
+                        if (need_mask) {
+                            const int qrow = qs0 + 8 * rg + 4 * h + e;
+                            p = key <= qrow ? p : 0.0f;
+                        }
+                        pv[r] = p;
+                        s[r] = p * (dp[r] - d4[e]);
+                    }
+                }
+                // dV^T += dO^T P and dK^T += Q^T dS over two 16-query steps; dO^T and
+                // Q^T via transpose loads of the row-major tiles.
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const int r0 = 8 * t2;
+                    const bf16x8 ph = pack8(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4], pv[r0 + 5],
+                                            pv[r0 + 6], pv[r0 + 7]);
+                    const bf16x8 sh = pack8(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5],
+                                            s[r0 + 6], s[r0 + 7]);
+                    bf16x8 pl, sl;
+                    if (precise) {
+                        pl = pack8(bf_lo(pv[r0]), bf_lo(pv[r0 + 1]), bf_lo(pv[r0 + 2]), bf_lo(pv[r0 + 3]),
+                                   bf_lo(pv[r0 + 4]), bf_lo(pv[r0 + 5]), bf_lo(pv[r0 + 6]), bf_lo(pv[r0 + 7]));
+                        sl = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
+                                   bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]), bf_lo(s[r0 + 7]));
+                    }
+                    const int roff = (qb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2)) * T::QP +
+                                     16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const bf16x8 dot = concat(lds_read_tr(Ds + roff + db * 32),
+                                                  lds_read_tr(Ds + roff + db * 32 + 8 * T::QP));
+                        const bf16x8 qt = concat(lds_read_tr(Qs + roff + db * 32),
+                                                 lds_read_tr(Qs + roff + db * 32 + 8 * T::QP));
+                        dv[db] = mfma32(dot, ph, dv[db]);
+                        dk[db] = mfma32(qt, sh, dk[db]);
+                        if (precise) {
+                            dv[db] = mfma32(dot, pl, dv[db]);
+                            dk[db] = mfma32(qt, sl, dk[db]);
+                        }
+                    }
+                }
+            }
+        }
+        if (step + 1 < steps) lstore(step + 1);
+        __syncthreads();
+    }
+
+    // Sum the two wave pairs' partials (same keys, disjoint iterations): pair 0
+    // finishes dK, pair 1 finishes dV. Layout [w2][tensor][db][r][lane].
+    float* xchg = (float*)lds_raw;
+    auto slot = [&](int ww, int tensor, int db, int r) {
+        return xchg + ((((ww * 2 + tensor) * DB + db) * 16 + r) * 64) + lane;
+    };
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (pair == 1) *slot(w2, 0, db, r) = dk[db][r];   // pair 1 hands over dK
+            else *slot(w2, 1, db, r) = dv[db][r];             // pair 0 hands over dV
+        }
+    __syncthreads();
+    if (key < S) {
+        float* out = (pair == 0 ? a.dk : a.dv) + (kvrow + key) * D;
+        const float sc = pair == 0 ? a.scale : 1.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    const float mine = pair == 0 ? dk[db][r] : dv[db][r];
+                    const float other = *slot(w2, pair == 0 ? 0 : 1, db, r);
+                    v[e] = (mine + other) * sc;
+                }
+                *(f32x4*)(out + db * 32 + 8 * g4 + 4 * h) = v;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+    const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
+    const long long qblocks = (long long)a.B * a.Hq * nQ;
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)qblocks), dim3(kDqThreads),
+                       DqTile<D>::LDS_BYTES, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nKB = (a.S + kKvBK - 1) / kKvBK;
+    const long long kvblocks = (long long)a.B * a.Hkv * nKB;
+    hipLaunchKernelGGL((dkv_kernel<D, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKvThreads),
+                       KvTile<D>::LDS_BYTES, stream, a);
+    return hipGetLastError();
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, int bytes) {
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+}  // namespace
+
+hipError_t bwd_setup_device() {
+    hipError_t e;
+    if ((e = set_lds(dq_kernel<64, false>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<64, true>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, false>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, true>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dkv_kernel<64, false>, KvTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dkv_kernel<64, true>, KvTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dkv_kernel<128, false>, KvTile<128>::LDS_BYTES))) return e;
+    return set_lds(dkv_kernel<128, true>, KvTile<128>::LDS_BYTES);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream) {
+    if (D == 64) return a.causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
+    return a.causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+}
+
 }  // namespace attn

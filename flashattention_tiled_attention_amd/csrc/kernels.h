@@ -32,6 +32,7 @@ struct BwdArgs {
     int causal;
     float scale;         // signed scale
     float scale_log2;    // scale * log2(e) (signed)
+    int precise_all;     // exact delta and split P/dS operands on every tile
 };
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
