@@ -106,8 +106,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.lse = lse;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.G = Hq / Hkv;
     a.causal = causal ? 1 : 0;
-    a.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+    // The kernel needs a strictly positive factor (masked scores are -inf); a zero
+    // scale becomes 2^-100, which leaves every exp2 of a finite score at exactly 1.
+    a.scale_log2 = fmaxf(fabsf(scale) * 1.4426950408889634f, 7.888609052210118e-31f);
     a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
+    // A stale row maximum leaves the dominant weight of a peaked row (|scale| *
+    // sqrt(D) > 2 for unit-variance inputs) off 1.0 and so exposed to bf16
+    // rounding; there the maximum is tracked exactly.
+    a.max_slack = fabsf(scale) * sqrtf((float)D) > 2.0f ? 0.0f : 8.0f;
     if (attn::launch_fwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
 }

@@ -46,9 +46,8 @@ constexpr int kDqThreads = 256;
 
 template <int D>
 struct DqTile {
-    static constexpr int KP = D + 8;
-    static constexpr int VP = D + 8;
-    static constexpr int KTILE = kDqBK * KP;
+    static constexpr int VP = D + 8;     // V: row reads only, padded
+    static constexpr int KTILE = kDqBK * D;  // K: row and transpose reads, swizzled (swz)
     static constexpr int VTILE = kDqBK * VP;
     static constexpr int STAGE = KTILE + VTILE;
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
@@ -157,7 +156,7 @@ __global__ void __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) dq_kernel(BwdArgs
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             const int ch = tid + kDqThreads * i, row = ch / T::CH, col = (ch % T::CH) * 8;
-            *(u32x4*)(Ks + row * T::KP + col) = kst[i];
+            *(u32x4*)(Ks + swz<D>(row, col)) = kst[i];
             *(u32x4*)(Vs + row * T::VP + col) = vst[i];
         }
     };
@@ -185,7 +184,7 @@ __global__ void __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) dq_kernel(BwdArgs
                     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                     for (int dk = 0; dk < DK; ++dk) {
-                        const bf16x8 kf = lds_read8(Ks + (kb * 32 + l32) * T::KP + dk * 16 + 8 * h);
+                        const bf16x8 kf = lds_read8(Ks + swz<D>(kb * 32 + l32, dk * 16 + 8 * h));
                         const bf16x8 vf = lds_read8(Vs + (kb * 32 + l32) * T::VP + dk * 16 + 8 * h);
                         s = mfma32(kf, qf[dk], s);
                         dp = mfma32(vf, df[dk], dp);
@@ -211,12 +210,12 @@ __global__ void __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) dq_kernel(BwdArgs
                         if (precise)
                             lo = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
                                        bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]), bf_lo(s[r0 + 7]));
-                        const __bf16* krow = Ks + (kb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2)) * T::KP +
-                                             16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                        const int trow = kb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2);
+                        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
                         for (int db = 0; db < DB; ++db) {
-                            const bf16x8 kt = concat(lds_read_tr(krow + db * 32),
-                                                     lds_read_tr(krow + db * 32 + 8 * T::KP));
+                            const bf16x8 kt = concat(lds_read_tr(Ks + swz<D>(trow, tcol + db * 32)),
+                                                     lds_read_tr(Ks + swz<D>(trow + 8, tcol + db * 32)));
                             dq[db] = mfma32(kt, hi, dq[db]);
                             if (precise) dq[db] = mfma32(kt, lo, dq[db]);
                         }
@@ -256,8 +255,7 @@ constexpr int kKvThreads = 256;
 
 template <int D>
 struct KvTile {
-    static constexpr int QP = D + 8;                       // Q / dO row pitch (b128 and transpose reads)
-    static constexpr int QTILE = kKvBQ * QP;               // elements
+    static constexpr int QTILE = kKvBQ * D;                // Q / dO tile, swizzled (swz), elements
     static constexpr int STAGE_BYTES = 2 * QTILE * 2 + 2 * kKvBQ * 4;  // Q, dO, lse*log2e, delta
     static constexpr int PAIR_BYTES = 2 * STAGE_BYTES;     // double buffered
     static constexpr int XCHG_BYTES = 2 * 2 * (D / 32) * 16 * 64 * 4;  // 2 waves x dK,dV partials
@@ -371,8 +369,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             const int ch = ptid + 128 * i, row = ch / T::CH, col = (ch % T::CH) * 8;
-            *(u32x4*)(Qs + row * T::QP + col) = qst[i];
-            *(u32x4*)(Ds + row * T::QP + col) = dst_[i];
+            *(u32x4*)(Qs + swz<D>(row, col)) = qst[i];
+            *(u32x4*)(Ds + swz<D>(row, col)) = dst_[i];
         }
         if (ptid < kKvBQ) {
             stage_lse(st)[ptid] = lst;
@@ -411,8 +409,9 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                 f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                 for (int dd = 0; dd < DK; ++dd) {
-                    const bf16x8 qa = lds_read8(Qs + (qb * 32 + l32) * T::QP + dd * 16 + 8 * h);
-                    const bf16x8 da = lds_read8(Ds + (qb * 32 + l32) * T::QP + dd * 16 + 8 * h);
+                    const int ro = swz<D>(qb * 32 + l32, dd * 16 + 8 * h);
+                    const bf16x8 qa = lds_read8(Qs + ro);
+                    const bf16x8 da = lds_read8(Ds + ro);
                     s = mfma32(qa, kf[dd], s);
                     dp = mfma32(da, vf[dd], dp);
                 }
@@ -450,14 +449,13 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                         sl = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
                                    bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]), bf_lo(s[r0 + 7]));
                     }
-                    const int roff = (qb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2)) * T::QP +
-                                     16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                    const int trow = qb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2);
+                    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const bf16x8 dot = concat(lds_read_tr(Ds + roff + db * 32),
-                                                  lds_read_tr(Ds + roff + db * 32 + 8 * T::QP));
-                        const bf16x8 qt = concat(lds_read_tr(Qs + roff + db * 32),
-                                                 lds_read_tr(Qs + roff + db * 32 + 8 * T::QP));
+                        const int o1 = swz<D>(trow, tcol + db * 32), o2 = swz<D>(trow + 8, tcol + db * 32);
+                        const bf16x8 dot = concat(lds_read_tr(Ds + o1), lds_read_tr(Ds + o2));
+                        const bf16x8 qt = concat(lds_read_tr(Qs + o1), lds_read_tr(Qs + o2));
                         dv[db] = mfma32(dot, ph, dv[db]);
                         dk[db] = mfma32(qt, sh, dk[db]);
                         if (precise) {

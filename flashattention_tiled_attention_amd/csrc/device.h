@@ -70,6 +70,34 @@ __device__ __forceinline__ bf16x8 lds_read8(const __bf16* lds_elem) {
     return *(const bf16x8*)lds_elem;
 }
 
+// Element offset of (row, col) in an unpadded row-major bf16 tile of D columns
+// whose 16-byte chunks are XOR-permuted per row. gfx950 LDS has 64 4-byte banks;
+// ds_read_b128 serves 16 lanes per cycle and ds_read_b64_tr_b16 32 lanes per
+// cycle. The permutation makes both access shapes the kernels use hit 16
+// distinct 16-byte bank groups: 16 consecutive rows at one chunk (A-operand row
+// reads) and 4 consecutive rows x 4 consecutive chunks (one transpose-read quad).
+// The permutation depends on row & 15 only, so adding a multiple of 16 rows to
+// an offset is a plain addition.
+template <int D>
+__device__ __forceinline__ int swz_f(int row) {
+    static_assert(D == 64 || D == 128, "tile width");
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                    : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * D + ((((col >> 3) ^ swz_f<D>(row))) << 3) + (col & 7);
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds_wave_base + 16 i. lds_wave_base must be the same
+// for every lane of the wave. Completion is tracked by vmcnt.
+__device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                     (ATTN_LDS void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Combine a value with the same register of the lane 32 away (v_permlane32_swap).
 __device__ __forceinline__ float halves_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);

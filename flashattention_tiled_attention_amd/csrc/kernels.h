@@ -13,8 +13,9 @@ struct FwdArgs {
     float* lse;
     int B, Hq, Hkv, S, G;
     int causal;
-    float scale_log2;    // |scale| * log2(e)
+    float scale_log2;    // max(|scale| * log2(e), 2^-100)
     uint32_t q_sign;     // 0x80008000 when scale < 0 (Q is negated on load), else 0
+    float max_slack;     // log2 growth of a row maximum tolerated before rescaling O
 };
 
 struct BwdArgs {
