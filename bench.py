@@ -77,6 +77,50 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
             "kind": "oracle", "sample": sample, "seconds": round(secs, 2)}
 
 
+KERNEL_SOURCES = {
+    "fwd_kernel": "flashattention_tiled_attention_amd/csrc/attn_fwd.hip",
+    "dq_kernel": "flashattention_tiled_attention_amd/csrc/attn_bwd.hip",
+    "dkv_kernel": "flashattention_tiled_attention_amd/csrc/attn_bwd.hip",
+}
+
+
+def source_sha(kernel):
+    import hashlib
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def hbm_traffic(kernel):
+    """HBM bytes per launch from profiles/hbm_traffic_<kernel>.txt (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE, each scaled by the factor a plain copy of known size gives), or None when
+    the record is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_llama8b_s4096.txt" % kernel)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("source_sha256_16") != source_sha(kernel):
+        return None
+    fetch = float(kv["fetch_kib_per_launch"]) * 1024 * float(kv["copy_factor_fetch"])
+    write = float(kv["write_kib_per_launch"]) * 1024 * float(kv["copy_factor_write"])
+    return fetch + write
+
+
+def copy_probe():
+    """A plain device-to-device copy of a known size, for calibrating FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,13 +129,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward kernel alone")
+    ap.add_argument("--copy-probe", action="store_true", help="run only the HBM counter calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
 
-    import numpy as np
     import torch
     import flashattention_tiled_attention_amd as fa
     from flashattention_tiled_attention_amd.inputs import CONFIGS, qkv
@@ -109,21 +156,18 @@ def main():
     gv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
     ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal),), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-
-    fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale)
     with_bwd = not args.fwd_only
+
+    bargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws, stream)
+    calls = {"fwd_kernel": lambda: fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream)}
     if with_bwd:
-        try:
-            fa.attn_bwd(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws)
-        except fa.AttnError as e:
-            log("backward unavailable (%s): timing the forward only" % e)
-            with_bwd = False
-    torch.cuda.synchronize()
+        calls["dq_kernel"] = lambda: fa.attn_bwd_dq(*bargs)
+        calls["dkv_kernel"] = lambda: fa.attn_bwd_dkdv(*bargs)
 
     def step():
         fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream)
         if with_bwd:
-            fa.attn_bwd(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws, stream)
+            fa.attn_bwd(*bargs)
 
     for _ in range(args.warmup):
         step()
@@ -135,7 +179,8 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # Per-kernel launch durations, with HIP events on the stream the kernels run on.
+    # Per-kernel launch durations with HIP events recorded on the stream the kernels
+    # run on; each entry point launches exactly one kernel.
     def time_calls(fn, n):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -147,21 +192,32 @@ def main():
         return e0.elapsed_time(e1) / n
 
     n_rep = max(args.steps, 10)
-    fwd_ms = time_calls(lambda: fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream), n_rep)
-    bwd_ms = None
-    if with_bwd:
-        bwd_ms = time_calls(lambda: fa.attn_bwd(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws,
-                                                stream), n_rep)
+    kernel_ms = {name: time_calls(fn, n_rep) for name, fn in calls.items()}
 
-    f_fwd = fwd_flops(B, Hq, S, D, causal)
-    f_bwd = 2.5 * f_fwd
+    # FLOP convention: one "product" is 2*B*Hq*S^2*D (halved when causal). The forward
+    # kernel computes 2 (S = Q K^T, O = P V); the dQ kernel 3 (S, dP = dO V^T, dQ = dS K);
+    # the dK/dV kernel 4 (S, dP, dV = P^T dO, dK = dS^T Q). The step's algorithmic work
+    # is forward 2 + backward 5 products (backward = 2.5 x forward).
+    product = fwd_flops(B, Hq, S, D, causal) / 2
+    kernel_products = {"fwd_kernel": 2, "dq_kernel": 3, "dkv_kernel": 4}
+    f_fwd = 2 * product
+    f_bwd = 5 * product
     step_flops = f_fwd + (f_bwd if with_bwd else 0.0)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    fwd_tflops = f_fwd / (fwd_ms * 1e-3) / 1e12
 
-    roofline = {"bound": "mfma", "kernel": "fwd_kernel<128,causal>", "achieved": round(fwd_tflops, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "flop_per_launch": f_fwd, "launch_ms": round(fwd_ms, 4)}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    dom_flops = kernel_products[dominant] * product
+    achieved = dom_flops / (kernel_ms[dominant] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": hbm_traffic(dominant),
+                "flop_per_launch": dom_flops, "launch_ms": round(kernel_ms[dominant], 4)}
+
+    kernels = {}
+    for name, ms in kernel_ms.items():
+        fl = kernel_products[name] * product
+        kernels[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                         "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "hbm_bytes": hbm_traffic(name)}
 
     result = {
         "metric": "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak on 1 MI355X",
@@ -172,14 +228,15 @@ def main():
                    "S": S, "D": D, "causal": bool(causal), "pass": "fwd+bwd" if with_bwd else "fwd",
                    "seed": 0},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"tflops": round(fwd_tflops, 2), "ms": round(fwd_ms, 4),
-                "frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
+        "fwd": {"tflops": kernels["fwd_kernel"]["tflops"], "ms": kernels["fwd_kernel"]["ms"],
+                "frac_of_peak": kernels["fwd_kernel"]["frac_of_peak"]},
+        "kernels": kernels,
         "roofline": roofline,
     }
     if with_bwd:
-        bwd_tflops = f_bwd / (bwd_ms * 1e-3) / 1e12
-        result["bwd"] = {"tflops": round(bwd_tflops, 2), "ms": round(bwd_ms, 4),
-                         "frac_of_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4)}
+        bwd_ms = kernel_ms["dq_kernel"] + kernel_ms["dkv_kernel"]
+        result["bwd"] = {"tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2), "ms": round(bwd_ms, 4),
+                         "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (~%.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(q, k, v, dout, cfg, args.cpu_seconds, with_bwd)

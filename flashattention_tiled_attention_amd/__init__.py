@@ -5,8 +5,8 @@ and streams, their data pointers and the current HIP stream go to the C entry
 points, and every step of the computation runs in the library's HIP kernels.
 There is no fallback: if ``libattn.so`` is missing, every call raises.
 
-Entry points with the C names (``attn_fwd``, ``attn_bwd``,
-``attn_bwd_workspace_bytes``, ``attn_status_str``) take caller-allocated
+Entry points with the C names (``attn_fwd``, ``attn_bwd``, ``attn_bwd_dq``,
+``attn_bwd_dkdv``, ``attn_bwd_workspace_bytes``, ``attn_status_str``) take caller-allocated
 tensors; ``fwd`` and ``bwd`` allocate their outputs with torch.
 """
 import ctypes
@@ -29,7 +29,8 @@ ATTN_ERR_SCALE = 7
 ATTN_ERR_HIP = 8
 ATTN_ERR_DEVICE = 9
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_bytes",
+                    "attn_status_str")
 
 
 class AttnError(RuntimeError):
@@ -54,8 +55,9 @@ def load_library(path=None):
     Z = ctypes.c_size_t
     lib.attn_fwd.argtypes = [V, V, V, V, V, I, I, I, I, I, I, F, V]
     lib.attn_fwd.restype = I
-    lib.attn_bwd.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, F, V, Z, V]
-    lib.attn_bwd.restype = I
+    for f in (lib.attn_bwd, lib.attn_bwd_dq, lib.attn_bwd_dkdv):
+        f.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, F, V, Z, V]
+        f.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_status_str.argtypes = [I]
@@ -122,8 +124,7 @@ def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal):
     return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, int(bool(causal))))
 
 
-def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
-    """C attn_bwd on torch tensors; dq/dk/dv are fp32; workspace is a uint8 GPU tensor."""
+def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream):
     import torch
     B, Hq, Hkv, S, D = _dims(q, k)
     for t, n, dt, sh in ((q, "q", torch.bfloat16, (B, Hq, S, D)), (k, "k", torch.bfloat16, (B, Hkv, S, D)),
@@ -135,11 +136,26 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream
     if workspace.device.type != "cuda":
         raise TypeError("workspace must be a GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                                 _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), float(scale),
-                                 _ptr(workspace), nbytes, _stream(stream))
+    rc = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), float(scale),
+                                       _ptr(workspace), nbytes, _stream(stream))
     if rc:
-        raise AttnError(rc, "attn_bwd")
+        raise AttnError(rc, name)
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
+    """C attn_bwd on torch tensors; dq/dk/dv are fp32; workspace is a uint8 GPU tensor."""
+    _bwd_call("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream)
+
+
+def attn_bwd_dq(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
+    """First backward stage: delta into the workspace and dq."""
+    _bwd_call("attn_bwd_dq", q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream)
+
+
+def attn_bwd_dkdv(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
+    """Second backward stage: dk and dv from the workspace's delta."""
+    _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream)
 
 
 def fwd(q, k, v, causal=False, scale=None):

@@ -124,10 +124,10 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal
     return delta_bytes(B, Hq, S);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
-             int D, int causal, float scale, void* workspace, size_t workspace_bytes,
-             void* stream) {
+static int bwd_stages(int stages, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv, int B,
+                      int Hq, int Hkv, int S, int D, int causal, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
     int rc = check_sizes(B, Hq, Hkv, S, D);
     if (rc) return rc;
@@ -158,8 +158,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     // Peaky softmax (score spread > 2 for unit-variance inputs): bf16 rounding of
     // P, dS and the stored O would dominate, so every tile takes the exact path.
     a.precise_all = fabsf(scale) * sqrtf((float)D) > 2.0f ? 1 : 0;
-    if (attn::launch_bwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+    if (attn::launch_bwd(a, D, stages, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
+             int D, int causal, float scale, void* workspace, size_t workspace_bytes,
+             void* stream) {
+    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, scale,
+                      workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
+                int D, int causal, float scale, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    return bwd_stages(1, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, scale,
+                      workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
+                  int D, int causal, float scale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    return bwd_stages(2, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, scale,
+                      workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -505,18 +505,23 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-    const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
-    const long long qblocks = (long long)a.B * a.Hq * nQ;
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)qblocks), dim3(kDqThreads),
-                       DqTile<D>::LDS_BYTES, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nKB = (a.S + kKvBK - 1) / kKvBK;
-    const long long kvblocks = (long long)a.B * a.Hkv * nKB;
-    hipLaunchKernelGGL((dkv_kernel<D, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKvThreads),
-                       KvTile<D>::LDS_BYTES, stream, a);
-    return hipGetLastError();
+hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
+    if (stages & 1) {
+        const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
+        const long long qblocks = (long long)a.B * a.Hq * nQ;
+        hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)qblocks), dim3(kDqThreads),
+                           DqTile<D>::LDS_BYTES, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (stages & 2) {
+        const int nKB = (a.S + kKvBK - 1) / kKvBK;
+        const long long kvblocks = (long long)a.B * a.Hkv * nKB;
+        hipLaunchKernelGGL((dkv_kernel<D, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKvThreads),
+                           KvTile<D>::LDS_BYTES, stream, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 template <typename K>
@@ -538,9 +543,10 @@ hipError_t bwd_setup_device() {
     return set_lds(dkv_kernel<128, true>, KvTile<128>::LDS_BYTES);
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream) {
-    if (D == 64) return a.causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
-    return a.causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, int stages, hipStream_t stream) {
+    if (D == 64)
+        return a.causal ? launch_bwd_t<64, true>(a, stages, stream) : launch_bwd_t<64, false>(a, stages, stream);
+    return a.causal ? launch_bwd_t<128, true>(a, stages, stream) : launch_bwd_t<128, false>(a, stages, stream);
 }
 
 }  // namespace attn

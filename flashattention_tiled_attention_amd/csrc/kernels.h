@@ -38,6 +38,7 @@ struct BwdArgs {
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream);
+// stages: bit 0 = dQ and delta, bit 1 = dK/dV (in that order when both are set)
+hipError_t launch_bwd(const BwdArgs& a, int D, int stages, hipStream_t stream);
 
 }  // namespace attn

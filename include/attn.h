@@ -95,6 +95,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int B, int Hq, int Hkv, int S, int D, int causal, float scale,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The two stages attn_bwd runs, for callers that schedule them separately
+ * (attn_bwd is exactly attn_bwd_dq followed by attn_bwd_dkdv on one stream).
+ * Arguments and errors are those of attn_bwd.
+ *   attn_bwd_dq    writes delta_i = sum_d dO_id O_id (exact sum_j P_ij dP_ij for
+ *                  rows whose visible keys all lie among the first 128) into the
+ *                  workspace, and dq = scale * dS K (section 2.1, Table 3, query
+ *                  gradient row). dk and dv are not touched.
+ *   attn_bwd_dkdv  reads delta from the workspace (it must hold attn_bwd_dq's
+ *                  result for the same inputs) and writes dk = scale * dS^T Q
+ *                  (Table 3, key gradient row) and dv = P^T dO, each summed over
+ *                  the query heads of its group. dq is not touched.
+ */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv,
+                int B, int Hq, int Hkv, int S, int D, int causal, float scale,
+                void* workspace, size_t workspace_bytes, void* stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, float* dq, float* dk, float* dv,
+                  int B, int Hq, int Hkv, int S, int D, int causal, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);
 

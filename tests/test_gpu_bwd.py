@@ -110,3 +110,25 @@ def test_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_stage_entry_points_match_attn_bwd():
+    """attn_bwd_dq followed by attn_bwd_dkdv gives exactly what attn_bwd gives."""
+    import torch
+    B, Hq, Hkv, S, D = 1, 8, 2, 700, 128
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 6, with_dout=True)
+    tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = fa.fwd(tq, tk, tv, causal=True)
+    ref = fa.bwd(tq, tk, tv, o, lse, tdo, causal=True)
+    dq = torch.full((B, Hq, S, D), float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.full((B, Hkv, S, D), float("nan"), dtype=torch.float32, device="cuda")
+    dv = torch.full((B, Hkv, S, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, True),), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    fa.attn_bwd_dq(tq, tk, tv, o, lse, tdo, dq, dk, dv, True, scale, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(dk).all() and torch.isnan(dv).all()   # stage 1 leaves dk, dv alone
+    fa.attn_bwd_dkdv(tq, tk, tv, o, lse, tdo, dq, dk, dv, True, scale, ws)
+    torch.cuda.synchronize()
+    for x, y in zip((dq, dk, dv), ref):
+        assert torch.equal(x, y)
