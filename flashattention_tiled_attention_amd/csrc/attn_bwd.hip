@@ -11,9 +11,10 @@
 // (ds_read_b64_tr_b16) from the row-major tile in LDS.
 //
 // Two kernels, ordered on the caller's stream, no atomics (deterministic):
-//   dq_kernel   one workgroup per (b, hq, 128-row query tile), K/V tiles streamed
-//               through double-buffered LDS as in the forward. It also computes
-//               delta for its rows and stores it in the workspace.
+//   dq_kernel   one workgroup per (b, hq, 128-row query tile); K/V tiles stream
+//               from HBM straight into double-buffered, swizzled LDS tiles
+//               (global_load_lds). It also computes delta for its rows and stores
+//               it in the workspace.
 //   dkv_kernel  one workgroup per (b, kv head, 64-key tile). K and V stay in
 //               registers; query/dO tiles of every query head of the group are
 //               streamed through LDS. Two wave pairs split the (head, query tile)
@@ -46,13 +47,14 @@ constexpr int kDqThreads = 256;
 
 template <int D>
 struct DqTile {
-    static constexpr int VP = D + 8;     // V: row reads only, padded
-    static constexpr int KTILE = kDqBK * D;  // K: row and transpose reads, swizzled (swz)
-    static constexpr int VTILE = kDqBK * VP;
-    static constexpr int STAGE = KTILE + VTILE;
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    // K and V tiles: unpadded [64][D] bf16 in the chunk order of swz<D> (the
+    // direct copies need 1 KB contiguous runs; swz keeps the K row reads, the K
+    // transpose reads and the V row reads free of bank conflicts).
+    static constexpr int TILE = kDqBK * D;
+    static constexpr int LDS_BYTES = 4 * TILE * 2;                // 2 K slots + 2 V slots
     static constexpr int CH = D / 8;
-    static constexpr int NLD = kDqBK * CH / kDqThreads;
+    static constexpr int ROWS_PER_COPY = 64 / CH;
+    static constexpr int COPIES = kDqBK / ROWS_PER_COPY / 4;      // per wave per tensor
 };
 
 __device__ __forceinline__ void decode_q_item(int bid, int nQ, int B, int Hkv, int G, bool causal,
@@ -80,13 +82,14 @@ __device__ __forceinline__ void decode_q_item(int bid, int nQ, int B, int Hkv, i
 __device__ __forceinline__ float bf_lo(float x) { return x - (float)(__bf16)x; }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
     using T = DqTile<D>;
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int S = a.S;
     const int nQ = (S + kDqBQ - 1) / kDqBQ;
@@ -134,68 +137,76 @@ __global__ void __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) dq_kernel(BwdArgs
     int wjend = CAUSAL ? min(jend, (q0 + 32 * wave + 31) / kDqBK + 1) : jend;
     if (q0 + 32 * wave >= S) wjend = 0;
 
-    u32x4 kst[T::NLD], vst[T::NLD];
-    auto gload = [&](int j) {
+    __bf16* const Kring = smem;
+    __bf16* const Vring = smem + 2 * T::TILE;
+    // Direct copies (as in the forward): rows past the end repeat row S-1; those
+    // keys are masked (probability 0) on the last tile.
+    int crow[T::COPIES], ccol[T::COPIES];
+#pragma unroll
+    for (int n = 0; n < T::COPIES; ++n) {
+        crow[n] = (wave * T::COPIES + n) * T::ROWS_PER_COPY + lane / T::CH;
+        ccol[n] = (((lane % T::CH) ^ swz_f<D>(crow[n]))) * 8;
+    }
+    auto copy_tile = [&](const uint16_t* src, __bf16* dst, int j) {
         const int k0 = j * kDqBK;
 #pragma unroll
-        for (int i = 0; i < T::NLD; ++i) {
-            const int ch = tid + kDqThreads * i, row = ch / T::CH, col = (ch % T::CH) * 8;
-            const int key = k0 + row;
-            if (key < S) {
-                kst[i] = *(const u32x4*)(Kp + (size_t)key * D + col);
-                vst[i] = *(const u32x4*)(Vp + (size_t)key * D + col);
-            } else {
-                kst[i] = u32x4{0, 0, 0, 0};
-                vst[i] = u32x4{0, 0, 0, 0};
-            }
+        for (int n = 0; n < T::COPIES; ++n) {
+            const int key = min(k0 + crow[n], S - 1);
+            copy16_to_lds(src + (size_t)key * D + ccol[n], dst + (wave * T::COPIES + n) * 512);
         }
     };
-    auto lstore = [&](int stage) {
-        __bf16* Ks = smem + stage * T::STAGE;
-        __bf16* Vs = Ks + T::KTILE;
+    // Per-lane LDS offsets: K/V rows (A operands of S^T and dP^T) per k-step, and
+    // K transpose quads per 32-column block and row half (row offsets that are
+    // multiples of 16 are added as constants).
+    int roff[DK], toff[2][DB];
 #pragma unroll
-        for (int i = 0; i < T::NLD; ++i) {
-            const int ch = tid + kDqThreads * i, row = ch / T::CH, col = (ch % T::CH) * 8;
-            *(u32x4*)(Ks + swz<D>(row, col)) = kst[i];
-            *(u32x4*)(Vs + row * T::VP + col) = vst[i];
-        }
-    };
+    for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
 
     // Pass 0 (precise tiles only) accumulates the exact delta; the last pass
-    // forms dS and accumulates dQ^T += K^T dS^T.
+    // forms dS and accumulates dQ^T += K^T dS^T. Tile j+1 is copied into the other
+    // slot while tile j is multiplied.
     for (int pass = precise ? 0 : 1; pass < 2; ++pass) {
         float dacc = 0.0f;
-        gload(0);
-        lstore(0);
+        copy_tile(Kp, Kring, 0);
+        copy_tile(Vp, Vring, 0);
+        wait_copies();
         __syncthreads();
         for (int j = 0; j < jend; ++j) {
-            if (j + 1 < jend) gload(j + 1);
+            if (j + 1 < jend) {
+                copy_tile(Kp, Kring + ((j + 1) & 1) * T::TILE, j + 1);
+                copy_tile(Vp, Vring + ((j + 1) & 1) * T::TILE, j + 1);
+            }
             if (j < wjend) {
-                const __bf16* Ks = smem + (j & 1) * T::STAGE;
-                const __bf16* Vs = Ks + T::KTILE;
+                const __bf16* Ks = Kring + (j & 1) * T::TILE;
+                const __bf16* Vs = Vring + (j & 1) * T::TILE;
                 const int k0 = j * kDqBK;
-                const bool need_mask = CAUSAL && (k0 + kDqBK - 1 > q0 + 32 * wave);
+                const bool need_mask = j == wjend - 1;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                     for (int dk = 0; dk < DK; ++dk) {
-                        const bf16x8 kf = lds_read8(Ks + swz<D>(kb * 32 + l32, dk * 16 + 8 * h));
-                        const bf16x8 vf = lds_read8(Vs + (kb * 32 + l32) * T::VP + dk * 16 + 8 * h);
+                        const bf16x8 kf = lds_read8(Ks + roff[dk] + kb * 32 * D);
+                        const bf16x8 vf = lds_read8(Vs + roff[dk] + kb * 32 * D);
                         s = mfma32(kf, qf[dk], s);
                         dp = mfma32(vf, df[dk], dp);
                     }
+                    // key k0 + kb*32 + 4h + off is visible iff off <= lim
+                    const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - k0 - kb * 32 - 4 * h;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float p = fast_exp2(fmaf(s[r], c, -lse2));
-                        if (need_mask) {
-                            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                            p = key <= qrow ? p : 0.0f;
-                        }
+                        if (need_mask && 8 * (r >> 2) + (r & 3) > lim) p = 0.0f;
                         if (pass == 0) dacc += p * dp[r];
                         s[r] = p * (dp[r] - delta);
                     }
@@ -210,19 +221,18 @@ __global__ void __launch_bounds__(kDqThreads, D == 64 ? 2 : 1) dq_kernel(BwdArgs
                         if (precise)
                             lo = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
                                        bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]), bf_lo(s[r0 + 7]));
-                        const int trow = kb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2);
-                        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                        const int rb = (kb * 32 + 16 * t2) * D;
 #pragma unroll
                         for (int db = 0; db < DB; ++db) {
-                            const bf16x8 kt = concat(lds_read_tr(Ks + swz<D>(trow, tcol + db * 32)),
-                                                     lds_read_tr(Ks + swz<D>(trow + 8, tcol + db * 32)));
+                            const bf16x8 kt = concat(lds_read_tr(Ks + toff[0][db] + rb),
+                                                     lds_read_tr(Ks + toff[1][db] + rb));
                             dq[db] = mfma32(kt, hi, dq[db]);
                             if (precise) dq[db] = mfma32(kt, lo, dq[db]);
                         }
                     }
                 }
             }
-            if (j + 1 < jend) lstore((j + 1) & 1);
+            wait_copies();
             __syncthreads();
         }
         if (pass == 0) delta = halves_sum(dacc);
