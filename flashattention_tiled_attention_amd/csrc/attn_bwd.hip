@@ -15,11 +15,12 @@
 //               from HBM straight into double-buffered, swizzled LDS tiles
 //               (global_load_lds). It also computes delta for its rows and stores
 //               it in the workspace.
-//   dkv_kernel  one workgroup per (b, kv head, 64-key tile). K and V stay in
-//               registers; query/dO tiles of every query head of the group are
-//               streamed through LDS. Two wave pairs split the (head, query tile)
-//               iterations and their dK/dV partial sums are added in LDS at the
-//               end, so the grouped-query sum never leaves the chip.
+//   dkv_kernel  one workgroup of 8 waves per (b, kv head, 64-key tile). K stays
+//               in registers and V in LDS; 32-row Q/dO tiles of every query head of
+//               the group stream from HBM into double-buffered LDS. Four wave pairs
+//               split the (head, query tile) iterations and their dK/dV partial
+//               sums are added in LDS at the end in a fixed order, so the
+//               grouped-query sum never leaves the chip and is deterministic.
 //
 // Rows whose visible keys all lie in the first 128 keys (the first query tile
 // of a causal problem, or every row when S <= 128) can carry probabilities near
@@ -259,19 +260,28 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK/dV kernel
 // ---------------------------------------------------------------------------
-constexpr int kKvBK = 64;    // keys per workgroup (2 waves x 32)
-constexpr int kKvBQ = 64;    // query rows per streamed tile
-constexpr int kKvThreads = 256;
+constexpr int kKvBK = 64;      // keys per workgroup (2 waves x 32)
+constexpr int kKvBQ = 32;      // query rows per streamed tile
+constexpr int kKvSplits = 4;   // wave pairs that split the (head, query tile) iterations
+constexpr int kKvThreads = 64 * 2 * kKvSplits;
 
 template <int D>
 struct KvTile {
-    static constexpr int QTILE = kKvBQ * D;                // Q / dO tile, swizzled (swz), elements
-    static constexpr int STAGE_BYTES = 2 * QTILE * 2 + 2 * kKvBQ * 4;  // Q, dO, lse*log2e, delta
-    static constexpr int PAIR_BYTES = 2 * STAGE_BYTES;     // double buffered
-    static constexpr int XCHG_BYTES = 2 * 2 * (D / 32) * 16 * 64 * 4;  // 2 waves x dK,dV partials
-    static constexpr int LDS_BYTES = (2 * PAIR_BYTES > XCHG_BYTES) ? 2 * PAIR_BYTES : XCHG_BYTES;
+    // V tile [64][D] and per-split double-buffered Q / dO tiles [32][D], all bf16
+    // in the swizzled chunk order of swz<D>; lse*log2e and delta per query row.
     static constexpr int CH = D / 8;
-    static constexpr int NLD = kKvBQ * CH / 128;           // chunks per thread of a pair, per tensor
+    static constexpr int ROWS_PER_COPY = 64 / CH;                    // rows per 1 KB copy
+    static constexpr int QTILE = kKvBQ * D;                          // elements
+    static constexpr int STAGE_BYTES = 2 * QTILE * 2 + 2 * kKvBQ * 4;
+    static constexpr int SPLIT_BYTES = 2 * STAGE_BYTES;
+    static constexpr int VTILE_BYTES = kKvBK * D * 2;
+    static constexpr int TILE_BYTES = VTILE_BYTES + kKvSplits * SPLIT_BYTES;
+    // final sum: two splits hand over dK and dV of both key halves
+    static constexpr int XCHG_BYTES = 2 * 2 * 2 * (D / 32) * 16 * 64 * 4;
+    static constexpr int LDS_BYTES = TILE_BYTES > XCHG_BYTES ? TILE_BYTES : XCHG_BYTES;
+    static constexpr int QCOPIES = kKvBQ / ROWS_PER_COPY / 2;        // per wave of a pair, per tensor
+    static constexpr int VCOPIES = kKvBK / ROWS_PER_COPY / (2 * kKvSplits);  // per wave
+    static_assert(QCOPIES >= 1 && VCOPIES >= 1, "copy split");
 };
 
 template <int D, bool CAUSAL>
@@ -281,9 +291,10 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     constexpr int DB = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
-    const int pair = wave >> 1, w2 = wave & 1, ptid = tid & 127;
+    const int split = wave >> 1, w2 = wave & 1, ptid = tid & 127;
     const int S = a.S, G = a.G;
     const int nQB = (S + kKvBQ - 1) / kKvBQ;
 
@@ -294,9 +305,9 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
         const int C = a.B * a.Hkv, bid = blockIdx.x;
         int rank, cgrp;
         if ((C & 7) == 0) {
-            const int x = bid & 7, s = bid >> 3, per = C >> 3;
-            rank = s / per;
-            cgrp = (s - rank * per) * 8 + x;
+            const int x = bid & 7, st = bid >> 3, per = C >> 3;
+            rank = st / per;
+            cgrp = (st - rank * per) * 8 + x;
         } else {
             rank = bid / C;
             cgrp = bid - rank * C;
@@ -312,57 +323,64 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     const float c = a.scale_log2;
     const bool precise_problem = CAUSAL || S <= kPreciseRows;
 
-    // K and V rows of this lane's key as B operands (zero past the end).
-    bf16x8 kf[DK], vf[DK];
+    // K rows of this lane's key as B operands (zero past the end).
+    bf16x8 kf[DK];
     if (key < S) {
         const u32x4* ks = (const u32x4*)(a.k + (kvrow + key) * D + 8 * h);
-        const u32x4* vs = (const u32x4*)(a.v + (kvrow + key) * D + 8 * h);
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) {
-            kf[dk] = __builtin_bit_cast(bf16x8, ks[2 * dk]);
-            vf[dk] = __builtin_bit_cast(bf16x8, vs[2 * dk]);
-        }
+        for (int dk = 0; dk < DK; ++dk) kf[dk] = __builtin_bit_cast(bf16x8, ks[2 * dk]);
     } else {
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) {
-            kf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-            vf[dk] = kf[dk];
-        }
+        for (int dk = 0; dk < DK; ++dk) kf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
 
-    // Iterations: (g, query tile qi) for qi >= first visible tile; pair p takes
-    // iterations p, p+2, ...
+    // LDS: V tile, then per split two stages of {Q, dO, lse*log2e, delta}.
+    __bf16* const Vs = (__bf16*)lds_raw;
+    unsigned char* const split_base = lds_raw + T::VTILE_BYTES + split * T::SPLIT_BYTES;
+    auto stage_q = [&](int st) { return (__bf16*)(split_base + st * T::STAGE_BYTES); };
+    auto stage_do = [&](int st) { return stage_q(st) + T::QTILE; };
+    auto stage_lse = [&](int st) { return (float*)(split_base + st * T::STAGE_BYTES + 2 * T::QTILE * 2); };
+    auto stage_dl = [&](int st) { return stage_lse(st) + kKvBQ; };
+
+    // V tile: every wave copies VCOPIES rows-runs (rows past the end repeat S-1;
+    // those keys' columns are never stored).
+#pragma unroll
+    for (int n = 0; n < T::VCOPIES; ++n) {
+        const int row = (wave * T::VCOPIES + n) * T::ROWS_PER_COPY + lane / T::CH;
+        const int col = (((lane % T::CH) ^ swz_f<D>(row))) * 8;
+        const int kr = min(kv0 + row, S - 1);
+        copy16_to_lds(a.v + (kvrow + kr) * D + col, Vs + (wave * T::VCOPIES + n) * 512);
+    }
+
+    // Iterations: (g, query tile qi) for qi >= first visible tile; split p takes
+    // iterations p, p + kKvSplits, ...
     const int qi_first = CAUSAL ? kv0 / kKvBQ : 0;
     const int per_g = nQB - qi_first;
     const int total = G * per_g;
-    const int steps = (total + 1) / 2;
+    const int steps = (total + kKvSplits - 1) / kKvSplits;
 
-    unsigned char* pair_base = lds_raw + pair * T::PAIR_BYTES;
-    auto stage_q = [&](int st) { return (__bf16*)(pair_base + st * T::STAGE_BYTES); };
-    auto stage_do = [&](int st) { return (__bf16*)(pair_base + st * T::STAGE_BYTES) + T::QTILE; };
-    auto stage_lse = [&](int st) { return (float*)(pair_base + st * T::STAGE_BYTES + 2 * T::QTILE * 2); };
-    auto stage_dl = [&](int st) { return stage_lse(st) + kKvBQ; };
-
-    u32x4 qst[T::NLD], dst_[T::NLD];
+    // Q / dO copies of a pair: copy n of wave w2 fills tile rows (w2*QCOPIES + n) *
+    // ROWS_PER_COPY + lane / CH. Rows past S repeat row S-1; their lse is +inf,
+    // so their probabilities, and every term they touch, are exactly 0.
+    int qcrow[T::QCOPIES], qccol[T::QCOPIES];
+#pragma unroll
+    for (int n = 0; n < T::QCOPIES; ++n) {
+        qcrow[n] = (w2 * T::QCOPIES + n) * T::ROWS_PER_COPY + lane / T::CH;
+        qccol[n] = (((lane % T::CH) ^ swz_f<D>(qcrow[n]))) * 8;
+    }
     float lst = 0.f, dlst = 0.f;
-    auto gload = [&](int step) {
-        const int it = 2 * step + pair;
+    auto fetch = [&](int step) {  // async copies of Q/dO + lse/delta into registers
+        const int it = kKvSplits * step + split;
         if (it >= total) return;
+        const int st = step & 1;
         const int g = it / per_g, qi = qi_first + it % per_g;
-        const int hq = hkv * G + g;
-        const size_t rb = ((size_t)b * a.Hq + hq) * (size_t)S;
+        const size_t rb = ((size_t)b * a.Hq + hkv * G + g) * (size_t)S;
         const int qr0 = qi * kKvBQ;
 #pragma unroll
-        for (int i = 0; i < T::NLD; ++i) {
-            const int ch = ptid + 128 * i, row = ch / T::CH, col = (ch % T::CH) * 8;
-            const int qr = qr0 + row;
-            if (qr < S) {
-                qst[i] = *(const u32x4*)(a.q + (rb + qr) * D + col);
-                dst_[i] = *(const u32x4*)(a.dout + (rb + qr) * D + col);
-            } else {
-                qst[i] = u32x4{0, 0, 0, 0};
-                dst_[i] = u32x4{0, 0, 0, 0};
-            }
+        for (int n = 0; n < T::QCOPIES; ++n) {
+            const size_t off = (rb + min(qr0 + qcrow[n], S - 1)) * D + qccol[n];
+            copy16_to_lds(a.q + off, stage_q(st) + (w2 * T::QCOPIES + n) * 512);
+            copy16_to_lds(a.dout + off, stage_do(st) + (w2 * T::QCOPIES + n) * 512);
         }
         if (ptid < kKvBQ) {
             const int qr = qr0 + ptid;
@@ -370,23 +388,26 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
             dlst = qr < S ? a.delta[rb + qr] : 0.0f;
         }
     };
-    auto lstore = [&](int step) {
-        const int it = 2 * step + pair;
+    auto publish = [&](int step) {  // row statistics into the stage the copies fill
+        const int it = kKvSplits * step + split;
         if (it >= total) return;
-        const int st = step & 1;
-        __bf16* Qs = stage_q(st);
-        __bf16* Ds = stage_do(st);
-#pragma unroll
-        for (int i = 0; i < T::NLD; ++i) {
-            const int ch = ptid + 128 * i, row = ch / T::CH, col = (ch % T::CH) * 8;
-            *(u32x4*)(Qs + swz<D>(row, col)) = qst[i];
-            *(u32x4*)(Ds + swz<D>(row, col)) = dst_[i];
-        }
         if (ptid < kKvBQ) {
-            stage_lse(st)[ptid] = lst;
-            stage_dl(st)[ptid] = dlst;
+            stage_lse(step & 1)[ptid] = lst;
+            stage_dl(step & 1)[ptid] = dlst;
         }
     };
+
+    // Per-lane LDS offsets: A-operand rows (Q, dO, V) per k-step; transpose quads
+    // (Q^T, dO^T) per 32-column block and row half.
+    int roff[DK], toff[2][DB];
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -395,77 +416,66 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
         dv[db] = zero16();
     }
 
-    gload(0);
-    lstore(0);
+    fetch(0);
+    publish(0);
+    wait_copies();
     __syncthreads();
     for (int step = 0; step < steps; ++step) {
-        if (step + 1 < steps) gload(step + 1);
-        const int it = 2 * step + pair;
+        if (step + 1 < steps) fetch(step + 1);
+        const int it = kKvSplits * step + split;
         if (it < total) {
             const int st = step & 1;
             const __bf16* Qs = stage_q(st);
             const __bf16* Ds = stage_do(st);
             const float* Ls = stage_lse(st);
             const float* Dl = stage_dl(st);
-            const int qi = qi_first + it % per_g;
-            const int qr0 = qi * kKvBQ;
-            const bool precise = a.precise_all || (precise_problem && qr0 < kPreciseRows);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int qs0 = qr0 + 32 * qb;
-                if (CAUSAL && qs0 + 31 < kw0) continue;  // every query precedes every key
-                if (qs0 >= S) continue;
+            const int qs0 = (qi_first + it % per_g) * kKvBQ;
+            const bool precise = a.precise_all || (precise_problem && qs0 < kPreciseRows);
+            const bool skip = (CAUSAL && qs0 + 31 < kw0) || qs0 >= S;  // every query precedes every key
+            if (!skip) {
                 const bool need_mask = CAUSAL && qs0 < kw0 + 31;
                 f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                 for (int dd = 0; dd < DK; ++dd) {
-                    const int ro = swz<D>(qb * 32 + l32, dd * 16 + 8 * h);
-                    const bf16x8 qa = lds_read8(Qs + ro);
-                    const bf16x8 da = lds_read8(Ds + ro);
+                    const bf16x8 qa = lds_read8(Qs + roff[dd]);
+                    const bf16x8 da = lds_read8(Ds + roff[dd]);
+                    const bf16x8 vb = lds_read8(Vs + roff[dd] + w2 * 32 * D);
                     s = mfma32(qa, kf[dd], s);
-                    dp = mfma32(da, vf[dd], dp);
+                    dp = mfma32(da, vb, dp);
                 }
-                // rows of s/dp are queries qb*32 + 8(r/4) + 4h + r%4; the column is this lane's key
-                float pv[16];
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const f32x4 l4 = *(const f32x4*)(Ls + qb * 32 + 8 * rg + 4 * h);
-                    const f32x4 d4 = *(const f32x4*)(Dl + qb * 32 + 8 * rg + 4 * h);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * rg + e;
-                        float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-                        if (need_mask) {
-                            const int qrow = qs0 + 8 * rg + 4 * h + e;
-                            p = key <= qrow ? p : 0.0f;
-                        }
-                        pv[r] = p;
-                        s[r] = p * (dp[r] - d4[e]);
-                    }
-                }
-                // dV^T += dO^T P and dK^T += Q^T dS over two 16-query steps; dO^T and
-                // Q^T via transpose loads of the row-major tiles.
+                // rows of s/dp are queries 8(r/4) + 4h + r%4; the column is this lane's key.
+                // dV^T += dO^T P and dK^T += Q^T dS over two 16-query steps.
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2) {
-                    const int r0 = 8 * t2;
-                    const bf16x8 ph = pack8(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4], pv[r0 + 5],
-                                            pv[r0 + 6], pv[r0 + 7]);
-                    const bf16x8 sh = pack8(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5],
-                                            s[r0 + 6], s[r0 + 7]);
+                    float pv[8], dsv[8];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int rg = 2 * t2 + half;
+                        const f32x4 l4 = *(const f32x4*)(Ls + 8 * rg + 4 * h);
+                        const f32x4 d4 = *(const f32x4*)(Dl + 8 * rg + 4 * h);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * rg + e;
+                            float p = fast_exp2(fmaf(s[r], c, -l4[e]));
+                            if (need_mask && key > qs0 + 8 * rg + 4 * h + e) p = 0.0f;
+                            pv[4 * half + e] = p;
+                            dsv[4 * half + e] = p * (dp[r] - d4[e]);
+                        }
+                    }
+                    const bf16x8 ph = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+                    const bf16x8 sh = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
                     bf16x8 pl, sl;
                     if (precise) {
-                        pl = pack8(bf_lo(pv[r0]), bf_lo(pv[r0 + 1]), bf_lo(pv[r0 + 2]), bf_lo(pv[r0 + 3]),
-                                   bf_lo(pv[r0 + 4]), bf_lo(pv[r0 + 5]), bf_lo(pv[r0 + 6]), bf_lo(pv[r0 + 7]));
-                        sl = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
-                                   bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]), bf_lo(s[r0 + 7]));
+                        pl = pack8(bf_lo(pv[0]), bf_lo(pv[1]), bf_lo(pv[2]), bf_lo(pv[3]), bf_lo(pv[4]),
+                                   bf_lo(pv[5]), bf_lo(pv[6]), bf_lo(pv[7]));
+                        sl = pack8(bf_lo(dsv[0]), bf_lo(dsv[1]), bf_lo(dsv[2]), bf_lo(dsv[3]), bf_lo(dsv[4]),
+                                   bf_lo(dsv[5]), bf_lo(dsv[6]), bf_lo(dsv[7]));
                     }
-                    const int trow = qb * 32 + 16 * t2 + 4 * h + ((lane & 15) >> 2);
-                    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                    const int rb = 16 * t2 * D;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const int o1 = swz<D>(trow, tcol + db * 32), o2 = swz<D>(trow + 8, tcol + db * 32);
-                        const bf16x8 dot = concat(lds_read_tr(Ds + o1), lds_read_tr(Ds + o2));
-                        const bf16x8 qt = concat(lds_read_tr(Qs + o1), lds_read_tr(Qs + o2));
+                        const bf16x8 dot = concat(lds_read_tr(Ds + toff[0][db] + rb), lds_read_tr(Ds + toff[1][db] + rb));
+                        const bf16x8 qt = concat(lds_read_tr(Qs + toff[0][db] + rb), lds_read_tr(Qs + toff[1][db] + rb));
                         dv[db] = mfma32(dot, ph, dv[db]);
                         dk[db] = mfma32(qt, sh, dk[db]);
                         if (precise) {
@@ -476,27 +486,53 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                 }
             }
         }
-        if (step + 1 < steps) lstore(step + 1);
+        if (step + 1 < steps) publish(step + 1);
+        wait_copies();
         __syncthreads();
     }
 
-    // Sum the two wave pairs' partials (same keys, disjoint iterations): pair 0
-    // finishes dK, pair 1 finishes dV. Layout [w2][tensor][db][r][lane].
+    // Sum the four splits' partials (same keys, disjoint iterations) in a fixed
+    // order: splits 2,3 hand over to splits 0,1; then split 1 hands dK to split 0
+    // and split 0 hands dV to split 1. Layout [slot][w2][tensor][db][r][lane].
     float* xchg = (float*)lds_raw;
-    auto slot = [&](int ww, int tensor, int db, int r) {
-        return xchg + ((((ww * 2 + tensor) * DB + db) * 16 + r) * 64) + lane;
+    auto slot = [&](int sl, int tensor, int db, int r) {
+        return xchg + (((((sl * 2 + w2) * 2 + tensor) * DB + db) * 16 + r) * 64) + lane;
     };
+    if (split >= 2) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            if (pair == 1) *slot(w2, 0, db, r) = dk[db][r];   // pair 1 hands over dK
-            else *slot(w2, 1, db, r) = dv[db][r];             // pair 0 hands over dV
-        }
+            for (int r = 0; r < 16; ++r) {
+                *slot(split - 2, 0, db, r) = dk[db][r];
+                *slot(split - 2, 1, db, r) = dv[db][r];
+            }
+    }
     __syncthreads();
-    if (key < S) {
-        float* out = (pair == 0 ? a.dk : a.dv) + (kvrow + key) * D;
-        const float sc = pair == 0 ? a.scale : 1.0f;
+    if (split < 2) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dk[db][r] += *slot(split, 0, db, r);
+                dv[db][r] += *slot(split, 1, db, r);
+            }
+    }
+    __syncthreads();
+    if (split == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) *slot(0, 0, db, r) = dk[db][r];
+    } else if (split == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) *slot(1, 1, db, r) = dv[db][r];
+    }
+    __syncthreads();
+    if (split < 2 && key < S) {
+        float* out = (split == 0 ? a.dk : a.dv) + (kvrow + key) * D;
+        const float sc = split == 0 ? a.scale : 1.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -505,8 +541,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g4 + e;
-                    const float mine = pair == 0 ? dk[db][r] : dv[db][r];
-                    const float other = *slot(w2, pair == 0 ? 0 : 1, db, r);
+                    const float mine = split == 0 ? dk[db][r] : dv[db][r];
+                    const float other = split == 0 ? *slot(0, 0, db, r) : *slot(1, 1, db, r);
                     v[e] = (mine + other) * sc;
                 }
                 *(f32x4*)(out + db * 32 + 8 * g4 + 4 * h) = v;
