@@ -58,8 +58,10 @@ struct DqTile {
     static constexpr int COPIES = kDqBK / ROWS_PER_COPY / 4;      // per wave per tensor
 };
 
-__device__ __forceinline__ void decode_q_item(int bid, int nQ, int B, int Hkv, int G, bool causal,
-                                              int& b, int& hq, int& qt) {
+// Work item of workgroup `bid` among nQ query-tile ranks: rank r is query tile
+// qt_first - r when causal (longest first), qt_first + r otherwise.
+__device__ __forceinline__ void decode_q_item(int bid, int nQ, int qt_first, int B, int Hkv, int G,
+                                              bool causal, int& b, int& hq, int& qt) {
     const int C = B * Hkv;
     int rank, c, g;
     if ((C & 7) == 0) {
@@ -75,15 +77,17 @@ __device__ __forceinline__ void decode_q_item(int bid, int nQ, int B, int Hkv, i
         c = rem / G;
         g = rem % G;
     }
-    qt = causal ? nQ - 1 - rank : rank;
+    qt = causal ? qt_first - rank : qt_first + rank;
     b = c / Hkv;
     hq = (c % Hkv) * G + g;
 }
 
 __device__ __forceinline__ float bf_lo(float x) { return x - (float)(__bf16)x; }
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
+// PRECISE instances run the tiles whose rows need the exact path (below);
+// the others never carry its registers.
+template <int D, bool CAUSAL, bool PRECISE>
+__global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a, int nq_launch, int qt_first) {
     using T = DqTile<D>;
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
@@ -93,9 +97,8 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int S = a.S;
-    const int nQ = (S + kDqBQ - 1) / kDqBQ;
     int b, hq, qt;
-    decode_q_item(blockIdx.x, nQ, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
+    decode_q_item(blockIdx.x, nq_launch, qt_first, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
     const int hkv = hq / a.G;
     const size_t rowbase = ((size_t)b * a.Hq + hq) * (size_t)S;
     const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
@@ -105,7 +108,7 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
     const int qrow = q0 + 32 * wave + l32;
     const bool live = qrow < S;
     const float c = a.scale_log2;
-    const bool precise = a.precise_all || ((qt == 0) && (CAUSAL || S <= kPreciseRows));
+    constexpr bool precise = PRECISE;
 
     // Q and dO rows as B operands; delta = rowsum(dO * O) from the stored O.
     bf16x8 qf[DK], df[DK];
@@ -153,7 +156,7 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int n = 0; n < T::COPIES; ++n) {
             const int key = min(k0 + crow[n], S - 1);
-            copy16_to_lds(src + (size_t)key * D + ccol[n], dst + (wave * T::COPIES + n) * 512);
+            copy16_to_lds(src + (uint32_t)(key * D + ccol[n]), dst + (wave * T::COPIES + n) * 512);
         }
     };
     // Per-lane LDS offsets: K/V rows (A operands of S^T and dP^T) per k-step, and
@@ -553,12 +556,32 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     if (stages & 1) {
+        // Query tiles whose rows need the exact path: all of them when asked for,
+        // else tile 0 of a causal problem or the single tile of S <= 128.
         const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
-        const long long qblocks = (long long)a.B * a.Hq * nQ;
-        hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)qblocks), dim3(kDqThreads),
-                           DqTile<D>::LDS_BYTES, stream, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        const long long heads = (long long)a.B * a.Hq;
+        int np, pfirst, nm, mfirst;  // (ranks, first tile) of the exact and plain launches
+        if (a.precise_all) {
+            np = nQ; pfirst = CAUSAL ? nQ - 1 : 0; nm = 0; mfirst = 0;
+        } else if (CAUSAL) {
+            np = 1; pfirst = 0; nm = nQ - 1; mfirst = nQ - 1;
+        } else if (a.S <= kPreciseRows) {
+            np = 1; pfirst = 0; nm = 0; mfirst = 0;
+        } else {
+            np = 0; pfirst = 0; nm = nQ; mfirst = 0;
+        }
+        if (nm > 0) {
+            hipLaunchKernelGGL((dq_kernel<D, CAUSAL, false>), dim3((unsigned)(heads * nm)), dim3(kDqThreads),
+                               DqTile<D>::LDS_BYTES, stream, a, nm, mfirst);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (np > 0) {
+            hipLaunchKernelGGL((dq_kernel<D, CAUSAL, true>), dim3((unsigned)(heads * np)), dim3(kDqThreads),
+                               DqTile<D>::LDS_BYTES, stream, a, np, pfirst);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     if (stages & 2) {
         const int nKB = (a.S + kKvBK - 1) / kKvBK;
@@ -579,10 +602,14 @@ hipError_t set_lds(K kernel, int bytes) {
 
 hipError_t bwd_setup_device() {
     hipError_t e;
-    if ((e = set_lds(dq_kernel<64, false>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<64, true>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, false>, DqTile<128>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, true>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<64, false, false>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<64, false, true>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<64, true, false>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<64, true, true>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, false, false>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, false, true>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, true, false>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, true, true>, DqTile<128>::LDS_BYTES))) return e;
     if ((e = set_lds(dkv_kernel<64, false>, KvTile<64>::LDS_BYTES))) return e;
     if ((e = set_lds(dkv_kernel<64, true>, KvTile<64>::LDS_BYTES))) return e;
     if ((e = set_lds(dkv_kernel<128, false>, KvTile<128>::LDS_BYTES))) return e;

@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int n = 0; n < T::COPIES; ++n) {
             const int key = min(k0 + crow[n], S - 1);
-            copy16_to_lds(src + (size_t)key * D + ccol[n], dst + (wave * T::COPIES + n) * 512);
+            copy16_to_lds(src + (uint32_t)(key * D + ccol[n]), dst + (wave * T::COPIES + n) * 512);
         }
     };
     // Per-lane read offsets (elements) into a slot: K rows (b128, A operand) for
