@@ -67,11 +67,11 @@ class Oracle:
         I64 = ctypes.c_int64
         Dbl = ctypes.c_double
         lib.oracle_num_threads.restype = I
-        lib.oracle_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, Dbl]
-        lib.oracle_attn_fwd_rows.argtypes = [P, P, P, P, I64, P, P, I, I, I, I, I, I, Dbl]
-        lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, Dbl]
+        lib.oracle_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_attn_fwd_rows.argtypes = [P, P, P, P, I64, P, P, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, Dbl]
         lib.oracle_attn_bwd_rows.argtypes = [P, P, P, P, P, I64, P, P, I64, P, P,
-                                             I, I, I, I, I, I, Dbl]
+                                             I, I, I, I, I, I, I, Dbl]
         for f in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_attn_bwd,
                   lib.oracle_attn_bwd_rows):
             f.restype = I
@@ -82,18 +82,19 @@ class Oracle:
         """OpenMP threads the oracle uses (honours OMP_NUM_THREADS)."""
         return self.lib.oracle_num_threads()
 
-    def fwd(self, q, k, v, causal, scale):
-        """O [B,Hq,S,D] and lse [B,Hq,S] (natural log), float64."""
+    def fwd(self, q, k, v, causal, scale, window=0):
+        """O [B,Hq,S,D] and lse [B,Hq,S] (natural log), float64. window > 0 (causal only):
+        query i sees keys i-window+1 .. i."""
         B, Hq, Hkv, S, D = _shapes(q, k, v)
         o = np.empty((B, Hq, S, D), np.float64)
         lse = np.empty((B, Hq, S), np.float64)
         rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                      B, Hq, Hkv, S, D, int(bool(causal)), float(scale))
+                                      B, Hq, Hkv, S, D, int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_fwd failed: %d" % rc)
         return o, lse
 
-    def fwd_rows(self, q, k, v, rows, causal, scale):
+    def fwd_rows(self, q, k, v, rows, causal, scale, window=0):
         """O and lse of selected flat query rows ((b*Hq + hq)*S + i)."""
         B, Hq, Hkv, S, D = _shapes(q, k, v)
         rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -101,12 +102,12 @@ class Oracle:
         lse = np.empty((rows.size,), np.float64)
         rc = self.lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(rows), rows.size,
                                            _ptr(o), _ptr(lse), B, Hq, Hkv, S, D,
-                                           int(bool(causal)), float(scale))
+                                           int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_fwd_rows failed: %d" % rc)
         return o, lse
 
-    def bwd(self, q, k, v, dout, causal, scale):
+    def bwd(self, q, k, v, dout, causal, scale, window=0):
         """dQ [B,Hq,S,D] and dK, dV [B,Hkv,S,D] (summed over each group), float64."""
         B, Hq, Hkv, S, D = _shapes(q, k, v, dout)
         dq = np.empty((B, Hq, S, D), np.float64)
@@ -114,12 +115,12 @@ class Oracle:
         dv = np.empty((B, Hkv, S, D), np.float64)
         rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
                                       _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D,
-                                      int(bool(causal)), float(scale))
+                                      int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_bwd failed: %d" % rc)
         return dq, dk, dv
 
-    def bwd_rows(self, q, k, v, dout, qrows, kvrows, causal, scale):
+    def bwd_rows(self, q, k, v, dout, qrows, kvrows, causal, scale, window=0):
         """dQ of selected query rows; dK, dV of selected key rows ((b*Hkv + hkv)*S + j)."""
         B, Hq, Hkv, S, D = _shapes(q, k, v, dout)
         qrows = np.ascontiguousarray(qrows, dtype=np.int64)
@@ -130,7 +131,7 @@ class Oracle:
         rc = self.lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(qrows),
                                            qrows.size, _ptr(dq), _ptr(kvrows), kvrows.size,
                                            _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D,
-                                           int(bool(causal)), float(scale))
+                                           int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_bwd_rows failed: %d" % rc)
         return dq, dk, dv
@@ -153,17 +154,17 @@ def num_threads():
     return default().num_threads()
 
 
-def fwd(q, k, v, causal, scale):
-    return default().fwd(q, k, v, causal, scale)
+def fwd(q, k, v, causal, scale, window=0):
+    return default().fwd(q, k, v, causal, scale, window)
 
 
-def fwd_rows(q, k, v, rows, causal, scale):
-    return default().fwd_rows(q, k, v, rows, causal, scale)
+def fwd_rows(q, k, v, rows, causal, scale, window=0):
+    return default().fwd_rows(q, k, v, rows, causal, scale, window)
 
 
-def bwd(q, k, v, dout, causal, scale):
-    return default().bwd(q, k, v, dout, causal, scale)
+def bwd(q, k, v, dout, causal, scale, window=0):
+    return default().bwd(q, k, v, dout, causal, scale, window)
 
 
-def bwd_rows(q, k, v, dout, qrows, kvrows, causal, scale):
-    return default().bwd_rows(q, k, v, dout, qrows, kvrows, causal, scale)
+def bwd_rows(q, k, v, dout, qrows, kvrows, causal, scale, window=0):
+    return default().bwd_rows(q, k, v, dout, qrows, kvrows, causal, scale, window)

@@ -15,6 +15,11 @@
  * where it is silent:
  *   - scale is an argument (the page uses 1/sqrt(d));
  *   - causal: key j is visible to query i iff j <= i (query and key lengths equal);
+ *   - sliding window W > 0 (causal only): key j is visible to query i iff
+ *     i - W < j <= i, the band of the W most recent keys: the sliding window
+ *     every query of the page's compressed sparse attention sees (Table 7,
+ *     W = 128; the cr0 kernels of section 3.1.1 attend to it alone);
+ *     W = 0 means no window;
  *   - grouped-query attention: query head hq reads key/value head hq / (Hq/Hkv);
  *   - lse_i = m_i + ln(sum_j exp(s_ij - m_i)), natural log; subtracting the row
  *     maximum m_i is an exact rescaling, not an approximation;
@@ -22,7 +27,8 @@
  *
  * Layout: contiguous [B][H][S][D]; inputs are bf16 bit patterns (uint16),
  * widened exactly to double; every output is double.
- * All functions return 0 on success and a negative value on bad arguments.
+ * All functions return 0 on success and a negative value on bad arguments
+ * (-5: a window that is negative, or set without causal).
  */
 #include <math.h>
 #include <stdint.h>
@@ -32,7 +38,7 @@
 
 typedef struct {
     const uint16_t *q, *k, *v, *dout;
-    int B, Hq, Hkv, S, D, G, causal;
+    int B, Hq, Hkv, S, D, G, causal, window;
     double scale;
 } ctx_t;
 
@@ -43,9 +49,10 @@ static double widen(uint16_t h) {
     return (double)f;
 }
 
-static int check_args(int B, int Hq, int Hkv, int S, int D) {
+static int check_args(int B, int Hq, int Hkv, int S, int D, int causal, int window) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return -1;
     if (Hq % Hkv != 0) return -2;
+    if (window < 0 || (window > 0 && !causal)) return -5;
     return 0;
 }
 
@@ -62,35 +69,44 @@ static double dot_bf16(const uint16_t* x, const uint16_t* y, int D) {
     return s;
 }
 
-/* Number of keys query row i sees: all S, or i+1 when causal. */
-static int visible(const ctx_t* c, int i) { return c->causal ? i + 1 : c->S; }
+/* Query row i sees the keys first_key(i) .. last_key(i); key j is seen by the
+ * query rows first_query(j) .. last_query(j). */
+static int first_key(const ctx_t* c, int i) {
+    return (c->window > 0 && i - c->window + 1 > 0) ? i - c->window + 1 : 0;
+}
+static int last_key(const ctx_t* c, int i) { return c->causal ? i : c->S - 1; }
+static int first_query(const ctx_t* c, int j) { return c->causal ? j : 0; }
+static int last_query(const ctx_t* c, int j) {
+    return (c->window > 0 && j + c->window - 1 < c->S - 1) ? j + c->window - 1 : c->S - 1;
+}
 
 /*
  * One query row of Eq. (1): scores s_j = scale * q_i . k_j over the visible
  * keys, their softmax P_j, and optionally O_i = sum_j P_j v_j and
  * lse_i = m + ln(l). If dout is set, also the row's backward quantities:
  * dP_j = dO_i . v_j, delta_i = sum_j P_j dP_j, dS_j = P_j (dP_j - delta_i),
- * dQ_i = scale * sum_j dS_j k_j.  `p` and `dp` are caller scratch of length S.
+ * dQ_i = scale * sum_j dS_j k_j.  `p` and `dp` are caller scratch of length S,
+ * indexed by key.
  */
 static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
                     double* o_out, double* lse_out, double* delta_out, double* dq_out) {
-    const int D = c->D, n = visible(c, i), hkv = hq / c->G;
+    const int D = c->D, j0 = first_key(c, i), j1 = last_key(c, i), hkv = hq / c->G;
     const uint16_t* qi = c->q + qrow_off(c, b, hq, i);
     double m = -INFINITY;
-    for (int j = 0; j < n; ++j) {
+    for (int j = j0; j <= j1; ++j) {
         p[j] = c->scale * dot_bf16(qi, c->k + kvrow_off(c, b, hkv, j), D);
         if (p[j] > m) m = p[j];
     }
     double l = 0.0;
-    for (int j = 0; j < n; ++j) {
+    for (int j = j0; j <= j1; ++j) {
         p[j] = exp(p[j] - m);
         l += p[j];
     }
-    for (int j = 0; j < n; ++j) p[j] /= l;
+    for (int j = j0; j <= j1; ++j) p[j] /= l;
     if (lse_out) *lse_out = m + log(l);
     if (o_out) {
         for (int d = 0; d < D; ++d) o_out[d] = 0.0;
-        for (int j = 0; j < n; ++j) {
+        for (int j = j0; j <= j1; ++j) {
             const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j);
             for (int d = 0; d < D; ++d) o_out[d] += p[j] * widen(vj[d]);
         }
@@ -98,14 +114,14 @@ static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
     if (c->dout && (delta_out || dq_out)) {
         const uint16_t* doi = c->dout + qrow_off(c, b, hq, i);
         double delta = 0.0;
-        for (int j = 0; j < n; ++j) {
+        for (int j = j0; j <= j1; ++j) {
             dp[j] = dot_bf16(doi, c->v + kvrow_off(c, b, hkv, j), D);
             delta += p[j] * dp[j];
         }
         if (delta_out) *delta_out = delta;
         if (dq_out) {
             for (int d = 0; d < D; ++d) dq_out[d] = 0.0;
-            for (int j = 0; j < n; ++j) {
+            for (int j = j0; j <= j1; ++j) {
                 const double ds = p[j] * (dp[j] - delta);
                 const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j);
                 for (int d = 0; d < D; ++d) dq_out[d] += c->scale * ds * widen(kj[d]);
@@ -124,13 +140,13 @@ static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
  */
 static void one_key(const ctx_t* c, int b, int hkv, int j, const double* lse,
                     const double* delta, double* dk_out, double* dv_out) {
-    const int D = c->D, S = c->S;
+    const int D = c->D, S = c->S, i0 = first_query(c, j), i1 = last_query(c, j);
     const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j);
     const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j);
     for (int d = 0; d < D; ++d) { dk_out[d] = 0.0; dv_out[d] = 0.0; }
     for (int g = 0; g < c->G; ++g) {
         const int hq = hkv * c->G + g;
-        for (int i = c->causal ? j : 0; i < S; ++i) {
+        for (int i = i0; i <= i1; ++i) {
             const uint16_t* qi = c->q + qrow_off(c, b, hq, i);
             const uint16_t* doi = c->dout + qrow_off(c, b, hq, i);
             const double pij = exp(c->scale * dot_bf16(qi, kj, D) - lse[(size_t)g * S + i]);
@@ -146,10 +162,11 @@ static void one_key(const ctx_t* c, int b, int hkv, int j, const double* lse,
 
 static void init_ctx(ctx_t* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const uint16_t* dout, int B, int Hq, int Hkv, int S, int D, int causal,
-                     double scale) {
+                     int window, double scale) {
     c->q = q; c->k = k; c->v = v; c->dout = dout;
     c->B = B; c->Hq = Hq; c->Hkv = Hkv; c->S = S; c->D = D; c->G = Hq / Hkv;
     c->causal = causal ? 1 : 0;
+    c->window = window;
     c->scale = scale;
 }
 
@@ -157,12 +174,12 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* Forward over every row: o [B][Hq][S][D], lse [B][Hq][S]. */
 int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* o,
-                    double* lse, int B, int Hq, int Hkv, int S, int D, int causal,
+                    double* lse, int B, int Hq, int Hkv, int S, int D, int causal, int window,
                     double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D);
+    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
     if (rc) return rc;
     ctx_t c;
-    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, scale);
+    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, window, scale);
     const long long rows = (long long)B * Hq * S;
 #pragma omp parallel
     {
@@ -181,13 +198,14 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
  * o_rows [n][D], lse_rows [n]. */
 int oracle_attn_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int64_t* rows, int64_t n, double* o_rows, double* lse_rows,
-                         int B, int Hq, int Hkv, int S, int D, int causal, double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D);
+                         int B, int Hq, int Hkv, int S, int D, int causal, int window,
+                         double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
     if (rc) return rc;
     for (int64_t t = 0; t < n; ++t)
         if (rows[t] < 0 || rows[t] >= (int64_t)B * Hq * S) return -3;
     ctx_t c;
-    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, scale);
+    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, window, scale);
 #pragma omp parallel
     {
         double* p = (double*)malloc(sizeof(double) * (size_t)S);
@@ -223,11 +241,11 @@ static void group_row_stats(const ctx_t* c, int b, int hkv, double* lse, double*
 /* Full backward: dq [B][Hq][S][D]; dk, dv [B][Hkv][S][D] (summed over the group). */
 int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dout, double* dq, double* dk, double* dv, int B, int Hq,
-                    int Hkv, int S, int D, int causal, double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D);
+                    int Hkv, int S, int D, int causal, int window, double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
     if (rc) return rc;
     ctx_t c;
-    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, scale);
+    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, window, scale);
     const int G = c.G;
     const long long rows = (long long)B * Hq * S;
     double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
@@ -269,15 +287,16 @@ int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dout, const int64_t* qrows, int64_t nq, double* dq_rows,
                          const int64_t* kvrows, int64_t nkv, double* dk_rows, double* dv_rows,
-                         int B, int Hq, int Hkv, int S, int D, int causal, double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D);
+                         int B, int Hq, int Hkv, int S, int D, int causal, int window,
+                         double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
     if (rc) return rc;
     for (int64_t t = 0; t < nq; ++t)
         if (qrows[t] < 0 || qrows[t] >= (int64_t)B * Hq * S) return -3;
     for (int64_t t = 0; t < nkv; ++t)
         if (kvrows[t] < 0 || kvrows[t] >= (int64_t)B * Hkv * S) return -3;
     ctx_t c;
-    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, scale);
+    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, window, scale);
     const int G = c.G;
 #pragma omp parallel
     {

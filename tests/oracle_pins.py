@@ -3,7 +3,8 @@
 Each check takes an oracle object (``oracle.Oracle``) and raises AssertionError
 when the oracle disagrees with the fact. The facts come from section 2.1 of
 Rao et al., "Scheduling Data to Compute: Hierarchical Data Pipelining for LLM
-Training on AMD GPUs" (Eq. (1): O = softmax(Q K^T / sqrt(d)) V) and from
+Training on AMD GPUs" (Eq. (1): O = softmax(Q K^T / sqrt(d)) V), the sliding
+window of its Table 7 (query i sees the keys i-W+1 .. i), and from
 mathematics: an independent brute force on tiny inputs, closed forms,
 invariants, torch's float64 CPU attention and autograd as a library routine,
 and central finite differences for the gradient.
@@ -23,11 +24,13 @@ def _f64(bits):
     return bf16_to_f32(bits).astype(np.float64)
 
 
-def _visible(causal, S, i):
+def _visible(causal, S, i, window=0):
+    if window:
+        return range(max(0, i - window + 1), i + 1)
     return range(i + 1) if causal else range(S)
 
 
-def brute_force_fwd(q, k, v, causal, scale):
+def brute_force_fwd(q, k, v, causal, scale, window=0):
     """Eq. (1) on tiny inputs in pure Python: exp(s)/sum(exp(s)) with math.fsum,
     no max subtraction, no numpy linear algebra."""
     qf, kf, vf = _f64(q), _f64(k), _f64(v)
@@ -39,7 +42,7 @@ def brute_force_fwd(q, k, v, causal, scale):
         for h in range(Hq):
             g = h // G
             for i in range(S):
-                js = list(_visible(causal, S, i))
+                js = list(_visible(causal, S, i, window))
                 e = [math.exp(scale * math.fsum(qf[b, h, i, d] * kf[b, g, j, d] for d in range(D)))
                      for j in js]
                 z = math.fsum(e)
@@ -49,7 +52,7 @@ def brute_force_fwd(q, k, v, causal, scale):
     return o, lse
 
 
-def _loss_py(qf, kf, vf, dof, causal, scale, G):
+def _loss_py(qf, kf, vf, dof, causal, scale, G, window=0):
     """L = sum(O * dO) of Eq. (1), float64 arrays in, pure Python out."""
     B, Hq, S, D = qf.shape
     total = []
@@ -57,7 +60,7 @@ def _loss_py(qf, kf, vf, dof, causal, scale, G):
         for h in range(Hq):
             g = h // G
             for i in range(S):
-                js = list(_visible(causal, S, i))
+                js = list(_visible(causal, S, i, window))
                 s = [scale * float(np.dot(qf[b, h, i], kf[b, g, j])) for j in js]
                 m = max(s)
                 e = [math.exp(x - m) for x in s]
@@ -67,14 +70,26 @@ def _loss_py(qf, kf, vf, dof, causal, scale, G):
     return math.fsum(total)
 
 
-def _torch_ref(q, k, v, causal, scale, dout=None):
-    """torch float64 CPU scaled_dot_product_attention (+ autograd) as a library routine."""
+def _band_mask(S, window):
+    """Boolean [S, S] mask, True where query i may attend key j: i - window < j <= i."""
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    return torch.from_numpy((j <= i) & (j > i - window))
+
+
+def _torch_ref(q, k, v, causal, scale, dout=None, window=0):
+    """torch float64 CPU scaled_dot_product_attention (+ autograd) as a library routine;
+    a window is passed to it as an explicit boolean attention mask."""
     G = q.shape[1] // k.shape[1]
     tq = torch.from_numpy(_f64(q)).requires_grad_(dout is not None)
     tk = torch.from_numpy(_f64(k)).requires_grad_(dout is not None)
     tv = torch.from_numpy(_f64(v)).requires_grad_(dout is not None)
-    o = torch.nn.functional.scaled_dot_product_attention(
-        tq, tk, tv, is_causal=bool(causal), scale=float(scale), enable_gqa=G > 1)
+    if window:
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, attn_mask=_band_mask(q.shape[2], window), scale=float(scale), enable_gqa=G > 1)
+    else:
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=bool(causal), scale=float(scale), enable_gqa=G > 1)
     if dout is None:
         return o.detach().numpy(), None
     o.backward(torch.from_numpy(_f64(dout)))
@@ -261,8 +276,109 @@ def pin_equal_keys(orc):
         _close(dq, np.zeros_like(dq), 1e-14, "equal keys dQ")
 
 
+# ---------------------------------------------------------------- sliding-window pins
+
+def pin_window_brute_force(orc):
+    """Windowed forward equals the pure-Python brute force over the band i-W < j <= i."""
+    for (B, Hq, Hkv, S, D, W, seed) in [(1, 2, 1, 9, 4, 1, 31), (1, 2, 2, 8, 3, 2, 32),
+                                        (2, 4, 2, 7, 5, 3, 33), (1, 1, 1, 9, 4, 5, 34)]:
+        q, k, v = qkv(B, Hq, Hkv, S, D, seed)
+        o, lse = orc.fwd(q, k, v, True, 0.6, W)
+        ob, lb = brute_force_fwd(q, k, v, True, 0.6, W)
+        _close(o, ob, 1e-12, "windowed O vs brute force W=%d" % W)
+        _close(lse, lb, 1e-12, "windowed lse vs brute force W=%d" % W)
+
+
+def pin_window_torch(orc):
+    """Windowed forward and gradients equal torch float64 SDPA (and its autograd) given
+    the band as an explicit boolean mask."""
+    for (B, Hq, Hkv, S, D, W, seed) in [(1, 4, 2, 37, 16, 8, 35), (2, 2, 2, 30, 8, 1, 36),
+                                        (1, 8, 2, 21, 32, 13, 37)]:
+        q, k, v, do = qkv(B, Hq, Hkv, S, D, seed, with_dout=True)
+        scale = 1.0 / math.sqrt(D)
+        o, _ = orc.fwd(q, k, v, True, scale, W)
+        dq, dk, dv = orc.bwd(q, k, v, do, True, scale, W)
+        ot, (tq, tk, tv) = _torch_ref(q, k, v, True, scale, do, window=W)
+        _close(o, ot, 1e-12, "windowed O vs torch sdpa W=%d" % W)
+        _close(dq, tq, 1e-12, "windowed dQ vs torch autograd")
+        _close(dk, tk, 1e-12, "windowed dK vs torch autograd")
+        _close(dv, tv, 1e-12, "windowed dV vs torch autograd")
+
+
+def pin_window_closed_forms(orc):
+    """W = 1: each query sees only its own key, so O_i = V_i, lse_i = scale q_i.k_i and
+    dQ = dK = 0. W >= S: the band is the whole causal triangle, so the result is the
+    causal one exactly. Q = 0: O_i is the mean of V over the min(i+1, W) keys in the band."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 11, 8
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 38, with_dout=True)
+    o, lse = orc.fwd(q, k, v, True, 0.45, 1)
+    _close(o, np.repeat(_f64(v), 2, axis=1), 0.0, "W=1 O")
+    _close(lse, 0.45 * np.einsum("bhsd,bhsd->bhs", _f64(q), np.repeat(_f64(k), 2, axis=1)), 1e-14,
+           "W=1 lse")
+    dq, dk, dv = orc.bwd(q, k, v, do, True, 0.45, 1)
+    _close(dq, np.zeros_like(dq), 0.0, "W=1 dQ")
+    _close(dk, np.zeros_like(dk), 0.0, "W=1 dK")
+    _close(dv, _f64(do).reshape(B, Hkv, 2, S, D).sum(axis=2), 1e-15, "W=1 dV")
+    for W in (S, S + 5):
+        o1, l1 = orc.fwd(q, k, v, True, 0.45, W)
+        o2, l2 = orc.fwd(q, k, v, True, 0.45)
+        _close(o1, o2, 0.0, "W>=S O")
+        _close(l1, l2, 0.0, "W>=S lse")
+        g1 = orc.bwd(q, k, v, do, True, 0.45, W)
+        g2 = orc.bwd(q, k, v, do, True, 0.45)
+        for a, b in zip(g1, g2):
+            _close(a, b, 0.0, "W>=S gradients")
+    q0 = np.zeros_like(q)
+    W = 4
+    o, lse = orc.fwd(q0, k, v, True, 0.45, W)
+    vf = _f64(v)
+    for i in range(S):
+        j0 = max(0, i - W + 1)
+        _close(o[:, :, i], np.repeat(vf[:, :, j0:i + 1].mean(axis=2), 2, axis=1), 1e-14, "Q=0 band mean")
+        _close(lse[:, :, i], np.full((B, Hq), math.log(i + 1 - j0)), 1e-14, "Q=0 band lse")
+
+
+def pin_window_gradients(orc):
+    """Windowed gradients equal central differences of L = sum(O * dO) from the
+    pure-Python forward; rows of P still sum to 1 and rows of dS to 0 inside the band;
+    the sampled-row entry points agree with the full ones."""
+    h = 1e-6
+    B, Hq, Hkv, S, D, W = 1, 2, 1, 6, 3, 2
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 39, with_dout=True)
+    dq, dk, dv = orc.bwd(q, k, v, do, True, 0.8, W)
+    base = [_f64(q), _f64(k), _f64(v)]
+    dof = _f64(do)
+    for which, grad in enumerate((dq, dk, dv)):
+        for idx in np.ndindex(*base[which].shape):
+            plus = [a.copy() for a in base]
+            minus = [a.copy() for a in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd = (_loss_py(*plus, dof, True, 0.8, Hq // Hkv, W)
+                  - _loss_py(*minus, dof, True, 0.8, Hq // Hkv, W)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), \
+                "windowed finite difference %s%s: fd %.9f analytic %.9f" % ("qkv"[which], idx, fd, grad[idx])
+    B, Hq, Hkv, S, D, W = 2, 4, 2, 23, 8, 5
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 40, with_dout=True)
+    dq, dk, dv = orc.bwd(q, k, v, do, True, 0.35, W)
+    dofull = _f64(do).reshape(B, Hkv, Hq // Hkv, S, D)
+    _close(dv.sum(axis=2), dofull.sum(axis=(2, 3)), 1e-12, "windowed sum dV")
+    _close(dk.sum(axis=2), np.zeros((B, Hkv, D)), 1e-12, "windowed sum dK")
+    o, lse = orc.fwd(q, k, v, True, 0.35, W)
+    rows = np.array([0, 4, 5, 22, 23, 99, 183])
+    o_r, l_r = orc.fwd_rows(q, k, v, rows, True, 0.35, W)
+    _close(o_r, o.reshape(-1, D)[rows], 0.0, "windowed fwd rows")
+    _close(l_r, lse.reshape(-1)[rows], 0.0, "windowed fwd rows lse")
+    kvr = np.array([0, 3, 22, 23, 40, 91])
+    dq_r, dk_r, dv_r = orc.bwd_rows(q, k, v, do, rows, kvr, True, 0.35, W)
+    _close(dq_r, dq.reshape(-1, D)[rows], 1e-15, "windowed dq rows")
+    _close(dk_r, dk.reshape(-1, D)[kvr], 1e-15, "windowed dk rows")
+    _close(dv_r, dv.reshape(-1, D)[kvr], 1e-15, "windowed dv rows")
+
+
 FORWARD_PINS = [pin_brute_force, pin_torch_sdpa, pin_single_key, pin_zero_query,
                 pin_causal_first_row, pin_permutation, pin_gqa_is_repeated_mha, pin_sharp_softmax,
                 pin_rows_match_full]
 BACKWARD_PINS = [pin_finite_differences, pin_torch_autograd, pin_backward_invariants, pin_equal_keys]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+WINDOW_PINS = [pin_window_brute_force, pin_window_torch, pin_window_closed_forms, pin_window_gradients]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + WINDOW_PINS

@@ -17,11 +17,15 @@ def test_oracle_pin(pin):
 # Each must make at least one pin fail; none reads or writes out of bounds.
 MUTATIONS = [
     ("dropped_scale", "p[j] = c->scale * dot_bf16(", "p[j] = dot_bf16("),
-    ("causal_sees_next_key", "return c->causal ? i + 1 : c->S;",
-     "return c->causal ? (i + 1 < c->S ? i + 2 : c->S) : c->S;"),
+    ("causal_sees_next_key", "static int last_key(const ctx_t* c, int i) { return c->causal ? i : c->S - 1; }",
+     "static int last_key(const ctx_t* c, int i) { return c->causal ? (i + 1 < c->S ? i + 1 : i) : c->S - 1; }"),
+    ("window_one_too_wide", "return (c->window > 0 && i - c->window + 1 > 0) ? i - c->window + 1 : 0;",
+     "return (c->window > 0 && i - c->window > 0) ? i - c->window : 0;"),
+    ("window_key_side_one_too_wide", "return (c->window > 0 && j + c->window - 1 < c->S - 1) ? j + c->window - 1 : c->S - 1;",
+     "return (c->window > 0 && j + c->window < c->S - 1) ? j + c->window : c->S - 1;"),
     ("gqa_interleaved_map", "hkv = hq / c->G;", "hkv = hq % c->Hkv;"),
     ("lse_log2", "*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
-    ("unnormalised_p", "for (int j = 0; j < n; ++j) p[j] /= l;", ""),
+    ("unnormalised_p", "for (int j = j0; j <= j1; ++j) p[j] /= l;", ""),
     ("ds_sign_flipped", "const double ds = p[j] * (dp[j] - delta);",
      "const double ds = p[j] * (delta - dp[j]);"),
     ("dp_uses_k_not_v", "dp[j] = dot_bf16(doi, c->v + kvrow_off", "dp[j] = dot_bf16(doi, c->k + kvrow_off"),
