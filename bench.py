@@ -3,10 +3,15 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 the forward kernel (O, lse) and the backward kernels (delta, dK/dV, dQ) on the
 Llama-3.1-8B-shaped causal GQA workload B=1, Hq=32, Hkv=8, S=4096, D=128,
-inputs resident in HBM. FLOP convention: forward 4*B*Hq*S^2*D (halved when
-causal), backward 2.5x the forward; softmax and exp work is not counted.
+inputs resident in HBM. FLOP convention: forward 4*B*Hq*D times the visible
+(query, key) pairs per head (S^2, S^2/2 when causal, S*W - W(W-1)/2 for a
+causal window of W keys), backward 2.5x the forward; softmax and exp work is
+not counted.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--fwd-only]
+
+--workload picks another entry of inputs.CONFIGS (the default is the headline
+workload above); a config with a "window" runs attn_fwd_window/attn_bwd_window.
 """
 import argparse
 import json
@@ -26,9 +31,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def fwd_flops(B, Hq, S, D, causal):
-    f = 4.0 * B * Hq * S * S * D
-    return f / 2 if causal else f
+def visible_pairs(S, causal, window=0):
+    """(query, key) pairs per head the FLOP convention counts."""
+    if window and window < S:
+        return float(S) * window - window * (window - 1) / 2.0
+    return S * S / 2.0 if causal else float(S) * S
+
+
+def fwd_flops(B, Hq, S, D, causal, window=0):
+    return 4.0 * B * Hq * D * visible_pairs(S, causal, window)
 
 
 def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
@@ -37,24 +48,27 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
     import numpy as np
     import oracle
     B, Hq, Hkv, S, D, causal = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"], cfg["causal"]
+    W = cfg.get("window", 0)
     scale = 1.0 / math.sqrt(D)
     rng = np.random.default_rng(123)
 
     def row_flops(rows):
         i = rows % S
         n = (i + 1) if causal else np.full_like(i, S)
+        if W:
+            n = np.minimum(n, W)
         return float(np.sum(4.0 * n * D))
 
     # calibrate on a small sample, then size the timed sample to ~target_s
     cal = rng.integers(0, B * Hq * S, size=64)
     t = time.perf_counter()
-    oracle.fwd_rows(q, k, v, cal, causal, scale)
+    oracle.fwd_rows(q, k, v, cal, causal, scale, W)
     per_flop = (time.perf_counter() - t) / row_flops(cal)
     budget = target_s * (0.5 if with_bwd else 1.0)
     n = int(min(B * Hq * S, max(64, budget / per_flop / (row_flops(cal) / cal.size))))
     rows = rng.choice(B * Hq * S, size=n, replace=False)
     t = time.perf_counter()
-    oracle.fwd_rows(q, k, v, rows, causal, scale)
+    oracle.fwd_rows(q, k, v, rows, causal, scale, W)
     t_f = time.perf_counter() - t
     flops, secs = row_flops(rows), t_f
     sample = "forward: %d of %d query rows (uniform without replacement)" % (n, B * Hq * S)
@@ -63,11 +77,14 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
         nk = 64
         keys = np.sort(rng.choice(S, size=nk, replace=False)).astype(np.int64)
         t = time.perf_counter()
-        oracle.bwd_rows(q, k, v, dout, np.zeros(0, np.int64), keys, causal, scale)
+        oracle.bwd_rows(q, k, v, dout, np.zeros(0, np.int64), keys, causal, scale, W)
         t_b = time.perf_counter() - t
         G = Hq // Hkv
         stat_flops = G * row_flops(np.arange(S, dtype=np.int64))           # S, P and dP rows of the group
-        key_flops = float(np.sum(G * 8.0 * D * ((S - keys) if causal else S)))
+        seen_by = (S - keys) if causal else np.full_like(keys, S)         # query rows that see each key
+        if W:
+            seen_by = np.minimum(seen_by, W)
+        key_flops = float(np.sum(G * 8.0 * D * seen_by))
         # the group's statistics are counted as work at the forward rate; their time is in t_b
         flops += stat_flops + key_flops
         secs += t_b
@@ -129,6 +146,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward kernel alone")
+    ap.add_argument("--workload", default=WORKLOAD, help="an entry of inputs.CONFIGS (default %(default)s)")
     ap.add_argument("--copy-probe", action="store_true", help="run only the HBM counter calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -144,8 +162,14 @@ def main():
     from flashattention_tiled_attention_amd.inputs import CONFIGS, qkv
     from tests.gpu_util import to_dev
 
-    cfg = CONFIGS[WORKLOAD]
+    if args.workload not in CONFIGS:
+        print("unknown workload %r; choose from %s" % (args.workload, ", ".join(CONFIGS)), file=sys.stderr)
+        sys.exit(2)
+    name = args.workload
+    headline = name == WORKLOAD
+    cfg = CONFIGS[name]
     B, Hq, Hkv, S, D, causal = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"], cfg["causal"]
+    W = cfg.get("window", 0)
     scale = 1.0 / math.sqrt(D)
     q, k, v, dout = qkv(B, Hq, Hkv, S, D, seed=0, with_dout=True)
     dq_, dk_, dv_, ddo = to_dev(q), to_dev(k), to_dev(v), to_dev(dout)
@@ -159,15 +183,31 @@ def main():
     with_bwd = not args.fwd_only
 
     bargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws, stream)
-    calls = {"fwd_kernel": lambda: fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream)}
-    if with_bwd:
-        calls["dq_kernel"] = lambda: fa.attn_bwd_dq(*bargs)
-        calls["dkv_kernel"] = lambda: fa.attn_bwd_dkdv(*bargs)
+    wargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, W, scale, ws, stream)
+    if W:
+        def run_fwd():
+            fa.attn_fwd_window(dq_, dk_, dv_, o, lse, W, scale, stream)
+
+        def run_bwd():
+            fa.attn_bwd_window(*wargs)
+        calls = {"fwd_kernel": run_fwd}
+        if with_bwd:
+            calls["bwd_kernels"] = run_bwd
+    else:
+        def run_fwd():
+            fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream)
+
+        def run_bwd():
+            fa.attn_bwd(*bargs)
+        calls = {"fwd_kernel": run_fwd}
+        if with_bwd:
+            calls["dq_kernel"] = lambda: fa.attn_bwd_dq(*bargs)
+            calls["dkv_kernel"] = lambda: fa.attn_bwd_dkdv(*bargs)
 
     def step():
-        fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream)
+        run_fwd()
         if with_bwd:
-            fa.attn_bwd(*bargs)
+            run_bwd()
 
     for _ in range(args.warmup):
         step()
@@ -179,8 +219,10 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # Per-kernel launch durations with HIP events recorded on the stream the kernels
-    # run on; each entry point launches exactly one kernel.
+    # Per-entry-point durations with HIP events recorded on the stream the kernels run
+    # on: attn_fwd (its main launch plus the small exact-path launch of the first
+    # causal query tile), attn_bwd_dq (likewise two launches) and attn_bwd_dkdv (one
+    # launch); a windowed workload times attn_fwd_window and attn_bwd_window.
     def time_calls(fn, n):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -198,8 +240,8 @@ def main():
     # kernel computes 2 (S = Q K^T, O = P V); the dQ kernel 3 (S, dP = dO V^T, dQ = dS K);
     # the dK/dV kernel 4 (S, dP, dV = P^T dO, dK = dS^T Q). The step's algorithmic work
     # is forward 2 + backward 5 products (backward = 2.5 x forward).
-    product = fwd_flops(B, Hq, S, D, causal) / 2
-    kernel_products = {"fwd_kernel": 2, "dq_kernel": 3, "dkv_kernel": 4}
+    product = fwd_flops(B, Hq, S, D, causal, W) / 2
+    kernel_products = {"fwd_kernel": 2, "dq_kernel": 3, "dkv_kernel": 4, "bwd_kernels": 7}
     f_fwd = 2 * product
     f_bwd = 5 * product
     step_flops = f_fwd + (f_bwd if with_bwd else 0.0)
@@ -209,24 +251,25 @@ def main():
     dom_flops = kernel_products[dominant] * product
     achieved = dom_flops / (kernel_ms[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": hbm_traffic(dominant),
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": hbm_traffic(dominant) if headline else None,
                 "flop_per_launch": dom_flops, "launch_ms": round(kernel_ms[dominant], 4)}
 
     kernels = {}
-    for name, ms in kernel_ms.items():
-        fl = kernel_products[name] * product
-        kernels[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+    for kname, ms in kernel_ms.items():
+        fl = kernel_products[kname] * product
+        kernels[kname] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                          "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "hbm_bytes": hbm_traffic(name)}
+                         "hbm_bytes": hbm_traffic(kname) if headline else None}
 
     result = {
         "metric": "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak on 1 MI355X",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOAD + ("" if with_bwd else "_fwd_only"), "B": B, "Hq": Hq, "Hkv": Hkv,
-                   "S": S, "D": D, "causal": bool(causal), "pass": "fwd+bwd" if with_bwd else "fwd",
-                   "seed": 0},
+        "config": {"workload": name + ("" if with_bwd else "_fwd_only"), "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "S": S, "D": D, "causal": bool(causal), "window": W or None,
+                   "pass": "fwd+bwd" if with_bwd else "fwd", "seed": 0},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd": {"tflops": kernels["fwd_kernel"]["tflops"], "ms": kernels["fwd_kernel"]["ms"],
                 "frac_of_peak": kernels["fwd_kernel"]["frac_of_peak"]},
@@ -234,7 +277,7 @@ def main():
         "roofline": roofline,
     }
     if with_bwd:
-        bwd_ms = kernel_ms["dq_kernel"] + kernel_ms["dkv_kernel"]
+        bwd_ms = kernel_ms["bwd_kernels"] if W else kernel_ms["dq_kernel"] + kernel_ms["dkv_kernel"]
         result["bwd"] = {"tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2), "ms": round(bwd_ms, 4),
                          "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_cpu_baseline:

@@ -6,8 +6,9 @@ points, and every step of the computation runs in the library's HIP kernels.
 There is no fallback: if ``libattn.so`` is missing, every call raises.
 
 Entry points with the C names (``attn_fwd``, ``attn_bwd``, ``attn_bwd_dq``,
-``attn_bwd_dkdv``, ``attn_bwd_workspace_bytes``, ``attn_status_str``) take caller-allocated
-tensors; ``fwd`` and ``bwd`` allocate their outputs with torch.
+``attn_bwd_dkdv``, ``attn_fwd_window``, ``attn_bwd_window``, ``attn_bwd_workspace_bytes``,
+``attn_status_str``) take caller-allocated tensors; ``fwd`` and ``bwd`` allocate their
+outputs with torch.
 """
 import ctypes
 import math
@@ -28,9 +29,10 @@ ATTN_ERR_WORKSPACE = 6
 ATTN_ERR_SCALE = 7
 ATTN_ERR_HIP = 8
 ATTN_ERR_DEVICE = 9
+ATTN_ERR_WINDOW = 10
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_bytes",
-                    "attn_status_str")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_window",
+                    "attn_bwd_window", "attn_bwd_workspace_bytes", "attn_status_str")
 
 
 class AttnError(RuntimeError):
@@ -58,6 +60,10 @@ def load_library(path=None):
     for f in (lib.attn_bwd, lib.attn_bwd_dq, lib.attn_bwd_dkdv):
         f.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, F, V, Z, V]
         f.restype = I
+    lib.attn_fwd_window.argtypes = [V, V, V, V, V, I, I, I, I, I, I, F, V]
+    lib.attn_fwd_window.restype = I
+    lib.attn_bwd_window.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, F, V, Z, V]
+    lib.attn_bwd_window.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_status_str.argtypes = [I]
@@ -105,8 +111,7 @@ def _dims(q, k):
     return B, Hq, k.shape[1], S, D
 
 
-def attn_fwd(q, k, v, o, lse, causal, scale, stream=None):
-    """C attn_fwd on torch tensors: q [B,Hq,S,D], k/v [B,Hkv,S,D] bf16; writes o (bf16) and lse (fp32)."""
+def _fwd_call(name, q, k, v, o, lse, flag, scale, stream):
     import torch
     B, Hq, Hkv, S, D = _dims(q, k)
     _check(q, "q", torch.bfloat16, (B, Hq, S, D))
@@ -114,17 +119,27 @@ def attn_fwd(q, k, v, o, lse, causal, scale, stream=None):
     _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
     _check(o, "o", torch.bfloat16, (B, Hq, S, D))
     _check(lse, "lse", torch.float32, (B, Hq, S))
-    rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, D,
-                                 int(bool(causal)), float(scale), _stream(stream))
+    rc = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S,
+                                       D, int(flag), float(scale), _stream(stream))
     if rc:
-        raise AttnError(rc, "attn_fwd")
+        raise AttnError(rc, name)
+
+
+def attn_fwd(q, k, v, o, lse, causal, scale, stream=None):
+    """C attn_fwd on torch tensors: q [B,Hq,S,D], k/v [B,Hkv,S,D] bf16; writes o (bf16) and lse (fp32)."""
+    _fwd_call("attn_fwd", q, k, v, o, lse, bool(causal), scale, stream)
+
+
+def attn_fwd_window(q, k, v, o, lse, window, scale, stream=None):
+    """C attn_fwd_window: causal attention where query i sees keys i-window+1 .. i."""
+    _fwd_call("attn_fwd_window", q, k, v, o, lse, window, scale, stream)
 
 
 def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal):
     return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, int(bool(causal))))
 
 
-def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream):
+def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, flag, scale, workspace, stream):
     import torch
     B, Hq, Hkv, S, D = _dims(q, k)
     for t, n, dt, sh in ((q, "q", torch.bfloat16, (B, Hq, S, D)), (k, "k", torch.bfloat16, (B, Hkv, S, D)),
@@ -137,7 +152,7 @@ def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace,
         raise TypeError("workspace must be a GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
     rc = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                                       _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), float(scale),
+                                       _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(flag), float(scale),
                                        _ptr(workspace), nbytes, _stream(stream))
     if rc:
         raise AttnError(rc, name)
@@ -145,33 +160,43 @@ def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace,
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
     """C attn_bwd on torch tensors; dq/dk/dv are fp32; workspace is a uint8 GPU tensor."""
-    _bwd_call("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream)
+    _bwd_call("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, bool(causal), scale, workspace, stream)
 
 
 def attn_bwd_dq(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
     """First backward stage: delta into the workspace and dq."""
-    _bwd_call("attn_bwd_dq", q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream)
+    _bwd_call("attn_bwd_dq", q, k, v, o, lse, dout, dq, dk, dv, bool(causal), scale, workspace, stream)
 
 
 def attn_bwd_dkdv(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
     """Second backward stage: dk and dv from the workspace's delta."""
-    _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream)
+    _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dout, dq, dk, dv, bool(causal), scale, workspace, stream)
 
 
-def fwd(q, k, v, causal=False, scale=None):
-    """Allocate o and lse and run attn_fwd. scale defaults to 1/sqrt(D)."""
+def attn_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, window, scale, workspace, stream=None):
+    """C attn_bwd_window: gradient of attn_fwd_window with the same window."""
+    _bwd_call("attn_bwd_window", q, k, v, o, lse, dout, dq, dk, dv, window, scale, workspace, stream)
+
+
+def fwd(q, k, v, causal=False, scale=None, window=0):
+    """Allocate o and lse and run attn_fwd (attn_fwd_window when window > 0, which
+    implies causal). scale defaults to 1/sqrt(D)."""
     import torch
     B, Hq, Hkv, S, D = _dims(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, causal, scale)
+    if window:
+        attn_fwd_window(q, k, v, o, lse, window, scale)
+    else:
+        attn_fwd(q, k, v, o, lse, causal, scale)
     return o, lse
 
 
-def bwd(q, k, v, o, lse, dout, causal=False, scale=None):
-    """Allocate dq/dk/dv (fp32) and the workspace and run attn_bwd."""
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, window=0):
+    """Allocate dq/dk/dv (fp32) and the workspace and run attn_bwd (attn_bwd_window
+    when window > 0)."""
     import torch
     B, Hq, Hkv, S, D = _dims(q, k)
     if scale is None:
@@ -179,7 +204,10 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None):
     dq = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=q.device)
     dv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=q.device)
-    ws = torch.empty((attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal),), dtype=torch.uint8,
-                     device=q.device)
-    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, ws)
+    ws = torch.empty((attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal or bool(window)),),
+                     dtype=torch.uint8, device=q.device)
+    if window:
+        attn_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, window, scale, ws)
+    else:
+        attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, ws)
     return dq, dk, dv

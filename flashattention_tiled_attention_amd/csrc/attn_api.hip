@@ -84,12 +84,14 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_HIP: return "HIP runtime error";
         case ATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+        case ATTN_ERR_WINDOW: return "window must be >= 1";
         default: return "unknown attn status";
     }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-             int Hkv, int S, int D, int causal, float scale, void* stream) {
+static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int Hq, int Hkv, int S, int D, int causal, int window, float scale,
+                    void* stream) {
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
     int rc = check_sizes(B, Hq, Hkv, S, D);
     if (rc) return rc;
@@ -106,6 +108,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.lse = lse;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.G = Hq / Hkv;
     a.causal = causal ? 1 : 0;
+    a.window = window;
     // The kernel needs a strictly positive factor (masked scores are -inf); a zero
     // scale becomes 2^-100, which leaves every exp2 of a finite score at exactly 1.
     a.scale_log2 = fmaxf(fabsf(scale) * 1.4426950408889634f, 7.888609052210118e-31f);
@@ -114,8 +117,21 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     // sqrt(D) > 2 for unit-variance inputs) off 1.0 and so exposed to bf16
     // rounding; there the maximum is tracked exactly.
     a.max_slack = fabsf(scale) * sqrtf((float)D) > 2.0f ? 0.0f : 8.0f;
+    a.precise_tiles = 0;  // set by the launcher, which knows the tile size
     if (attn::launch_fwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int S, int D, int causal, float scale, void* stream) {
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, causal, 0, scale, stream);
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int Hq, int Hkv, int S, int D, int window, float scale, void* stream) {
+    if (window < 1) return ATTN_ERR_WINDOW;
+    // a window of S or more keys is the whole causal triangle
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, 1, window >= S ? 0 : window, scale, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal) {
@@ -126,8 +142,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal
 
 static int bwd_stages(int stages, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv, int B,
-                      int Hq, int Hkv, int S, int D, int causal, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      int Hq, int Hkv, int S, int D, int causal, int window, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
     int rc = check_sizes(B, Hq, Hkv, S, D);
     if (rc) return rc;
@@ -153,11 +169,14 @@ static int bwd_stages(int stages, const void* q, const void* k, const void* v, c
     a.delta = (float*)workspace;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.G = Hq / Hkv;
     a.causal = causal ? 1 : 0;
+    a.window = window;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    // Peaky softmax (score spread > 2 for unit-variance inputs): bf16 rounding of
-    // P, dS and the stored O would dominate, so every tile takes the exact path.
-    a.precise_all = fabsf(scale) * sqrtf((float)D) > 2.0f ? 1 : 0;
+    // Every tile takes the exact path when rows can concentrate on few keys: a
+    // peaked softmax (score spread > 2 for unit-variance inputs), where bf16
+    // rounding of P, dS and the stored O would dominate, or a window of at most
+    // 128 keys, where every row sees no more keys than the first causal rows do.
+    a.precise_all = (fabsf(scale) * sqrtf((float)D) > 2.0f || (window > 0 && window <= 128)) ? 1 : 0;
     if (attn::launch_bwd(a, D, stages, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
 }
@@ -166,7 +185,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
              int D, int causal, float scale, void* workspace, size_t workspace_bytes,
              void* stream) {
-    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, scale,
+    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, 0, scale,
                       workspace, workspace_bytes, stream);
 }
 
@@ -174,7 +193,7 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, cons
                 const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
                 int D, int causal, float scale, void* workspace, size_t workspace_bytes,
                 void* stream) {
-    return bwd_stages(1, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, scale,
+    return bwd_stages(1, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, 0, scale,
                       workspace, workspace_bytes, stream);
 }
 
@@ -182,8 +201,17 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, co
                   const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
                   int D, int causal, float scale, void* workspace, size_t workspace_bytes,
                   void* stream) {
-    return bwd_stages(2, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, scale,
+    return bwd_stages(2, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, 0, scale,
                       workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv,
+                    int S, int D, int window, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (window < 1) return ATTN_ERR_WINDOW;
+    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, 1,
+                      window >= S ? 0 : window, scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

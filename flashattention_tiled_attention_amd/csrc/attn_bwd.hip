@@ -29,7 +29,13 @@
 // sum_j P_ij dP_ij in fp32, and the P and dS operands are split into a bf16 high
 // part plus a bf16 remainder (two MFMAs each). When |scale| * sqrt(D) > 2 the
 // scores of unit-variance inputs spread wide enough for any row to concentrate
-// on a few keys, and the host asks for this treatment on every tile.
+// on a few keys, and the host asks for this treatment on every tile; so it does
+// for a sliding window of at most 128 keys, where no row sees more keys than the
+// first causal rows do.
+//
+// Sliding window (query i sees keys i-W+1 .. i, the window of the page's
+// compressed sparse attention, Table 7): both kernels skip the tiles outside
+// the band and mask the tiles that cross either of its edges.
 #include "device.h"
 #include "kernels.h"
 
@@ -82,23 +88,19 @@ __device__ __forceinline__ void decode_q_item(int bid, int nQ, int qt_first, int
     hq = (c % Hkv) * G + g;
 }
 
-__device__ __forceinline__ float bf_lo(float x) { return x - (float)(__bf16)x; }
 
-// PRECISE instances run the tiles whose rows need the exact path (below);
-// the others never carry its registers.
+// The PRECISE body runs the tiles whose rows need the exact path (below); the
+// plain body never touches its registers.
 template <int D, bool CAUSAL, bool PRECISE>
-__global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a, int nq_launch, int qt_first) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, int hq, int qt) {
     using T = DqTile<D>;
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
-    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int S = a.S;
-    int b, hq, qt;
-    decode_q_item(blockIdx.x, nq_launch, qt_first, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
     const int hkv = hq / a.G;
     const size_t rowbase = ((size_t)b * a.Hq + hq) * (size_t)S;
     const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
@@ -138,8 +140,12 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a, int nq_lau
 
     const int nK = (S + kDqBK - 1) / kDqBK;
     const int jend = CAUSAL ? min(nK, (q0 + kDqBQ - 1) / kDqBK + 1) : nK;
-    int wjend = CAUSAL ? min(jend, (q0 + 32 * wave + 31) / kDqBK + 1) : jend;
-    if (q0 + 32 * wave >= S) wjend = 0;
+    const int row0 = q0 + 32 * wave;
+    int wjend = CAUSAL ? min(jend, (row0 + 31) / kDqBK + 1) : jend;
+    if (row0 >= S) wjend = 0;
+    const int W = CAUSAL ? a.window : 0;
+    const int jstart = W > 0 ? max(0, q0 - W + 1) / kDqBK : 0;
+    const int wjstart = W > 0 ? max(0, row0 - W + 1) / kDqBK : 0;
 
     __bf16* const Kring = smem;
     __bf16* const Vring = smem + 2 * T::TILE;
@@ -181,20 +187,20 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a, int nq_lau
     // slot while tile j is multiplied.
     for (int pass = precise ? 0 : 1; pass < 2; ++pass) {
         float dacc = 0.0f;
-        copy_tile(Kp, Kring, 0);
-        copy_tile(Vp, Vring, 0);
+        copy_tile(Kp, Kring + (jstart & 1) * T::TILE, jstart);
+        copy_tile(Vp, Vring + (jstart & 1) * T::TILE, jstart);
         wait_copies();
         __syncthreads();
-        for (int j = 0; j < jend; ++j) {
+        for (int j = jstart; j < jend; ++j) {
             if (j + 1 < jend) {
                 copy_tile(Kp, Kring + ((j + 1) & 1) * T::TILE, j + 1);
                 copy_tile(Vp, Vring + ((j + 1) & 1) * T::TILE, j + 1);
             }
-            if (j < wjend) {
+            if (j >= wjstart && j < wjend) {
                 const __bf16* Ks = Kring + (j & 1) * T::TILE;
                 const __bf16* Vs = Vring + (j & 1) * T::TILE;
                 const int k0 = j * kDqBK;
-                const bool need_mask = j == wjend - 1;
+                const bool need_mask = j == wjend - 1 || (W > 0 && k0 < row0 + 32 - W);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     f32x16 s = zero16(), dp = zero16();
@@ -205,12 +211,14 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a, int nq_lau
                         s = mfma32(kf, qf[dk], s);
                         dp = mfma32(vf, df[dk], dp);
                     }
-                    // key k0 + kb*32 + 4h + off is visible iff off <= lim
+                    // key k0 + kb*32 + 4h + off is visible iff lo <= off <= lim
                     const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - k0 - kb * 32 - 4 * h;
+                    const int lo = W > 0 ? qrow - W + 1 - k0 - kb * 32 - 4 * h : -(1 << 30);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float p = fast_exp2(fmaf(s[r], c, -lse2));
-                        if (need_mask && 8 * (r >> 2) + (r & 3) > lim) p = 0.0f;
+                        const int off = 8 * (r >> 2) + (r & 3);
+                        if (need_mask && (off > lim || off < lo)) p = 0.0f;
                         if (pass == 0) dacc += p * dp[r];
                         s[r] = p * (dp[r] - delta);
                     }
@@ -258,6 +266,20 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a, int nq_lau
                 *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * h) = v;
             }
     }
+}
+
+// One launch over every query tile; tiles 0 .. a.precise_tiles-1 take the exact
+// path, so its few workgroups run in the tail of the longest-first schedule.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+    const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
+    int b, hq, qt;
+    decode_q_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
+    if (qt < a.precise_tiles)
+        dq_body<D, CAUSAL, true>(a, smem, b, hq, qt);
+    else
+        dq_body<D, CAUSAL, false>(a, smem, b, hq, qt);
 }
 
 // ---------------------------------------------------------------------------
@@ -355,10 +377,12 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
         copy16_to_lds(a.v + (kvrow + kr) * D + col, Vs + (wave * T::VCOPIES + n) * 512);
     }
 
-    // Iterations: (g, query tile qi) for qi >= first visible tile; split p takes
-    // iterations p, p + kKvSplits, ...
+    // Iterations: (g, query tile qi) for the query tiles that see some key of the
+    // tile; split p takes iterations p, p + kKvSplits, ...
+    const int W = CAUSAL ? a.window : 0;
     const int qi_first = CAUSAL ? kv0 / kKvBQ : 0;
-    const int per_g = nQB - qi_first;
+    const int qi_last = W > 0 ? min(nQB - 1, (kv0 + kKvBK - 1 + W - 1) / kKvBQ) : nQB - 1;
+    const int per_g = qi_last - qi_first + 1;
     const int total = G * per_g;
     const int steps = (total + kKvSplits - 1) / kKvSplits;
 
@@ -434,9 +458,11 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
             const float* Dl = stage_dl(st);
             const int qs0 = (qi_first + it % per_g) * kKvBQ;
             const bool precise = a.precise_all || (precise_problem && qs0 < kPreciseRows);
-            const bool skip = (CAUSAL && qs0 + 31 < kw0) || qs0 >= S;  // every query precedes every key
+            // skip when every query precedes every key of the wave, or (window)
+            // every query lies past the band of the wave's last key
+            const bool skip = (CAUSAL && qs0 + 31 < kw0) || qs0 >= S || (W > 0 && qs0 > kw0 + 31 + W - 1);
             if (!skip) {
-                const bool need_mask = CAUSAL && qs0 < kw0 + 31;
+                const bool need_mask = (CAUSAL && qs0 < kw0 + 31) || (W > 0 && qs0 + 31 > kw0 + W - 1);
                 f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                 for (int dd = 0; dd < DK; ++dd) {
@@ -460,7 +486,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                         for (int e = 0; e < 4; ++e) {
                             const int r = 4 * rg + e;
                             float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-                            if (need_mask && key > qs0 + 8 * rg + 4 * h + e) p = 0.0f;
+                            const int qrow = qs0 + 8 * rg + 4 * h + e;
+                            if (need_mask && (key > qrow || (W > 0 && qrow >= key + W))) p = 0.0f;
                             pv[4 * half + e] = p;
                             dsv[4 * half + e] = p * (dp[r] - d4[e]);
                         }
@@ -554,34 +581,18 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& args, int stages, hipStream_t stream) {
+    BwdArgs a = args;
     if (stages & 1) {
         // Query tiles whose rows need the exact path: all of them when asked for,
         // else tile 0 of a causal problem or the single tile of S <= 128.
         const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
-        const long long heads = (long long)a.B * a.Hq;
-        int np, pfirst, nm, mfirst;  // (ranks, first tile) of the exact and plain launches
-        if (a.precise_all) {
-            np = nQ; pfirst = CAUSAL ? nQ - 1 : 0; nm = 0; mfirst = 0;
-        } else if (CAUSAL) {
-            np = 1; pfirst = 0; nm = nQ - 1; mfirst = nQ - 1;
-        } else if (a.S <= kPreciseRows) {
-            np = 1; pfirst = 0; nm = 0; mfirst = 0;
-        } else {
-            np = 0; pfirst = 0; nm = nQ; mfirst = 0;
-        }
-        if (nm > 0) {
-            hipLaunchKernelGGL((dq_kernel<D, CAUSAL, false>), dim3((unsigned)(heads * nm)), dim3(kDqThreads),
-                               DqTile<D>::LDS_BYTES, stream, a, nm, mfirst);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        if (np > 0) {
-            hipLaunchKernelGGL((dq_kernel<D, CAUSAL, true>), dim3((unsigned)(heads * np)), dim3(kDqThreads),
-                               DqTile<D>::LDS_BYTES, stream, a, np, pfirst);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
+        a.precise_tiles = a.precise_all ? nQ : (CAUSAL || a.S <= kPreciseRows) ? 1 : 0;
+        const long long blocks = (long long)a.B * a.Hq * nQ;
+        hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kDqThreads),
+                           DqTile<D>::LDS_BYTES, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     if (stages & 2) {
         const int nKB = (a.S + kKvBK - 1) / kKvBK;
@@ -602,14 +613,10 @@ hipError_t set_lds(K kernel, int bytes) {
 
 hipError_t bwd_setup_device() {
     hipError_t e;
-    if ((e = set_lds(dq_kernel<64, false, false>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<64, false, true>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<64, true, false>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<64, true, true>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, false, false>, DqTile<128>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, false, true>, DqTile<128>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, true, false>, DqTile<128>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, true, true>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<64, false>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<64, true>, DqTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, false>, DqTile<128>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<128, true>, DqTile<128>::LDS_BYTES))) return e;
     if ((e = set_lds(dkv_kernel<64, false>, KvTile<64>::LDS_BYTES))) return e;
     if ((e = set_lds(dkv_kernel<64, true>, KvTile<64>::LDS_BYTES))) return e;
     if ((e = set_lds(dkv_kernel<128, false>, KvTile<128>::LDS_BYTES))) return e;

@@ -30,6 +30,19 @@
 // that keeps both the K row reads and the V transpose reads free of bank
 // conflicts. Causal tiles entirely above the diagonal are never loaded; each
 // wave masks only its last tile (the diagonal, or the ragged end of S).
+//
+// Rows that see few keys carry large probabilities, where rounding P to bf16 for
+// the P V product would cost up to about 2^-9 of |V| in O. For those rows (a
+// window of at most 128 keys, the first query tile of a causal problem, a
+// single tile of S <= 128) the workgroup takes a PRECISE body that splits P into
+// a bf16 high part and a bf16 remainder and runs the P V product on both. Both
+// bodies live in one launch, so the few exact-path workgroups run in the tail
+// of the longest-first schedule instead of in a launch of their own.
+//
+// With a sliding window of W keys (query i sees keys i-W+1 .. i, the window of
+// the page's compressed sparse attention, Table 7) the tiles entirely below the
+// band are skipped as well, and a wave also masks the tiles that cross the
+// band's lower edge.
 #include "device.h"
 #include "kernels.h"
 
@@ -54,12 +67,13 @@ struct FwdTile {
     static_assert(COPIES >= 1, "copy split");
 };
 
-// Work item of workgroup `bid`: (b, hq, query tile). Causal tiles are issued
-// longest first. When the (b, kv-head) groups divide evenly over the 8 XCDs,
-// all query heads of one group land on the same XCD (workgroups are dealt to
-// XCDs round-robin by id), so its K/V stay in that XCD's L2.
-__device__ __forceinline__ void decode_item(int bid, int nQ, int B, int Hkv, int G, bool causal,
-                                            int& b, int& hq, int& qt) {
+// Work item of workgroup `bid` among nQ query-tile ranks: rank r is query tile
+// qt_first - r when causal (longest first), qt_first + r otherwise. When the
+// (b, kv-head) groups divide evenly over the 8 XCDs, all query heads of one
+// group land on the same XCD (workgroups are dealt to XCDs round-robin by id),
+// so its K/V stay in that XCD's L2.
+__device__ __forceinline__ void decode_item(int bid, int nQ, int qt_first, int B, int Hkv, int G,
+                                            bool causal, int& b, int& hq, int& qt) {
     const int C = B * Hkv;
     int rank, c, g;
     if ((C & 7) == 0) {
@@ -75,26 +89,22 @@ __device__ __forceinline__ void decode_item(int bid, int nQ, int B, int Hkv, int
         c = rem / G;
         g = rem % G;
     }
-    qt = causal ? nQ - 1 - rank : rank;
+    qt = causal ? qt_first - rank : qt_first + rank;
     b = c / Hkv;
     hq = (c % Hkv) * G + g;
 }
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
+template <int D, bool CAUSAL, bool PRECISE>
+__device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, int hq, int qt) {
     using T = FwdTile<D>;
     constexpr int DK = D / 16;  // k-steps of the score product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
-    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2;  // ping-pong group; waves w and w+4 share a SIMD
     const int h = lane >> 5, l32 = lane & 31;
     const int S = a.S;
-    const int nQ = (S + kFwdBQ - 1) / kFwdBQ;
-    int b, hq, qt;
-    decode_item(blockIdx.x, nQ, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
     const int hkv = hq / a.G;
     const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
     const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
@@ -126,6 +136,11 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
     const int jend = CAUSAL ? min(nK, (q0 + kFwdBQ - 1) / kFwdBK + 1) : nK;
     int wjend = CAUSAL ? min(jend, (row0 + 31) / kFwdBK + 1) : jend;
     if (row0 >= S) wjend = 0;  // a wave with no live rows only helps load
+    // Window: the workgroup's first tile holds the first row's first key, a wave's
+    // first tile its first row's; tiles with keys below row0 + 32 - W are masked.
+    const int W = CAUSAL ? a.window : 0;
+    const int jstart = W > 0 ? max(0, q0 - W + 1) / kFwdBK : 0;
+    const int wjstart = W > 0 ? max(0, row0 - W + 1) / kFwdBK : 0;
 
     __bf16* const Kring = smem;
     __bf16* const Vring = smem + 2 * T::TILE;
@@ -164,35 +179,42 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = zero16();
-    float m = -INFINITY, l = 0.0f;
+    // m starts finite: a row whose keys in its first tiles all fall below the
+    // window keeps m, and exp2(-inf - m) is then 0 rather than NaN; the first
+    // visible key moves it, and exp2(m - mnew) is 0 as it would be from -inf.
+    float m = -1e30f, l = 0.0f;
     f32x16 sc[2];   // scores of the tile between its matrix and softmax phases
     bf16x8 pk[4];   // probabilities of the tile between its softmax and P V phases
+    bf16x8 pl[4];   // their bf16 remainders (PRECISE only)
 
     // Matrix phase of tile j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
     auto matrix_phase = [&](int j) {
         __builtin_amdgcn_s_setprio(1);
-        if (j >= 1 && j - 1 < wjend) {
+        if (j - 1 >= wjstart && j - 1 < wjend) {
             const __bf16* Vs = Vring + ((j - 1) & 1) * T::TILE;
+            constexpr int MPER = PRECISE ? 2 : 1;  // MFMAs per V^T operand
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const bf16x4 v1 = lds_read_tr(Vs + voff[0][db] + 16 * t * D);
                     const bf16x4 v2 = lds_read_tr(Vs + voff[1][db] + 16 * t * D);
-                    oacc[db] = mfma32(concat(v1, v2), pk[t], oacc[db]);
+                    const bf16x8 vt = concat(v1, v2);
+                    oacc[db] = mfma32(vt, pk[t], oacc[db]);
+                    if (PRECISE) oacc[db] = mfma32(vt, pl[t], oacc[db]);
                 }
-            // transpose reads run LOOK MFMAs ahead: enough to cover LDS latency
-            // with bounded register use
+            // transpose reads run LOOK operands ahead of the MFMAs: enough to
+            // cover LDS latency with bounded register use
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 0);
 #pragma unroll
             for (int i = 0; i < 4 * DB - kLook; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MPER, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, kLook * MPER, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (j < wjend) {
+        if (j >= wjstart && j < wjend) {
             const __bf16* Ks = Kring + (j & 1) * T::TILE;
             sc[0] = zero16();
             sc[1] = zero16();
@@ -218,15 +240,19 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
     // Softmax phase of tile j: mask (last tile only), row maxima, lazy move of
     // the running maximum, probabilities as bf16 B operands, row sums.
     auto softmax_phase = [&](int j) {
-        if (j >= wjend) return;
-        if (j == wjend - 1) {
-            // key j*64 + 4h + off is visible iff off <= lim
-            const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - j * kFwdBK - 4 * h;
+        if (j < wjstart || j >= wjend) return;
+        if (j == wjend - 1 || (W > 0 && j * kFwdBK < row0 + 32 - W)) {
+            // key j*64 + 4h + off is visible iff lo <= off <= lim
+            const int base = j * kFwdBK + 4 * h;
+            const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - base;
+            const int lo = W > 0 ? qrow - W + 1 - base : -(1 << 30);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+                    if (off > lim || off < lo) sc[kb][r] = -INFINITY;
+                }
         }
         float mx0 = fmaxf(sc[0][0], sc[0][1]), mx1 = fmaxf(sc[1][0], sc[1][1]);
 #pragma unroll
@@ -238,8 +264,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
         // The running maximum only moves when some row's grows by more than
         // max_slack (log2 units; 8 for ordinary score spreads): until then every
         // exp2(t - m) <= 2^slack, carried by fp32 and bf16 without loss, and the
-        // O rescale is skipped. Tile 0 always moves it (m starts at -inf and key 0
-        // is visible to every row).
+        // O rescale is skipped. A row's first visible key always moves it.
         if (__any(mt > m + a.max_slack)) {
             const float mnew = fmaxf(m, mt);
             const float alpha = fast_exp2(m - mnew);
@@ -260,33 +285,38 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
                 rs[e & 3] += p[e];
             }
             pk[t] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            if (PRECISE)
+                pl[t] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
+                              bf_lo(p[6]), bf_lo(p[7]));
         }
         l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     };
 
-    // Prologue: K0 in K slot 0, K1 in K slot 1, V0 in V slot 0.
-    copy_tile(Kp, Kring, 0);
-    if (jend > 1) copy_tile(Kp, Kring + T::TILE, 1);
-    copy_tile(Vp, Vring, 0);
+    // Prologue: tile j sits in slot j & 1 of its ring; the first two K tiles and
+    // the first V tile.
+    copy_tile(Kp, Kring + (jstart & 1) * T::TILE, jstart);
+    if (jstart + 1 < jend) copy_tile(Kp, Kring + ((jstart + 1) & 1) * T::TILE, jstart + 1);
+    copy_tile(Vp, Vring + (jstart & 1) * T::TILE, jstart);
     wait_copies();
     __syncthreads();
 
     // Two phases per step s, each closed by a workgroup barrier. Group 0 runs the
     // matrix phase of tile s then its softmax; group 1 runs the softmax of tile
     // s-1 then the matrix phase of tile s, so on every SIMD one wave multiplies
-    // while the other exponentiates. Tiles K_s and V_{s-1} are read in step s;
+    // while the other exponentiates. Steps run from the first tile the workgroup
+    // needs to one past its last. Tiles K_s and V_{s-1} are read in step s;
     // at the start of step s+1 the copies of K_{s+2} and V_{s+1} go into the
     // slots those two released, and they are complete before the barrier that
     // ends step s+1. Every wave passes every barrier; waves with fewer tiles idle
     // in their late phases.
     auto refill = [&](int s) {
-        if (s >= 1) {
+        if (s > jstart) {
             if (s + 1 < jend) copy_tile(Kp, Kring + ((s - 1) & 1) * T::TILE, s + 1);
             if (s < jend) copy_tile(Vp, Vring + (s & 1) * T::TILE, s);
         }
     };
     if (grp == 0) {
-        for (int s = 0; s <= jend; ++s) {
+        for (int s = jstart; s <= jend; ++s) {
             refill(s);
             matrix_phase(s);
             __syncthreads();
@@ -295,9 +325,9 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
             __syncthreads();
         }
     } else {
-        for (int s = 0; s <= jend; ++s) {
+        for (int s = jstart; s <= jend; ++s) {
             refill(s);
-            if (s >= 1) softmax_phase(s - 1);
+            softmax_phase(s - 1);
             __syncthreads();
             matrix_phase(s);
             wait_copies();
@@ -322,13 +352,37 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
     }
 }
 
+// Query tiles 0 .. a.precise_tiles-1 take the exact P V product.
 template <int D, bool CAUSAL>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+__global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
     const int nQ = (a.S + kFwdBQ - 1) / kFwdBQ;
+    int b, hq, qt;
+    decode_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
+    if (qt < a.precise_tiles)
+        fwd_body<D, CAUSAL, true>(a, smem, b, hq, qt);
+    else
+        fwd_body<D, CAUSAL, false>(a, smem, b, hq, qt);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
+    // Rows that see at most 128 keys take the exact P V product: every tile of a
+    // window of <= 128 keys, else tile 0 of a causal problem (rows 0..255 see at
+    // most 256 keys; the first 128 of them, the ones that need it, are there) or
+    // the single tile of S <= 128.
+    const int nQ = (args.S + kFwdBQ - 1) / kFwdBQ;
+    FwdArgs a = args;
+    a.precise_tiles = (CAUSAL && a.window > 0 && a.window <= 128) ? nQ : (CAUSAL || a.S <= 128) ? 1 : 0;
     const long long blocks = (long long)a.B * a.Hq * nQ;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kFwdThreads),
                        FwdTile<D>::LDS_BYTES, stream, a);
     return hipGetLastError();
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, int bytes) {
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 }  // namespace
@@ -336,17 +390,10 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 // Raise the dynamic-LDS limit of every forward instance on the current device.
 hipError_t fwd_setup_device() {
     hipError_t e;
-    if ((e = hipFuncSetAttribute((const void*)fwd_kernel<64, false>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, FwdTile<64>::LDS_BYTES)))
-        return e;
-    if ((e = hipFuncSetAttribute((const void*)fwd_kernel<64, true>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, FwdTile<64>::LDS_BYTES)))
-        return e;
-    if ((e = hipFuncSetAttribute((const void*)fwd_kernel<128, false>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, FwdTile<128>::LDS_BYTES)))
-        return e;
-    return hipFuncSetAttribute((const void*)fwd_kernel<128, true>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, FwdTile<128>::LDS_BYTES);
+    if ((e = set_lds(fwd_kernel<64, false>, FwdTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(fwd_kernel<64, true>, FwdTile<64>::LDS_BYTES))) return e;
+    if ((e = set_lds(fwd_kernel<128, false>, FwdTile<128>::LDS_BYTES))) return e;
+    return set_lds(fwd_kernel<128, true>, FwdTile<128>::LDS_BYTES);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t stream) {

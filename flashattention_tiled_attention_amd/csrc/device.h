@@ -46,6 +46,11 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
     return r;
 }
 
+// Remainder of x after rounding it to bf16: x = bf16(x) + bf_lo(x) up to the
+// rounding of the remainder, so a product with hi and lo bf16 operands carries
+// about 16 significant bits of x.
+__device__ __forceinline__ float bf_lo(float x) { return x - (float)(__bf16)x; }
+
 __device__ __forceinline__ bf16x4 pack4(float a0, float a1, float a2, float a3) {
     bf16x4 r;
     r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;

@@ -46,4 +46,6 @@ CONFIGS = {
     "long_causal_gqa_s8192": dict(B=2, Hq=32, Hkv=8, S=8192, D=128, causal=True, bwd=False),
     "mha_noncausal_s2048_d64": dict(B=8, Hq=16, Hkv=16, S=2048, D=64, causal=False, bwd=False),
     "llama8b_causal_gqa_s4096_bwd": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, bwd=True),
+    # causal sliding window of 128 keys (the window of the compressed sparse attention, Table 7)
+    "llama8b_window128_s4096": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, window=128, bwd=True),
 }

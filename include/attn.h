@@ -51,7 +51,8 @@ enum attn_status {
     ATTN_ERR_WORKSPACE = 6,     /* workspace is NULL or smaller than attn_bwd_workspace_bytes() */
     ATTN_ERR_SCALE = 7,         /* scale is NaN or infinite */
     ATTN_ERR_HIP = 8,           /* the HIP runtime failed (no device, launch error) */
-    ATTN_ERR_DEVICE = 9         /* the current device is not a gfx950 GPU */
+    ATTN_ERR_DEVICE = 9,        /* the current device is not a gfx950 GPU */
+    ATTN_ERR_WINDOW = 10        /* a sliding window of fewer than 1 key */
 };
 
 /*
@@ -116,6 +117,27 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, co
                   const void* dout, float* dq, float* dk, float* dv,
                   int B, int Hq, int Hkv, int S, int D, int causal, float scale,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sliding-window causal attention: query row i sees only the `window` most
+ * recent keys, i - window < j <= i. This is the window every query of the
+ * compressed sparse attention on the same page attends to (Table 7, window =
+ * 128; section 3.1.1 describes its sliding-window kernels); within the band,
+ * Eq. (1) and its gradient are computed exactly as by attn_fwd / attn_bwd with
+ * causal != 0. window >= S gives the plain causal result. Tiles outside the
+ * band are neither loaded nor multiplied, so the work is O(S * window).
+ *   window  >= 1, else ATTN_ERR_WINDOW (checked before anything else)
+ * Every other argument, the layouts and the errors are those of attn_fwd and
+ * attn_bwd; attn_bwd_window takes a workspace of
+ * attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, 1) bytes, and needs o and lse
+ * from attn_fwd_window with the same window.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int S, int D, int window, float scale, void* stream);
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, float* dq, float* dk, float* dv,
+                    int B, int Hq, int Hkv, int S, int D, int window, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

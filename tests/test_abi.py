@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = fa.attn_status_str(code)
         assert isinstance(s, str) and s
     assert fa.attn_status_str(0) == "ok"
@@ -96,6 +96,35 @@ def test_bwd_workspace():
     assert lib.attn_bwd_workspace_bytes(1, 4, 2, 128, 96, 1) == 0
 
 
+def fwd_window(*, window=128, q=P, B=1, Hq=4, Hkv=2, S=128, D=128, scale=0.088):
+    return fa.load_library().attn_fwd_window(q, P, P, P, P, B, Hq, Hkv, S, D, window, scale, None)
+
+
+def bwd_window(*, window=128, dq=P, B=1, Hq=4, Hkv=2, S=128, D=128, scale=0.088, wsb=None):
+    lib = fa.load_library()
+    if wsb is None:
+        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, 1)
+    return lib.attn_bwd_window(P, P, P, P, P, P, dq, P, P, B, Hq, Hkv, S, D, window, scale, P, wsb, None)
+
+
+@pytest.mark.parametrize("window", [0, -1, -(1 << 30)])
+def test_window_rejects_empty_window(window):
+    assert fwd_window(window=window) == fa.ATTN_ERR_WINDOW
+    assert bwd_window(window=window) == fa.ATTN_ERR_WINDOW
+
+
+def test_window_validates_like_the_plain_entry_points():
+    assert fwd_window(q=None) == fa.ATTN_ERR_NULL
+    assert fwd_window(Hq=6, Hkv=4) == fa.ATTN_ERR_GQA
+    assert fwd_window(D=96) == fa.ATTN_ERR_UNSUPPORTED_D
+    assert fwd_window(scale=math.nan) == fa.ATTN_ERR_SCALE
+    assert fwd_window(q=MIS) == fa.ATTN_ERR_ALIGN
+    assert bwd_window(dq=None) == fa.ATTN_ERR_NULL
+    assert bwd_window(dq=MIS) == fa.ATTN_ERR_ALIGN
+    assert bwd_window(wsb=16) == fa.ATTN_ERR_WORKSPACE
+    assert bwd_window(S=0) == fa.ATTN_ERR_SHAPE
+
+
 def test_no_gpu_reports_hip_error():
     """Valid arguments on a machine without a usable gfx950 device end in a HIP or device
     error from the set-up step, never in a launch."""
@@ -103,3 +132,4 @@ def test_no_gpu_reports_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert fwd() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
+    assert fwd_window() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)

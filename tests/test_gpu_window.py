@@ -1,0 +1,114 @@
+"""Sliding-window causal attention on the GPU (attn_fwd_window / attn_bwd_window through
+the C ABI) against the fp64 oracle with the same window: query i sees keys i-W+1 .. i."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import flashattention_tiled_attention_amd as fa
+from flashattention_tiled_attention_amd.inputs import CONFIGS, bf16_to_f32, qkv
+from tests.gpu_util import TOL_LSE, assert_close, bf16_dev_to_f64, f32_dev_to_f64, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(q, k, v, do, window, scale):
+    import torch
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    o, lse = fa.fwd(tq, tk, tv, scale=scale, window=window)
+    grads = None
+    if do is not None:
+        grads = fa.bwd(tq, tk, tv, o, lse, to_dev(do), scale=scale, window=window)
+    torch.cuda.synchronize()
+    out = [bf16_dev_to_f64(o), f32_dev_to_f64(lse)]
+    if grads is not None:
+        out += [f32_dev_to_f64(g) for g in grads]
+    return out
+
+
+def check(B, Hq, Hkv, S, D, W, seed, scale=None, backward=True):
+    print("case B=%d Hq=%d Hkv=%d S=%d D=%d window=%d seed=%d scale=%s backward=%d"
+          % (B, Hq, Hkv, S, D, W, seed, scale, backward), flush=True)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, seed, with_dout=True)
+    got = run(q, k, v, do if backward else None, W, scale)
+    o_ref, lse_ref = oracle.fwd(q, k, v, True, scale, W)
+    assert_close(got[0], o_ref, "O")
+    assert_close(got[1], lse_ref, "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)
+    if backward:
+        rq, rk, rv = oracle.bwd(q, k, v, do, True, scale, W)
+        assert_close(got[2], rq, "dQ")
+        assert_close(got[3], rk, "dK")
+        assert_close(got[4], rv, "dV")
+
+
+@pytest.mark.parametrize("W", [1, 2, 31, 64, 65, 127, 128, 129, 200, 300])
+@pytest.mark.parametrize("D", [64, 128])
+def test_windows(W, D):
+    check(1, 4, 2, 390, D, W, seed=W + D)
+
+
+@pytest.mark.parametrize("S", [1, 5, 63, 64, 65, 129, 257])
+def test_ragged_lengths(S):
+    check(2, 2, 1, S, 128, 128, seed=S)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (8, 2), (8, 1), (16, 16)])
+def test_gqa_groups(Hq, Hkv):
+    check(2, Hq, Hkv, 300, 128, 100, seed=Hq * 10 + Hkv)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0884, 0.5])
+def test_scales(scale):
+    check(1, 4, 2, 333, 128, 128, seed=7, scale=scale)
+
+
+def test_multi_tile():
+    check(2, 8, 2, 1500, 128, 500, seed=11)
+    check(1, 16, 8, 1100, 64, 128, seed=12)
+
+
+def test_window_covering_sequence_is_causal():
+    """A window of S or more keys is the causal triangle: the results equal attn_fwd /
+    attn_bwd with causal set, bit for bit."""
+    import torch
+    B, Hq, Hkv, S, D = 1, 8, 2, 700, 128
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 13, with_dout=True)
+    tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o1, l1 = fa.fwd(tq, tk, tv, causal=True)
+    o2, l2 = fa.fwd(tq, tk, tv, window=S)
+    g1 = fa.bwd(tq, tk, tv, o1, l1, tdo, causal=True)
+    g2 = fa.bwd(tq, tk, tv, o2, l2, tdo, window=S + 50)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_full_size_window128_sampled():
+    """The Llama-3.1-8B attention shape (B=1, Hq=32, Hkv=8, S=4096, D=128) with the
+    128-key window: O/lse and dQ on sampled rows, dK/dV on sampled keys of two KV heads,
+    plus sum_j dV_j = sum of dO over each group."""
+    c = CONFIGS["llama8b_window128_s4096"]
+    B, Hq, Hkv, S, D, W = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], c["window"]
+    scale = 1.0 / math.sqrt(D)
+    print("case full-size window B=%d Hq=%d Hkv=%d S=%d D=%d W=%d" % (B, Hq, Hkv, S, D, W), flush=True)
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 0, with_dout=True)
+    o, lse, dq, dk, dv = run(q, k, v, do, W, scale)
+    rows = sample_rows(B, Hq, S, 300, seed=4)
+    ro, rl = oracle.fwd_rows(q, k, v, rows, True, scale, W)
+    assert_close(o.reshape(-1, D)[rows], ro, "O (%d sampled rows)" % rows.size)
+    assert_close(lse.reshape(-1)[rows], rl, "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)
+    rng = np.random.default_rng(5)
+    keys = []
+    for grp in (0, Hkv - 1):
+        ks = set([0, 1, 127, 128, S - 129, S - 128, S - 1]) | set(int(x) for x in rng.integers(0, S, 40))
+        keys += [grp * S + j for j in sorted(ks)]
+    kvrows = np.array(keys, dtype=np.int64)
+    rq, rk, rv = oracle.bwd_rows(q, k, v, do, rows, kvrows, True, scale, W)
+    assert_close(dq.reshape(-1, D)[rows], rq, "dQ (%d sampled rows)" % rows.size)
+    assert_close(dk.reshape(-1, D)[kvrows], rk, "dK (%d sampled keys)" % kvrows.size)
+    assert_close(dv.reshape(-1, D)[kvrows], rv, "dV (%d sampled keys)" % kvrows.size)
+    dof = bf16_to_f32(do).astype(np.float64).reshape(B, Hkv, Hq // Hkv, S, D)
+    assert_close(dv.sum(axis=2), dof.sum(axis=(2, 3)), "sum_j dV_j", tol_max=0.05, tol_mean=0.01)
