@@ -211,16 +211,22 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
                         s = mfma32(kf, qf[dk], s);
                         dp = mfma32(vf, df[dk], dp);
                     }
-                    // key k0 + kb*32 + 4h + off is visible iff lo <= off <= lim
-                    const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - k0 - kb * 32 - 4 * h;
-                    const int lo = W > 0 ? qrow - W + 1 - k0 - kb * 32 - 4 * h : -(1 << 30);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lse2));
+                    if (need_mask) {  // one uniform branch, taken on edge tiles only
+                        // key k0 + kb*32 + 4h + off is visible iff lo <= off <= lim
+                        const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - k0 - kb * 32 - 4 * h;
+                        const int lo = W > 0 ? qrow - W + 1 - k0 - kb * 32 - 4 * h : -(1 << 30);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int off = 8 * (r >> 2) + (r & 3);
+                            s[r] = (off > lim || off < lo) ? 0.0f : s[r];
+                        }
+                    }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float p = fast_exp2(fmaf(s[r], c, -lse2));
-                        const int off = 8 * (r >> 2) + (r & 3);
-                        if (need_mask && (off > lim || off < lo)) p = 0.0f;
-                        if (pass == 0) dacc += p * dp[r];
-                        s[r] = p * (dp[r] - delta);
+                        if (precise) dacc += s[r] * dp[r];  // used by pass 0 only
+                        s[r] = s[r] * (dp[r] - delta);
                     }
                     if (pass == 0) continue;
                     // dQ^T += K^T dS^T over two 16-key steps; K^T via transpose loads.
@@ -410,8 +416,11 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
             copy16_to_lds(a.dout + off, stage_do(st) + (w2 * T::QCOPIES + n) * 512);
         }
         if (ptid < kKvBQ) {
+            // raw values only: any use of a loaded value here would make the wave
+            // wait for its vector-memory counter, which also counts the tile
+            // copies just issued, and so for the whole prefetch
             const int qr = qr0 + ptid;
-            lst = qr < S ? a.lse[rb + qr] * kLog2e : INFINITY;
+            lst = qr < S ? a.lse[rb + qr] : INFINITY;
             dlst = qr < S ? a.delta[rb + qr] : 0.0f;
         }
     };
@@ -419,7 +428,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
         const int it = kKvSplits * step + split;
         if (it >= total) return;
         if (ptid < kKvBQ) {
-            stage_lse(step & 1)[ptid] = lst;
+            stage_lse(step & 1)[ptid] = lst * kLog2e;
             stage_dl(step & 1)[ptid] = dlst;
         }
     };
@@ -476,7 +485,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                 // dV^T += dO^T P and dK^T += Q^T dS over two 16-query steps.
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2) {
-                    float pv[8], dsv[8];
+                    float pv[8], dsv[8], dl[8];
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const int rg = 2 * t2 + half;
@@ -484,14 +493,19 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                         const f32x4 d4 = *(const f32x4*)(Dl + 8 * rg + 4 * h);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int r = 4 * rg + e;
-                            float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-                            const int qrow = qs0 + 8 * rg + 4 * h + e;
-                            if (need_mask && (key > qrow || (W > 0 && qrow >= key + W))) p = 0.0f;
-                            pv[4 * half + e] = p;
-                            dsv[4 * half + e] = p * (dp[r] - d4[e]);
+                            pv[4 * half + e] = fast_exp2(fmaf(s[4 * rg + e], c, -l4[e]));
+                            dl[4 * half + e] = d4[e];
                         }
                     }
+                    if (need_mask) {  // one uniform branch, taken on edge tiles only
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int qrow = qs0 + 8 * (2 * t2 + (i >> 2)) + 4 * h + (i & 3);
+                            pv[i] = (key > qrow || (W > 0 && qrow >= key + W)) ? 0.0f : pv[i];
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) dsv[i] = pv[i] * (dp[8 * t2 + i] - dl[i]);
                     const bf16x8 ph = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
                     const bf16x8 sh = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
                     bf16x8 pl, sl;

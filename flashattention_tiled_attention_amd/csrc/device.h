@@ -96,11 +96,28 @@ __device__ __forceinline__ int swz(int row, int col) {
 
 // Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
 // lane i's 16 bytes land at lds_wave_base + 16 i. lds_wave_base must be the same
-// for every lane of the wave. Completion is tracked by vmcnt.
+// for every lane of the wave. Completion is tracked by vmcnt only: the caller
+// waits with wait_copies() and then a workgroup barrier before any wave reads
+// the destination. The instruction is issued from inline assembly on purpose:
+// the compiler then does not know that LDS is being written behind its back, and
+// does not make every later LDS read (of any slot) and every workgroup fence
+// wait for the copy to land, which would expose the full copy latency in every
+// step of the tile pipeline. The "memory" clobber keeps LDS accesses from moving
+// across the copy.
 __device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                     (ATTN_LDS void*)lds_wave_base, 16, 0, 0);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS void*)lds_wave_base);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gsrc), "s"(lds)
+        : "memory", "m0");
 }
+// Wait until every copy this wave issued has landed in LDS (s_waitcnt 0). The
+// compiler sees this wait, so it also knows that every vector-memory load it
+// issued before is complete; otherwise it would keep counter waits for those
+// loads inside the tile loop, and those would now also wait for the copies.
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Combine a value with the same register of the lane 32 away (v_permlane32_swap).
