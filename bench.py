@@ -94,17 +94,22 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
             "kind": "oracle", "sample": sample, "seconds": round(secs, 2)}
 
 
-KERNEL_SOURCES = {
-    "fwd_kernel": "flashattention_tiled_attention_amd/csrc/attn_fwd.hip",
-    "dq_kernel": "flashattention_tiled_attention_amd/csrc/attn_bwd.hip",
-    "dkv_kernel": "flashattention_tiled_attention_amd/csrc/attn_bwd.hip",
+_CSRC = "flashattention_tiled_attention_amd/csrc/"
+KERNEL_SOURCES = {   # every source a kernel's machine code depends on
+    "fwd_kernel": [_CSRC + "attn_fwd.hip", _CSRC + "device.h", _CSRC + "kernels.h"],
+    "dq_kernel": [_CSRC + "attn_bwd.hip", _CSRC + "device.h", _CSRC + "kernels.h"],
+    "dkv_kernel": [_CSRC + "attn_bwd.hip", _CSRC + "device.h", _CSRC + "kernels.h"],
 }
 
 
 def source_sha(kernel):
+    """First 16 hex digits of sha256 over the kernel's sources, concatenated in order."""
     import hashlib
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def hbm_traffic(kernel):
