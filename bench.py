@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward kernel alone")
     ap.add_argument("--workload", default=WORKLOAD, help="an entry of inputs.CONFIGS (default %(default)s)")
     ap.add_argument("--copy-probe", action="store_true", help="run only the HBM counter calibration copy")
+    ap.add_argument("--lds-transpose", action="store_true",
+                    help="run only the LDS-to-register transpose microbenchmark (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -160,6 +162,12 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.lds_transpose:
+        from flashattention_tiled_attention_amd import lds_transpose
+        rows = lds_transpose.table()
+        print(json.dumps({"metric": "LDS-to-register operand bandwidth, normalized to ds_read_b128",
+                          "unit": "GB/s", "device": "MI355X (gfx950)", "methods": rows}), flush=True)
         return
 
     import torch

@@ -1,4 +1,5 @@
-"""Build the HIP attention library (libattn.so) in-tree for gfx950 with hipcc."""
+"""Build the HIP attention library (libattn.so) and the LDS transpose
+microbenchmark (liblds_transpose.so) in-tree for gfx950 with hipcc."""
 import os
 import subprocess
 import sys
@@ -10,6 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
 SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip"]
+LDS_LIB = os.path.join(HERE, "liblds_transpose.so")
+LDS_SOURCES = ["lds_transpose.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -26,22 +29,25 @@ def _compile(src, obj, extra):
 
 
 def build(extra=None, verbose=False):
-    """Compile every source and link libattn.so; raises on any compiler error."""
+    """Compile every source and link libattn.so and liblds_transpose.so; raises on any
+    compiler error. Returns the path of libattn.so."""
     extra = list(extra or [])
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(SOURCES, objs)))
+    srcs = SOURCES + LDS_SOURCES
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in srcs]
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        results = list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(srcs, objs)))
     for rc, cmd, err in results:
         if err and (verbose or rc):
             sys.stderr.write(err + "\n")
         if rc:
             raise RuntimeError("hipcc failed: " + " ".join(cmd))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    for lib, members in ((LIB, objs[:len(SOURCES)]), (LDS_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + members
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

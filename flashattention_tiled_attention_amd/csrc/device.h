@@ -103,7 +103,8 @@ __device__ __forceinline__ int swz(int row, int col) {
 // does not make every later LDS read (of any slot) and every workgroup fence
 // wait for the copy to land, which would expose the full copy latency in every
 // step of the tile pipeline. The "memory" clobber keeps LDS accesses from moving
-// across the copy.
+// across the copy. M0 (the LDS address of the copy) cannot be named as a clobber
+// (the compiler reserves it); these kernels keep no value of their own in M0.
 __device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_base) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS void*)lds_wave_base);
     asm volatile(
@@ -112,7 +113,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_b
         "global_load_lds_dwordx4 %0, off"
         :
         : "v"(gsrc), "s"(lds)
-        : "memory", "m0");
+        : "memory");
 }
 // Wait until every copy this wave issued has landed in LDS (s_waitcnt 0). The
 // compiler sees this wait, so it also knows that every vector-memory load it

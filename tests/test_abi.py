@@ -32,6 +32,23 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_lds_transpose_library_exports_its_header():
+    from flashattention_tiled_attention_amd import lds_transpose
+    text = open(os.path.join(ROOT, "include", "lds_transpose.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(lds_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["lds_transpose_bench"]
+    lib = lds_transpose.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    # argument checks happen before any HIP call
+    import ctypes
+    ms = ctypes.c_float(0)
+    assert lib.lds_transpose_bench(7, 1, 1, 1, ctypes.byref(ms), P, P, None) == 1
+    assert lib.lds_transpose_bench(0, 0, 1, 1, ctypes.byref(ms), P, P, None) == 2
+    assert lib.lds_transpose_bench(0, 1, 1, 1, ctypes.byref(ms), MIS, P, None) == 2
+
+
 def test_status_strings():
     for code in range(0, 11):
         s = fa.attn_status_str(code)
