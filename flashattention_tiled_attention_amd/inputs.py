@@ -27,15 +27,17 @@ def bf16_to_f32(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-def qkv(B, Hq, Hkv, S, D, seed=0, with_dout=False):
-    """Q [B,Hq,S,D], K and V [B,Hkv,S,D] (and dO like Q) as bf16 bits, iid N(0,1)."""
+def qkv(B, Hq, Hkv, S, D, seed=0, with_dout=False, Dv=None):
+    """Q [B,Hq,S,D], K [B,Hkv,S,D], V [B,Hkv,S,Dv] (and dO [B,Hq,S,Dv]) as bf16 bits,
+    iid N(0,1). Dv (the value head dimension) defaults to D."""
+    Dv = D if Dv is None else Dv
     rng = np.random.default_rng(seed)
     q = bf16_bits(rng.standard_normal((B, Hq, S, D), dtype=np.float32))
     k = bf16_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32))
-    v = bf16_bits(rng.standard_normal((B, Hkv, S, D), dtype=np.float32))
+    v = bf16_bits(rng.standard_normal((B, Hkv, S, Dv), dtype=np.float32))
     if not with_dout:
         return q, k, v
-    dout = bf16_bits(rng.standard_normal((B, Hq, S, D), dtype=np.float32))
+    dout = bf16_bits(rng.standard_normal((B, Hq, S, Dv), dtype=np.float32))
     return q, k, v, dout
 
 

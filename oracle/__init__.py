@@ -10,8 +10,9 @@ in double precision, plus the exact gradient of that equation (the products
 section 2.1's Table 3 lists for the backward pass). The C source,
 ``attn_oracle.c``, documents every reading of the page it takes.
 
-Inputs are numpy ``uint16`` arrays of bf16 bit patterns in [B][H][S][D] layout;
-outputs are float64 arrays.
+Inputs are numpy ``uint16`` arrays of bf16 bit patterns in [B][H][S][D] layout
+(V and dO may have their own last dimension Dv, the d_v of Eq. (1)); outputs are
+float64 arrays.
 """
 import ctypes
 import os
@@ -48,13 +49,14 @@ def _shapes(q, k, v, dout=None):
             raise ValueError("%s must be a C-contiguous uint16 [B][H][S][D] array of bf16 bits" % name)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [B][Hkv][S][D] matching q")
-    if dout is not None and dout.shape != q.shape:
-        raise ValueError("dout must match q")
+    Dv = v.shape[3]
+    if k.shape != (B, Hkv, S, D) or v.shape != (B, Hkv, S, Dv):
+        raise ValueError("k must be [B][Hkv][S][D] and v [B][Hkv][S][Dv], matching q")
+    if dout is not None and dout.shape != (B, Hq, S, Dv):
+        raise ValueError("dout must be [B][Hq][S][Dv]")
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    return B, Hq, Hkv, S, D
+    return B, Hq, Hkv, S, D, Dv
 
 
 class Oracle:
@@ -67,11 +69,11 @@ class Oracle:
         I64 = ctypes.c_int64
         Dbl = ctypes.c_double
         lib.oracle_num_threads.restype = I
-        lib.oracle_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, Dbl]
-        lib.oracle_attn_fwd_rows.argtypes = [P, P, P, P, I64, P, P, I, I, I, I, I, I, I, Dbl]
-        lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_attn_fwd_rows.argtypes = [P, P, P, P, I64, P, P, I, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, Dbl]
         lib.oracle_attn_bwd_rows.argtypes = [P, P, P, P, P, I64, P, P, I64, P, P,
-                                             I, I, I, I, I, I, I, Dbl]
+                                             I, I, I, I, I, I, I, I, Dbl]
         for f in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_attn_bwd,
                   lib.oracle_attn_bwd_rows):
             f.restype = I
@@ -83,38 +85,38 @@ class Oracle:
         return self.lib.oracle_num_threads()
 
     def fwd(self, q, k, v, causal, scale, window=0):
-        """O [B,Hq,S,D] and lse [B,Hq,S] (natural log), float64. window > 0 (causal only):
+        """O [B,Hq,S,Dv] and lse [B,Hq,S] (natural log), float64. window > 0 (causal only):
         query i sees keys i-window+1 .. i."""
-        B, Hq, Hkv, S, D = _shapes(q, k, v)
-        o = np.empty((B, Hq, S, D), np.float64)
+        B, Hq, Hkv, S, D, Dv = _shapes(q, k, v)
+        o = np.empty((B, Hq, S, Dv), np.float64)
         lse = np.empty((B, Hq, S), np.float64)
         rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                      B, Hq, Hkv, S, D, int(bool(causal)), int(window), float(scale))
+                                      B, Hq, Hkv, S, D, Dv, int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_fwd failed: %d" % rc)
         return o, lse
 
     def fwd_rows(self, q, k, v, rows, causal, scale, window=0):
         """O and lse of selected flat query rows ((b*Hq + hq)*S + i)."""
-        B, Hq, Hkv, S, D = _shapes(q, k, v)
+        B, Hq, Hkv, S, D, Dv = _shapes(q, k, v)
         rows = np.ascontiguousarray(rows, dtype=np.int64)
-        o = np.empty((rows.size, D), np.float64)
+        o = np.empty((rows.size, Dv), np.float64)
         lse = np.empty((rows.size,), np.float64)
         rc = self.lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(rows), rows.size,
-                                           _ptr(o), _ptr(lse), B, Hq, Hkv, S, D,
+                                           _ptr(o), _ptr(lse), B, Hq, Hkv, S, D, Dv,
                                            int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_fwd_rows failed: %d" % rc)
         return o, lse
 
     def bwd(self, q, k, v, dout, causal, scale, window=0):
-        """dQ [B,Hq,S,D] and dK, dV [B,Hkv,S,D] (summed over each group), float64."""
-        B, Hq, Hkv, S, D = _shapes(q, k, v, dout)
+        """dQ [B,Hq,S,D], dK [B,Hkv,S,D] and dV [B,Hkv,S,Dv] (summed over each group), float64."""
+        B, Hq, Hkv, S, D, Dv = _shapes(q, k, v, dout)
         dq = np.empty((B, Hq, S, D), np.float64)
         dk = np.empty((B, Hkv, S, D), np.float64)
-        dv = np.empty((B, Hkv, S, D), np.float64)
+        dv = np.empty((B, Hkv, S, Dv), np.float64)
         rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
-                                      _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D,
+                                      _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, Dv,
                                       int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_bwd failed: %d" % rc)
@@ -122,15 +124,15 @@ class Oracle:
 
     def bwd_rows(self, q, k, v, dout, qrows, kvrows, causal, scale, window=0):
         """dQ of selected query rows; dK, dV of selected key rows ((b*Hkv + hkv)*S + j)."""
-        B, Hq, Hkv, S, D = _shapes(q, k, v, dout)
+        B, Hq, Hkv, S, D, Dv = _shapes(q, k, v, dout)
         qrows = np.ascontiguousarray(qrows, dtype=np.int64)
         kvrows = np.ascontiguousarray(kvrows, dtype=np.int64)
         dq = np.empty((qrows.size, D), np.float64)
         dk = np.empty((kvrows.size, D), np.float64)
-        dv = np.empty((kvrows.size, D), np.float64)
+        dv = np.empty((kvrows.size, Dv), np.float64)
         rc = self.lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(qrows),
                                            qrows.size, _ptr(dq), _ptr(kvrows), kvrows.size,
-                                           _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D,
+                                           _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, Dv,
                                            int(bool(causal)), int(window), float(scale))
         if rc:
             raise ValueError("oracle_attn_bwd_rows failed: %d" % rc)

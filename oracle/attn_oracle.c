@@ -23,10 +23,12 @@
  *   - grouped-query attention: query head hq reads key/value head hq / (Hq/Hkv);
  *   - lse_i = m_i + ln(sum_j exp(s_ij - m_i)), natural log; subtracting the row
  *     maximum m_i is an exact rescaling, not an approximation;
- *   - dK and dV of a key/value head are summed over every query head that reads it.
+ *   - dK and dV of a key/value head are summed over every query head that reads it;
+ *   - Eq. (1) gives queries and keys d columns and values d_v: here D and Dv.
+ *     V, O, dO and dV have Dv columns, Q, K, dQ and dK have D.
  *
- * Layout: contiguous [B][H][S][D]; inputs are bf16 bit patterns (uint16),
- * widened exactly to double; every output is double.
+ * Layout: contiguous [B][H][S][D] (Dv for V, O, dO, dV); inputs are bf16 bit
+ * patterns (uint16), widened exactly to double; every output is double.
  * All functions return 0 on success and a negative value on bad arguments
  * (-5: a window that is negative, or set without causal).
  */
@@ -38,7 +40,7 @@
 
 typedef struct {
     const uint16_t *q, *k, *v, *dout;
-    int B, Hq, Hkv, S, D, G, causal, window;
+    int B, Hq, Hkv, S, D, Dv, G, causal, window;
     double scale;
 } ctx_t;
 
@@ -49,18 +51,19 @@ static double widen(uint16_t h) {
     return (double)f;
 }
 
-static int check_args(int B, int Hq, int Hkv, int S, int D, int causal, int window) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return -1;
+static int check_args(int B, int Hq, int Hkv, int S, int D, int Dv, int causal, int window) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || Dv <= 0) return -1;
     if (Hq % Hkv != 0) return -2;
     if (window < 0 || (window > 0 && !causal)) return -5;
     return 0;
 }
 
-static size_t qrow_off(const ctx_t* c, int b, int hq, int i) {
-    return (((size_t)b * c->Hq + hq) * c->S + i) * (size_t)c->D;
+/* Element offset of a row: `width` is D for Q, K, dQ, dK and Dv for V, O, dO, dV. */
+static size_t qrow_off(const ctx_t* c, int b, int hq, int i, int width) {
+    return (((size_t)b * c->Hq + hq) * c->S + i) * (size_t)width;
 }
-static size_t kvrow_off(const ctx_t* c, int b, int hkv, int j) {
-    return (((size_t)b * c->Hkv + hkv) * c->S + j) * (size_t)c->D;
+static size_t kvrow_off(const ctx_t* c, int b, int hkv, int j, int width) {
+    return (((size_t)b * c->Hkv + hkv) * c->S + j) * (size_t)width;
 }
 
 static double dot_bf16(const uint16_t* x, const uint16_t* y, int D) {
@@ -90,11 +93,11 @@ static int last_query(const ctx_t* c, int j) {
  */
 static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
                     double* o_out, double* lse_out, double* delta_out, double* dq_out) {
-    const int D = c->D, j0 = first_key(c, i), j1 = last_key(c, i), hkv = hq / c->G;
-    const uint16_t* qi = c->q + qrow_off(c, b, hq, i);
+    const int D = c->D, Dv = c->Dv, j0 = first_key(c, i), j1 = last_key(c, i), hkv = hq / c->G;
+    const uint16_t* qi = c->q + qrow_off(c, b, hq, i, D);
     double m = -INFINITY;
     for (int j = j0; j <= j1; ++j) {
-        p[j] = c->scale * dot_bf16(qi, c->k + kvrow_off(c, b, hkv, j), D);
+        p[j] = c->scale * dot_bf16(qi, c->k + kvrow_off(c, b, hkv, j, D), D);
         if (p[j] > m) m = p[j];
     }
     double l = 0.0;
@@ -105,17 +108,17 @@ static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
     for (int j = j0; j <= j1; ++j) p[j] /= l;
     if (lse_out) *lse_out = m + log(l);
     if (o_out) {
-        for (int d = 0; d < D; ++d) o_out[d] = 0.0;
+        for (int d = 0; d < Dv; ++d) o_out[d] = 0.0;
         for (int j = j0; j <= j1; ++j) {
-            const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j);
-            for (int d = 0; d < D; ++d) o_out[d] += p[j] * widen(vj[d]);
+            const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j, Dv);
+            for (int d = 0; d < Dv; ++d) o_out[d] += p[j] * widen(vj[d]);
         }
     }
     if (c->dout && (delta_out || dq_out)) {
-        const uint16_t* doi = c->dout + qrow_off(c, b, hq, i);
+        const uint16_t* doi = c->dout + qrow_off(c, b, hq, i, Dv);
         double delta = 0.0;
         for (int j = j0; j <= j1; ++j) {
-            dp[j] = dot_bf16(doi, c->v + kvrow_off(c, b, hkv, j), D);
+            dp[j] = dot_bf16(doi, c->v + kvrow_off(c, b, hkv, j, Dv), Dv);
             delta += p[j] * dp[j];
         }
         if (delta_out) *delta_out = delta;
@@ -123,7 +126,7 @@ static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
             for (int d = 0; d < D; ++d) dq_out[d] = 0.0;
             for (int j = j0; j <= j1; ++j) {
                 const double ds = p[j] * (dp[j] - delta);
-                const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j);
+                const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j, D);
                 for (int d = 0; d < D; ++d) dq_out[d] += c->scale * ds * widen(kj[d]);
             }
         }
@@ -140,31 +143,30 @@ static void one_row(const ctx_t* c, int b, int hq, int i, double* p, double* dp,
  */
 static void one_key(const ctx_t* c, int b, int hkv, int j, const double* lse,
                     const double* delta, double* dk_out, double* dv_out) {
-    const int D = c->D, S = c->S, i0 = first_query(c, j), i1 = last_query(c, j);
-    const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j);
-    const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j);
-    for (int d = 0; d < D; ++d) { dk_out[d] = 0.0; dv_out[d] = 0.0; }
+    const int D = c->D, Dv = c->Dv, S = c->S, i0 = first_query(c, j), i1 = last_query(c, j);
+    const uint16_t* kj = c->k + kvrow_off(c, b, hkv, j, D);
+    const uint16_t* vj = c->v + kvrow_off(c, b, hkv, j, Dv);
+    for (int d = 0; d < D; ++d) dk_out[d] = 0.0;
+    for (int d = 0; d < Dv; ++d) dv_out[d] = 0.0;
     for (int g = 0; g < c->G; ++g) {
         const int hq = hkv * c->G + g;
         for (int i = i0; i <= i1; ++i) {
-            const uint16_t* qi = c->q + qrow_off(c, b, hq, i);
-            const uint16_t* doi = c->dout + qrow_off(c, b, hq, i);
+            const uint16_t* qi = c->q + qrow_off(c, b, hq, i, D);
+            const uint16_t* doi = c->dout + qrow_off(c, b, hq, i, Dv);
             const double pij = exp(c->scale * dot_bf16(qi, kj, D) - lse[(size_t)g * S + i]);
-            const double dpij = dot_bf16(doi, vj, D);
+            const double dpij = dot_bf16(doi, vj, Dv);
             const double ds = pij * (dpij - delta[(size_t)g * S + i]);
-            for (int d = 0; d < D; ++d) {
-                dv_out[d] += pij * widen(doi[d]);
-                dk_out[d] += c->scale * ds * widen(qi[d]);
-            }
+            for (int d = 0; d < Dv; ++d) dv_out[d] += pij * widen(doi[d]);
+            for (int d = 0; d < D; ++d) dk_out[d] += c->scale * ds * widen(qi[d]);
         }
     }
 }
 
 static void init_ctx(ctx_t* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                     const uint16_t* dout, int B, int Hq, int Hkv, int S, int D, int causal,
-                     int window, double scale) {
+                     const uint16_t* dout, int B, int Hq, int Hkv, int S, int D, int Dv,
+                     int causal, int window, double scale) {
     c->q = q; c->k = k; c->v = v; c->dout = dout;
-    c->B = B; c->Hq = Hq; c->Hkv = Hkv; c->S = S; c->D = D; c->G = Hq / Hkv;
+    c->B = B; c->Hq = Hq; c->Hkv = Hkv; c->S = S; c->D = D; c->Dv = Dv; c->G = Hq / Hkv;
     c->causal = causal ? 1 : 0;
     c->window = window;
     c->scale = scale;
@@ -172,14 +174,14 @@ static void init_ctx(ctx_t* c, const uint16_t* q, const uint16_t* k, const uint1
 
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
-/* Forward over every row: o [B][Hq][S][D], lse [B][Hq][S]. */
+/* Forward over every row: o [B][Hq][S][Dv], lse [B][Hq][S]. */
 int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* o,
-                    double* lse, int B, int Hq, int Hkv, int S, int D, int causal, int window,
-                    double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
+                    double* lse, int B, int Hq, int Hkv, int S, int D, int Dv, int causal,
+                    int window, double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D, Dv, causal, window);
     if (rc) return rc;
     ctx_t c;
-    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, window, scale);
+    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, Dv, causal, window, scale);
     const long long rows = (long long)B * Hq * S;
 #pragma omp parallel
     {
@@ -187,7 +189,7 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
 #pragma omp for schedule(dynamic, 16)
         for (long long r = 0; r < rows; ++r) {
             const int i = (int)(r % S), bh = (int)(r / S);
-            one_row(&c, bh / Hq, bh % Hq, i, p, NULL, o + (size_t)r * D, lse + r, NULL, NULL);
+            one_row(&c, bh / Hq, bh % Hq, i, p, NULL, o + (size_t)r * Dv, lse + r, NULL, NULL);
         }
         free(p);
     }
@@ -195,17 +197,17 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
 }
 
 /* Forward for selected rows only; rows[n] are flat indices (b*Hq + hq)*S + i.
- * o_rows [n][D], lse_rows [n]. */
+ * o_rows [n][Dv], lse_rows [n]. */
 int oracle_attn_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int64_t* rows, int64_t n, double* o_rows, double* lse_rows,
-                         int B, int Hq, int Hkv, int S, int D, int causal, int window,
+                         int B, int Hq, int Hkv, int S, int D, int Dv, int causal, int window,
                          double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
+    int rc = check_args(B, Hq, Hkv, S, D, Dv, causal, window);
     if (rc) return rc;
     for (int64_t t = 0; t < n; ++t)
         if (rows[t] < 0 || rows[t] >= (int64_t)B * Hq * S) return -3;
     ctx_t c;
-    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, causal, window, scale);
+    init_ctx(&c, q, k, v, NULL, B, Hq, Hkv, S, D, Dv, causal, window, scale);
 #pragma omp parallel
     {
         double* p = (double*)malloc(sizeof(double) * (size_t)S);
@@ -213,7 +215,7 @@ int oracle_attn_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
         for (int64_t t = 0; t < n; ++t) {
             const int64_t r = rows[t];
             const int i = (int)(r % S), bh = (int)(r / S);
-            one_row(&c, bh / Hq, bh % Hq, i, p, NULL, o_rows + (size_t)t * D, lse_rows + t,
+            one_row(&c, bh / Hq, bh % Hq, i, p, NULL, o_rows + (size_t)t * Dv, lse_rows + t,
                     NULL, NULL);
         }
         free(p);
@@ -238,14 +240,14 @@ static void group_row_stats(const ctx_t* c, int b, int hkv, double* lse, double*
     }
 }
 
-/* Full backward: dq [B][Hq][S][D]; dk, dv [B][Hkv][S][D] (summed over the group). */
+/* Full backward: dq [B][Hq][S][D]; dk [B][Hkv][S][D], dv [B][Hkv][S][Dv] (summed over the group). */
 int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dout, double* dq, double* dk, double* dv, int B, int Hq,
-                    int Hkv, int S, int D, int causal, int window, double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
+                    int Hkv, int S, int D, int Dv, int causal, int window, double scale) {
+    int rc = check_args(B, Hq, Hkv, S, D, Dv, causal, window);
     if (rc) return rc;
     ctx_t c;
-    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, window, scale);
+    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, Dv, causal, window, scale);
     const int G = c.G;
     const long long rows = (long long)B * Hq * S;
     double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
@@ -271,7 +273,7 @@ int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         const int b = bh / Hkv, hkv = bh % Hkv;
         /* the group's query heads are hkv*G .. hkv*G+G-1, contiguous in [Hq] */
         const size_t base = ((size_t)b * Hq + (size_t)hkv * G) * S;
-        one_key(&c, b, hkv, j, lse + base, delta + base, dk + (size_t)r * D, dv + (size_t)r * D);
+        one_key(&c, b, hkv, j, lse + base, delta + base, dk + (size_t)r * D, dv + (size_t)r * Dv);
     }
     free(lse);
     free(delta);
@@ -281,22 +283,22 @@ int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 /*
  * Backward for selected rows only. qrows[nq]: flat query rows (b*Hq+hq)*S+i,
  * giving dq_rows [nq][D]. kvrows[nkv]: flat key rows (b*Hkv+hkv)*S+j, giving
- * dk_rows, dv_rows [nkv][D]. Every query row of each group that a selected key
+ * dk_rows [nkv][D] and dv_rows [nkv][Dv]. Every query row of each group that a selected key
  * belongs to is visited once for its lse and delta.
  */
 int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dout, const int64_t* qrows, int64_t nq, double* dq_rows,
                          const int64_t* kvrows, int64_t nkv, double* dk_rows, double* dv_rows,
-                         int B, int Hq, int Hkv, int S, int D, int causal, int window,
+                         int B, int Hq, int Hkv, int S, int D, int Dv, int causal, int window,
                          double scale) {
-    int rc = check_args(B, Hq, Hkv, S, D, causal, window);
+    int rc = check_args(B, Hq, Hkv, S, D, Dv, causal, window);
     if (rc) return rc;
     for (int64_t t = 0; t < nq; ++t)
         if (qrows[t] < 0 || qrows[t] >= (int64_t)B * Hq * S) return -3;
     for (int64_t t = 0; t < nkv; ++t)
         if (kvrows[t] < 0 || kvrows[t] >= (int64_t)B * Hkv * S) return -3;
     ctx_t c;
-    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, causal, window, scale);
+    init_ctx(&c, q, k, v, dout, B, Hq, Hkv, S, D, Dv, causal, window, scale);
     const int G = c.G;
 #pragma omp parallel
     {
@@ -327,7 +329,7 @@ int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
         for (int64_t u = t; u < nkv; ++u) {
             if (kvrows[u] / S != grp) continue;
             one_key(&c, b, hkv, (int)(kvrows[u] % S), lse, delta, dk_rows + (size_t)u * D,
-                    dv_rows + (size_t)u * D);
+                    dv_rows + (size_t)u * Dv);
         }
     }
     free(lse);

@@ -4,7 +4,8 @@ Each check takes an oracle object (``oracle.Oracle``) and raises AssertionError
 when the oracle disagrees with the fact. The facts come from section 2.1 of
 Rao et al., "Scheduling Data to Compute: Hierarchical Data Pipelining for LLM
 Training on AMD GPUs" (Eq. (1): O = softmax(Q K^T / sqrt(d)) V), the sliding
-window of its Table 7 (query i sees the keys i-W+1 .. i), and from
+window of its Table 7 (query i sees the keys i-W+1 .. i), the separate value
+width d_v that Eq. (1) allows, and from
 mathematics: an independent brute force on tiny inputs, closed forms,
 invariants, torch's float64 CPU attention and autograd as a library routine,
 and central finite differences for the gradient.
@@ -35,8 +36,9 @@ def brute_force_fwd(q, k, v, causal, scale, window=0):
     no max subtraction, no numpy linear algebra."""
     qf, kf, vf = _f64(q), _f64(k), _f64(v)
     B, Hq, S, D = q.shape
+    Dv = v.shape[3]
     G = Hq // k.shape[1]
-    o = np.zeros((B, Hq, S, D))
+    o = np.zeros((B, Hq, S, Dv))
     lse = np.zeros((B, Hq, S))
     for b in range(B):
         for h in range(Hq):
@@ -47,7 +49,7 @@ def brute_force_fwd(q, k, v, causal, scale, window=0):
                      for j in js]
                 z = math.fsum(e)
                 lse[b, h, i] = math.log(z)
-                for d in range(D):
+                for d in range(Dv):
                     o[b, h, i, d] = math.fsum(e[t] / z * vf[b, g, j, d] for t, j in enumerate(js))
     return o, lse
 
@@ -376,9 +378,99 @@ def pin_window_gradients(orc):
     _close(dv_r, dv.reshape(-1, D)[kvr], 1e-15, "windowed dv rows")
 
 
+# ------------------------------------------------------ value head dim d_v != d
+
+def _fd_check(orc, B, Hq, Hkv, S, D, Dv, causal, scale, seed, window=0):
+    """Central differences of L = sum(O * dO) (pure-Python forward) against the
+    oracle's analytic gradients."""
+    h = 1e-6
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, seed, with_dout=True, Dv=Dv)
+    dq, dk, dv = orc.bwd(q, k, v, do, causal, scale, window)
+    base = [_f64(q), _f64(k), _f64(v)]
+    dof = _f64(do)
+    for which, grad in enumerate((dq, dk, dv)):
+        assert grad.shape == base[which].shape, "gradient shape %s" % (grad.shape,)
+        for idx in np.ndindex(*base[which].shape):
+            plus = [a.copy() for a in base]
+            minus = [a.copy() for a in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd = (_loss_py(*plus, dof, causal, scale, Hq // Hkv, window)
+                  - _loss_py(*minus, dof, causal, scale, Hq // Hkv, window)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), \
+                "d_v != d finite difference %s%s: fd %.9f analytic %.9f" % ("qkv"[which], idx, fd, grad[idx])
+
+
+def pin_value_dim(orc):
+    """Eq. (1) lets the value width d_v differ from the query/key width d. With
+    Dv != D: the forward equals the pure-Python brute force and torch's float64
+    attention (which takes V of its own width), the gradients equal central
+    differences and torch autograd, Q = 0 gives prefix means of V, and the
+    sampled-row entry points agree with the full ones. Every Dv > D case runs
+    before any Dv < D case."""
+    # Dv > D
+    for (B, Hq, Hkv, S, D, Dv, causal, seed) in [(1, 2, 1, 6, 3, 5, True, 41), (2, 4, 2, 5, 4, 7, False, 42)]:
+        q, k, v = qkv(B, Hq, Hkv, S, D, seed, Dv=Dv)
+        scale = 1.0 / math.sqrt(D)
+        o, lse = orc.fwd(q, k, v, causal, scale)
+        ob, lb = brute_force_fwd(q, k, v, causal, scale)
+        _close(o, ob, 1e-12, "d_v > d: O vs brute force %s" % ((B, Hq, Hkv, S, D, Dv, causal),))
+        _close(lse, lb, 1e-12, "d_v > d: lse vs brute force")
+    q, k, v, do = qkv(1, 4, 2, 21, 8, 0, with_dout=True, Dv=16)
+    dq, dk, dv = orc.bwd(q, k, v, do, True, 0.3)
+    o, _ = orc.fwd(q, k, v, True, 0.3)
+    ot, (tq, tk, tv) = _torch_ref(q, k, v, True, 0.3, do)
+    _close(o, ot, 1e-12, "d_v > d: O vs torch sdpa")
+    _close(dq, tq, 1e-12, "d_v > d: dQ vs torch autograd")
+    _close(dk, tk, 1e-12, "d_v > d: dK vs torch autograd")
+    _close(dv, tv, 1e-12, "d_v > d: dV vs torch autograd")
+    _fd_check(orc, 1, 2, 1, 4, 2, 3, True, 0.7, 43)
+    q, k, v = qkv(1, 2, 1, 9, 4, 44, Dv=6)
+    q = np.zeros_like(q)
+    o, _ = orc.fwd(q, k, v, True, 0.5)
+    vf = _f64(v)
+    prefix = np.cumsum(vf, axis=2) / np.arange(1, 10.0)[None, None, :, None]
+    _close(o, np.broadcast_to(prefix, o.shape), 1e-14, "d_v > d: Q=0 causal O")
+    B, Hq, Hkv, S, D, Dv = 2, 4, 2, 23, 8, 12
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 45, with_dout=True, Dv=Dv)
+    rows = np.array([0, 4, 5, 22, 23, 99, 183])
+    kvr = np.array([0, 3, 22, 23, 40, 91])
+    for causal, window in ((False, 0), (True, 0), (True, 4)):
+        o, lse = orc.fwd(q, k, v, causal, 0.35, window)
+        o_r, l_r = orc.fwd_rows(q, k, v, rows, causal, 0.35, window)
+        _close(o_r, o.reshape(-1, Dv)[rows], 0.0, "d_v > d: fwd rows")
+        _close(l_r, lse.reshape(-1)[rows], 0.0, "d_v > d: fwd rows lse")
+        dq, dk, dv = orc.bwd(q, k, v, do, causal, 0.35, window)
+        dq_r, dk_r, dv_r = orc.bwd_rows(q, k, v, do, rows, kvr, causal, 0.35, window)
+        _close(dq_r, dq.reshape(-1, D)[rows], 1e-15, "d_v > d: dq rows")
+        _close(dk_r, dk.reshape(-1, D)[kvr], 1e-15, "d_v > d: dk rows")
+        _close(dv_r, dv.reshape(-1, Dv)[kvr], 1e-15, "d_v > d: dv rows")
+        # rows of P sum to 1 and rows of dS to 0
+        _close(dv.sum(axis=2), _f64(do).reshape(B, Hkv, 2, S, Dv).sum(axis=(2, 3)), 1e-12, "d_v > d: sum dV")
+        _close(dk.sum(axis=2), np.zeros((B, Hkv, D)), 1e-12, "d_v > d: sum dK")
+    # Dv < D
+    for (B, Hq, Hkv, S, D, Dv, causal, seed) in [(1, 2, 2, 5, 6, 3, True, 46), (1, 3, 1, 4, 5, 2, False, 47)]:
+        q, k, v = qkv(B, Hq, Hkv, S, D, seed, Dv=Dv)
+        o, lse = orc.fwd(q, k, v, causal, 0.45)
+        ob, lb = brute_force_fwd(q, k, v, causal, 0.45)
+        _close(o, ob, 1e-12, "d_v < d: O vs brute force")
+        _close(lse, lb, 1e-12, "d_v < d: lse vs brute force")
+    for causal, window in ((False, 0), (True, 0), (True, 6)):
+        q, k, v, do = qkv(2, 4, 2, 19, 16, 48, with_dout=True, Dv=8)
+        o, _ = orc.fwd(q, k, v, causal, 0.25, window)
+        dq, dk, dv = orc.bwd(q, k, v, do, causal, 0.25, window)
+        ot, (tq, tk, tv) = _torch_ref(q, k, v, causal, 0.25, do, window)
+        _close(o, ot, 1e-12, "d_v < d: O vs torch sdpa")
+        _close(dq, tq, 1e-12, "d_v < d: dQ vs torch autograd")
+        _close(dk, tk, 1e-12, "d_v < d: dK vs torch autograd")
+        _close(dv, tv, 1e-12, "d_v < d: dV vs torch autograd")
+    _fd_check(orc, 1, 2, 1, 5, 3, 2, True, 0.6, 49, window=2)
+
+
 FORWARD_PINS = [pin_brute_force, pin_torch_sdpa, pin_single_key, pin_zero_query,
                 pin_causal_first_row, pin_permutation, pin_gqa_is_repeated_mha, pin_sharp_softmax,
                 pin_rows_match_full]
 BACKWARD_PINS = [pin_finite_differences, pin_torch_autograd, pin_backward_invariants, pin_equal_keys]
 WINDOW_PINS = [pin_window_brute_force, pin_window_torch, pin_window_closed_forms, pin_window_gradients]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + WINDOW_PINS
+VALUE_DIM_PINS = [pin_value_dim]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + WINDOW_PINS + VALUE_DIM_PINS

@@ -34,6 +34,15 @@ MUTATIONS = [
     ("dk_dv_first_head_only", "for (int g = 0; g < c->G; ++g) {", "for (int g = 0; g < 1; ++g) {"),
     ("dv_uses_q_not_do", "dv_out[d] += pij * widen(doi[d]);", "dv_out[d] += pij * widen(qi[d]);"),
     ("delta_missing_p", "delta += p[j] * dp[j];", "delta += dp[j];"),
+    # value width d_v != d: each of these stays in bounds while Dv > D, and the
+    # d_v pin runs all its Dv > D cases before any Dv < D one
+    ("o_uses_d_columns", "for (int d = 0; d < Dv; ++d) o_out[d] += p[j] * widen(vj[d]);",
+     "for (int d = 0; d < D; ++d) o_out[d] += p[j] * widen(vj[d]);"),
+    ("v_row_stride_d", "dp[j] = dot_bf16(doi, c->v + kvrow_off(c, b, hkv, j, Dv), Dv);",
+     "dp[j] = dot_bf16(doi, c->v + kvrow_off(c, b, hkv, j, D), Dv);"),
+    ("dv_uses_d_columns", "for (int d = 0; d < Dv; ++d) dv_out[d] += pij * widen(doi[d]);",
+     "for (int d = 0; d < D; ++d) dv_out[d] += pij * widen(doi[d]);"),
+    ("dp_dot_over_d", "const double dpij = dot_bf16(doi, vj, Dv);", "const double dpij = dot_bf16(doi, vj, D);"),
 ]
 
 
