@@ -3,15 +3,17 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 the forward kernel (O, lse) and the backward kernels (delta, dK/dV, dQ) on the
 Llama-3.1-8B-shaped causal GQA workload B=1, Hq=32, Hkv=8, S=4096, D=128,
-inputs resident in HBM. FLOP convention: forward 4*B*Hq*D times the visible
-(query, key) pairs per head (S^2, S^2/2 when causal, S*W - W(W-1)/2 for a
-causal window of W keys), backward 2.5x the forward; softmax and exp work is
-not counted.
+inputs resident in HBM. FLOP convention, per visible (query, key) pair of a
+head (S^2, S^2/2 when causal, S*W - W(W-1)/2 for a causal window of W keys):
+forward 2*D (Q K^T) + 2*Dv (P V), backward 2*D (recomputed scores) + 2*Dv
+(dO V^T) + 2*Dv (P^T dO) + 2*D (dS K) + 2*D (dS^T Q), which is 2.5x the forward
+when Dv = D; softmax and exp work is not counted.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--fwd-only]
 
 --workload picks another entry of inputs.CONFIGS (the default is the headline
-workload above); a config with a "window" runs attn_fwd_window/attn_bwd_window.
+workload above); a config with a "window" runs attn_fwd_window/attn_bwd_window,
+one with a value head dimension "Dv" other than D runs attn_fwd_vdim/attn_bwd_vdim.
 """
 import argparse
 import json
@@ -38,8 +40,14 @@ def visible_pairs(S, causal, window=0):
     return S * S / 2.0 if causal else float(S) * S
 
 
-def fwd_flops(B, Hq, S, D, causal, window=0):
-    return 4.0 * B * Hq * D * visible_pairs(S, causal, window)
+def pair_flops(D, Dv):
+    """FLOP per visible (query, key) pair: each launch's products and the pass totals."""
+    return {"fwd_kernel": 2.0 * (D + Dv),          # S = Q K^T, O = P V
+            "dq_kernel": 4.0 * D + 2.0 * Dv,       # S, dP = dO V^T, dQ = dS K
+            "dkv_kernel": 4.0 * (D + Dv),          # S, dP, dV = P^T dO, dK = dS^T Q
+            "bwd_kernels": 8.0 * D + 6.0 * Dv,     # both backward launches
+            "fwd": 2.0 * (D + Dv),
+            "bwd": 6.0 * D + 4.0 * Dv}
 
 
 def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
@@ -49,6 +57,8 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
     import oracle
     B, Hq, Hkv, S, D, causal = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"], cfg["causal"]
     W = cfg.get("window", 0)
+    Dv = cfg.get("Dv", D)
+    pf = pair_flops(D, Dv)
     scale = 1.0 / math.sqrt(D)
     rng = np.random.default_rng(123)
 
@@ -57,7 +67,7 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
         n = (i + 1) if causal else np.full_like(i, S)
         if W:
             n = np.minimum(n, W)
-        return float(np.sum(4.0 * n * D))
+        return float(np.sum(pf["fwd"] * n))
 
     # calibrate on a small sample, then size the timed sample to ~target_s
     cal = rng.integers(0, B * Hq * S, size=64)
@@ -84,7 +94,7 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
         seen_by = (S - keys) if causal else np.full_like(keys, S)         # query rows that see each key
         if W:
             seen_by = np.minimum(seen_by, W)
-        key_flops = float(np.sum(G * 8.0 * D * seen_by))
+        key_flops = float(np.sum(G * pf["dkv_kernel"] * seen_by))
         # the group's statistics are counted as work at the forward rate; their time is in t_b
         flops += stat_flops + key_flops
         secs += t_b
@@ -183,21 +193,31 @@ def main():
     cfg = CONFIGS[name]
     B, Hq, Hkv, S, D, causal = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"], cfg["causal"]
     W = cfg.get("window", 0)
+    Dv = cfg.get("Dv", D)
     scale = 1.0 / math.sqrt(D)
-    q, k, v, dout = qkv(B, Hq, Hkv, S, D, seed=0, with_dout=True)
+    q, k, v, dout = qkv(B, Hq, Hkv, S, D, seed=0, with_dout=True, Dv=Dv)
     dq_, dk_, dv_, ddo = to_dev(q), to_dev(k), to_dev(v), to_dev(dout)
-    o = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((B, Hq, S, Dv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
     gq = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
     gk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
-    gv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
+    gv = torch.empty((B, Hkv, S, Dv), dtype=torch.float32, device="cuda")
     ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal),), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     with_bwd = not args.fwd_only
 
     bargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws, stream)
     wargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, W, scale, ws, stream)
-    if W:
+    if Dv != D:
+        def run_fwd():
+            fa.attn_fwd_vdim(dq_, dk_, dv_, o, lse, causal, W, scale, stream)
+
+        def run_bwd():
+            fa.attn_bwd_vdim(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, W, scale, ws, stream)
+        calls = {"fwd_kernel": run_fwd}
+        if with_bwd:
+            calls["bwd_kernels"] = run_bwd
+    elif W:
         def run_fwd():
             fa.attn_fwd_window(dq_, dk_, dv_, o, lse, W, scale, stream)
 
@@ -249,19 +269,17 @@ def main():
     n_rep = max(args.steps, 10)
     kernel_ms = {name: time_calls(fn, n_rep) for name, fn in calls.items()}
 
-    # FLOP convention: one "product" is 2*B*Hq*S^2*D (halved when causal). The forward
-    # kernel computes 2 (S = Q K^T, O = P V); the dQ kernel 3 (S, dP = dO V^T, dQ = dS K);
-    # the dK/dV kernel 4 (S, dP, dV = P^T dO, dK = dS^T Q). The step's algorithmic work
-    # is forward 2 + backward 5 products (backward = 2.5 x forward).
-    product = fwd_flops(B, Hq, S, D, causal, W) / 2
-    kernel_products = {"fwd_kernel": 2, "dq_kernel": 3, "dkv_kernel": 4, "bwd_kernels": 7}
-    f_fwd = 2 * product
-    f_bwd = 5 * product
+    # FLOP convention (pair_flops): each launch's products over the visible pairs; the
+    # step's algorithmic work is the forward plus the backward's five products.
+    pairs = B * Hq * visible_pairs(S, causal, W)
+    pf = pair_flops(D, Dv)
+    f_fwd = pf["fwd"] * pairs
+    f_bwd = pf["bwd"] * pairs
     step_flops = f_fwd + (f_bwd if with_bwd else 0.0)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     dominant = max(kernel_ms, key=kernel_ms.get)
-    dom_flops = kernel_products[dominant] * product
+    dom_flops = pf[dominant] * pairs
     achieved = dom_flops / (kernel_ms[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -270,7 +288,7 @@ def main():
 
     kernels = {}
     for kname, ms in kernel_ms.items():
-        fl = kernel_products[kname] * product
+        fl = pf[kname] * pairs
         kernels[kname] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                          "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "hbm_bytes": hbm_traffic(kname) if headline else None}
@@ -281,7 +299,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name + ("" if with_bwd else "_fwd_only"), "B": B, "Hq": Hq, "Hkv": Hkv,
-                   "S": S, "D": D, "causal": bool(causal), "window": W or None,
+                   "S": S, "D": D, "Dv": Dv, "causal": bool(causal), "window": W or None,
                    "pass": "fwd+bwd" if with_bwd else "fwd", "seed": 0},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd": {"tflops": kernels["fwd_kernel"]["tflops"], "ms": kernels["fwd_kernel"]["ms"],
@@ -290,7 +308,7 @@ def main():
         "roofline": roofline,
     }
     if with_bwd:
-        bwd_ms = kernel_ms["bwd_kernels"] if W else kernel_ms["dq_kernel"] + kernel_ms["dkv_kernel"]
+        bwd_ms = kernel_ms["bwd_kernels"] if "bwd_kernels" in kernel_ms else kernel_ms["dq_kernel"] + kernel_ms["dkv_kernel"]
         result["bwd"] = {"tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2), "ms": round(bwd_ms, 4),
                          "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_cpu_baseline:

@@ -6,9 +6,9 @@ points, and every step of the computation runs in the library's HIP kernels.
 There is no fallback: if ``libattn.so`` is missing, every call raises.
 
 Entry points with the C names (``attn_fwd``, ``attn_bwd``, ``attn_bwd_dq``,
-``attn_bwd_dkdv``, ``attn_fwd_window``, ``attn_bwd_window``, ``attn_bwd_workspace_bytes``,
-``attn_status_str``) take caller-allocated tensors; ``fwd`` and ``bwd`` allocate their
-outputs with torch.
+``attn_bwd_dkdv``, ``attn_fwd_window``, ``attn_bwd_window``, ``attn_fwd_vdim``,
+``attn_bwd_vdim``, ``attn_bwd_workspace_bytes``, ``attn_status_str``) take
+caller-allocated tensors; ``fwd`` and ``bwd`` allocate their outputs with torch.
 """
 import ctypes
 import math
@@ -32,7 +32,8 @@ ATTN_ERR_DEVICE = 9
 ATTN_ERR_WINDOW = 10
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_window",
-                    "attn_bwd_window", "attn_bwd_workspace_bytes", "attn_status_str")
+                    "attn_bwd_window", "attn_fwd_vdim", "attn_bwd_vdim", "attn_bwd_workspace_bytes",
+                    "attn_status_str")
 
 
 class AttnError(RuntimeError):
@@ -64,6 +65,10 @@ def load_library(path=None):
     lib.attn_fwd_window.restype = I
     lib.attn_bwd_window.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, F, V, Z, V]
     lib.attn_bwd_window.restype = I
+    lib.attn_fwd_vdim.argtypes = [V, V, V, V, V, I, I, I, I, I, I, I, I, F, V]
+    lib.attn_fwd_vdim.restype = I
+    lib.attn_bwd_vdim.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, I, F, V, Z, V]
+    lib.attn_bwd_vdim.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_status_str.argtypes = [I]
@@ -104,55 +109,66 @@ def _check(t, name, dtype, shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
-def _dims(q, k):
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q and k must be [B][H][S][D]")
+def _dims(q, k, v=None):
+    """(B, Hq, Hkv, S, D, Dv): D from q, Dv (the value head dimension) from v."""
+    if q.dim() != 4 or k.dim() != 4 or (v is not None and v.dim() != 4):
+        raise ValueError("q, k and v must be [B][H][S][D]")
     B, Hq, S, D = q.shape
-    return B, Hq, k.shape[1], S, D
+    return B, Hq, k.shape[1], S, D, (D if v is None else v.shape[3])
 
 
-def _fwd_call(name, q, k, v, o, lse, flag, scale, stream):
+def _fwd_call(name, q, k, v, o, lse, flags, scale, stream, vdim=False):
+    """flags: the int arguments between the sizes and scale (causal or window; for
+    the vdim entry point, causal and window after Dv)."""
     import torch
-    B, Hq, Hkv, S, D = _dims(q, k)
+    B, Hq, Hkv, S, D, Dv = _dims(q, k, v if vdim else None)
     _check(q, "q", torch.bfloat16, (B, Hq, S, D))
     _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
-    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
-    _check(o, "o", torch.bfloat16, (B, Hq, S, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, S, Dv))
+    _check(o, "o", torch.bfloat16, (B, Hq, S, Dv))
     _check(lse, "lse", torch.float32, (B, Hq, S))
-    rc = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S,
-                                       D, int(flag), float(scale), _stream(stream))
+    dims = (B, Hq, Hkv, S, D, Dv) if vdim else (B, Hq, Hkv, S, D)
+    rc = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), *dims,
+                                       *[int(f) for f in flags], float(scale), _stream(stream))
     if rc:
         raise AttnError(rc, name)
 
 
 def attn_fwd(q, k, v, o, lse, causal, scale, stream=None):
     """C attn_fwd on torch tensors: q [B,Hq,S,D], k/v [B,Hkv,S,D] bf16; writes o (bf16) and lse (fp32)."""
-    _fwd_call("attn_fwd", q, k, v, o, lse, bool(causal), scale, stream)
+    _fwd_call("attn_fwd", q, k, v, o, lse, (bool(causal),), scale, stream)
 
 
 def attn_fwd_window(q, k, v, o, lse, window, scale, stream=None):
     """C attn_fwd_window: causal attention where query i sees keys i-window+1 .. i."""
-    _fwd_call("attn_fwd_window", q, k, v, o, lse, window, scale, stream)
+    _fwd_call("attn_fwd_window", q, k, v, o, lse, (window,), scale, stream)
+
+
+def attn_fwd_vdim(q, k, v, o, lse, causal, window, scale, stream=None):
+    """C attn_fwd_vdim: v [B,Hkv,S,Dv] and o [B,Hq,S,Dv] with their own head dimension
+    Dv; window = 0 (none) or >= 1 with causal."""
+    _fwd_call("attn_fwd_vdim", q, k, v, o, lse, (bool(causal), window), scale, stream, vdim=True)
 
 
 def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal):
     return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, int(bool(causal))))
 
 
-def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, flag, scale, workspace, stream):
+def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, flags, scale, workspace, stream, vdim=False):
     import torch
-    B, Hq, Hkv, S, D = _dims(q, k)
+    B, Hq, Hkv, S, D, Dv = _dims(q, k, v if vdim else None)
     for t, n, dt, sh in ((q, "q", torch.bfloat16, (B, Hq, S, D)), (k, "k", torch.bfloat16, (B, Hkv, S, D)),
-                         (v, "v", torch.bfloat16, (B, Hkv, S, D)), (o, "o", torch.bfloat16, (B, Hq, S, D)),
-                         (lse, "lse", torch.float32, (B, Hq, S)), (dout, "dout", torch.bfloat16, (B, Hq, S, D)),
+                         (v, "v", torch.bfloat16, (B, Hkv, S, Dv)), (o, "o", torch.bfloat16, (B, Hq, S, Dv)),
+                         (lse, "lse", torch.float32, (B, Hq, S)), (dout, "dout", torch.bfloat16, (B, Hq, S, Dv)),
                          (dq, "dq", torch.float32, (B, Hq, S, D)), (dk, "dk", torch.float32, (B, Hkv, S, D)),
-                         (dv, "dv", torch.float32, (B, Hkv, S, D))):
+                         (dv, "dv", torch.float32, (B, Hkv, S, Dv))):
         _check(t, n, dt, sh)
     if workspace.device.type != "cuda":
         raise TypeError("workspace must be a GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
+    dims = (B, Hq, Hkv, S, D, Dv) if vdim else (B, Hq, Hkv, S, D)
     rc = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                                       _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(flag), float(scale),
+                                       _ptr(dk), _ptr(dv), *dims, *[int(f) for f in flags], float(scale),
                                        _ptr(workspace), nbytes, _stream(stream))
     if rc:
         raise AttnError(rc, name)
@@ -160,34 +176,44 @@ def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, flag, scale, workspace, s
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
     """C attn_bwd on torch tensors; dq/dk/dv are fp32; workspace is a uint8 GPU tensor."""
-    _bwd_call("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, bool(causal), scale, workspace, stream)
+    _bwd_call("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, (bool(causal),), scale, workspace, stream)
 
 
 def attn_bwd_dq(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
     """First backward stage: delta into the workspace and dq."""
-    _bwd_call("attn_bwd_dq", q, k, v, o, lse, dout, dq, dk, dv, bool(causal), scale, workspace, stream)
+    _bwd_call("attn_bwd_dq", q, k, v, o, lse, dout, dq, dk, dv, (bool(causal),), scale, workspace, stream)
 
 
 def attn_bwd_dkdv(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
     """Second backward stage: dk and dv from the workspace's delta."""
-    _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dout, dq, dk, dv, bool(causal), scale, workspace, stream)
+    _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dout, dq, dk, dv, (bool(causal),), scale, workspace, stream)
 
 
 def attn_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, window, scale, workspace, stream=None):
     """C attn_bwd_window: gradient of attn_fwd_window with the same window."""
-    _bwd_call("attn_bwd_window", q, k, v, o, lse, dout, dq, dk, dv, window, scale, workspace, stream)
+    _bwd_call("attn_bwd_window", q, k, v, o, lse, dout, dq, dk, dv, (window,), scale, workspace, stream)
+
+
+def attn_bwd_vdim(q, k, v, o, lse, dout, dq, dk, dv, causal, window, scale, workspace, stream=None):
+    """C attn_bwd_vdim: gradient of attn_fwd_vdim with the same arguments; v, o, dout
+    and dv have the value head dimension Dv."""
+    _bwd_call("attn_bwd_vdim", q, k, v, o, lse, dout, dq, dk, dv, (bool(causal), window), scale, workspace,
+              stream, vdim=True)
 
 
 def fwd(q, k, v, causal=False, scale=None, window=0):
     """Allocate o and lse and run attn_fwd (attn_fwd_window when window > 0, which
-    implies causal). scale defaults to 1/sqrt(D)."""
+    implies causal; attn_fwd_vdim when v's head dimension differs from q's).
+    scale defaults to 1/sqrt(D)."""
     import torch
-    B, Hq, Hkv, S, D = _dims(q, k)
+    B, Hq, Hkv, S, D, Dv = _dims(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    o = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=q.device)
+    o = torch.empty((B, Hq, S, Dv), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    if window:
+    if Dv != D:
+        attn_fwd_vdim(q, k, v, o, lse, causal or bool(window), window, scale)
+    elif window:
         attn_fwd_window(q, k, v, o, lse, window, scale)
     else:
         attn_fwd(q, k, v, o, lse, causal, scale)
@@ -196,17 +222,19 @@ def fwd(q, k, v, causal=False, scale=None, window=0):
 
 def bwd(q, k, v, o, lse, dout, causal=False, scale=None, window=0):
     """Allocate dq/dk/dv (fp32) and the workspace and run attn_bwd (attn_bwd_window
-    when window > 0)."""
+    when window > 0; attn_bwd_vdim when v's head dimension differs from q's)."""
     import torch
-    B, Hq, Hkv, S, D = _dims(q, k)
+    B, Hq, Hkv, S, D, Dv = _dims(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dq = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=q.device)
-    dv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, S, Dv), dtype=torch.float32, device=q.device)
     ws = torch.empty((attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal or bool(window)),),
                      dtype=torch.uint8, device=q.device)
-    if window:
+    if Dv != D:
+        attn_bwd_vdim(q, k, v, o, lse, dout, dq, dk, dv, causal or bool(window), window, scale, ws)
+    elif window:
         attn_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, window, scale, ws)
     else:
         attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, ws)

@@ -53,14 +53,15 @@ int setup_current_device() {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
-int check_sizes(int B, int Hq, int Hkv, int S, int D) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1) return ATTN_ERR_SHAPE;
-    const double elems = (double)B * Hq * S * D;
+// D: query/key head dimension; Dv: value head dimension.
+int check_sizes(int B, int Hq, int Hkv, int S, int D, int Dv) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || Dv < 1) return ATTN_ERR_SHAPE;
+    const double elems = (double)B * Hq * S * (D > Dv ? D : Dv);
     if (elems >= 1099511627776.0) return ATTN_ERR_SHAPE;  // 2^40
     // grid size: B * Hq * ceil(S / 128) work groups must fit a 32-bit grid
     if ((double)B * Hq * ((S + 127) / 128) >= 2147483647.0) return ATTN_ERR_SHAPE;
     if (Hq % Hkv != 0) return ATTN_ERR_GQA;
-    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
+    if ((D != 64 && D != 128) || (Dv != 64 && Dv != 128)) return ATTN_ERR_UNSUPPORTED_D;
     return ATTN_OK;
 }
 
@@ -76,24 +77,24 @@ const char* attn_status_str(int status) {
     switch (status) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL: return "a required pointer is NULL";
-        case ATTN_ERR_SHAPE: return "B, Hq, Hkv, S and D must be >= 1 and B*Hq*S*D < 2^40";
+        case ATTN_ERR_SHAPE: return "B, Hq, Hkv, S, D and Dv must be >= 1 and B*Hq*S*max(D, Dv) < 2^40";
         case ATTN_ERR_GQA: return "Hq must be a multiple of Hkv";
-        case ATTN_ERR_UNSUPPORTED_D: return "head dimension D must be 64 or 128";
+        case ATTN_ERR_UNSUPPORTED_D: return "head dimensions D and Dv must be 64 or 128";
         case ATTN_ERR_ALIGN: return "tensor and workspace pointers must be 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_HIP: return "HIP runtime error";
         case ATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
-        case ATTN_ERR_WINDOW: return "window must be >= 1";
+        case ATTN_ERR_WINDOW: return "window must be >= 1 (>= 0 and causal for the vdim entry points)";
         default: return "unknown attn status";
     }
 }
 
 static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                    int Hq, int Hkv, int S, int D, int causal, int window, float scale,
+                    int Hq, int Hkv, int S, int D, int Dv, int causal, int window, float scale,
                     void* stream) {
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-    int rc = check_sizes(B, Hq, Hkv, S, D);
+    int rc = check_sizes(B, Hq, Hkv, S, D, Dv);
     if (rc) return rc;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
@@ -118,34 +119,42 @@ static int fwd_impl(const void* q, const void* k, const void* v, void* o, float*
     // rounding; there the maximum is tracked exactly.
     a.max_slack = fabsf(scale) * sqrtf((float)D) > 2.0f ? 0.0f : 8.0f;
     a.precise_tiles = 0;  // set by the launcher, which knows the tile size
-    if (attn::launch_fwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+    if (attn::launch_fwd(a, D, Dv, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int S, int D, int causal, float scale, void* stream) {
-    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, causal, 0, scale, stream);
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, D, causal, 0, scale, stream);
 }
 
 int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                     int Hq, int Hkv, int S, int D, int window, float scale, void* stream) {
     if (window < 1) return ATTN_ERR_WINDOW;
     // a window of S or more keys is the whole causal triangle
-    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, 1, window >= S ? 0 : window, scale, stream);
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, D, 1, window >= S ? 0 : window, scale, stream);
+}
+
+int attn_fwd_vdim(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int Hq, int Hkv, int S, int D, int Dv, int causal, int window, float scale,
+                  void* stream) {
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_WINDOW;
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, Dv, causal, window >= S ? 0 : window,
+                    scale, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal) {
     (void)causal;
-    if (check_sizes(B, Hq, Hkv, S, D) != ATTN_OK) return 0;
+    if (check_sizes(B, Hq, Hkv, S, D, D) != ATTN_OK) return 0;
     return delta_bytes(B, Hq, S);
 }
 
 static int bwd_stages(int stages, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv, int B,
-                      int Hq, int Hkv, int S, int D, int causal, int window, float scale,
+                      int Hq, int Hkv, int S, int D, int Dv, int causal, int window, float scale,
                       void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
-    int rc = check_sizes(B, Hq, Hkv, S, D);
+    int rc = check_sizes(B, Hq, Hkv, S, D, Dv);
     if (rc) return rc;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal))
@@ -177,7 +186,7 @@ static int bwd_stages(int stages, const void* q, const void* k, const void* v, c
     // rounding of P, dS and the stored O would dominate, or a window of at most
     // 128 keys, where every row sees no more keys than the first causal rows do.
     a.precise_all = (fabsf(scale) * sqrtf((float)D) > 2.0f || (window > 0 && window <= 128)) ? 1 : 0;
-    if (attn::launch_bwd(a, D, stages, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+    if (attn::launch_bwd(a, D, Dv, stages, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
 }
 
@@ -185,7 +194,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
              int D, int causal, float scale, void* workspace, size_t workspace_bytes,
              void* stream) {
-    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, 0, scale,
+    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, D, causal, 0, scale,
                       workspace, workspace_bytes, stream);
 }
 
@@ -193,7 +202,7 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, cons
                 const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
                 int D, int causal, float scale, void* workspace, size_t workspace_bytes,
                 void* stream) {
-    return bwd_stages(1, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, 0, scale,
+    return bwd_stages(1, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, D, causal, 0, scale,
                       workspace, workspace_bytes, stream);
 }
 
@@ -201,7 +210,7 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, co
                   const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
                   int D, int causal, float scale, void* workspace, size_t workspace_bytes,
                   void* stream) {
-    return bwd_stages(2, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, causal, 0, scale,
+    return bwd_stages(2, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, D, causal, 0, scale,
                       workspace, workspace_bytes, stream);
 }
 
@@ -210,7 +219,16 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
                     int S, int D, int window, float scale, void* workspace,
                     size_t workspace_bytes, void* stream) {
     if (window < 1) return ATTN_ERR_WINDOW;
-    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, 1,
+    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, D, 1,
+                      window >= S ? 0 : window, scale, workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_vdim(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv,
+                  int S, int D, int Dv, int causal, int window, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_WINDOW;
+    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, Dv, causal,
                       window >= S ? 0 : window, scale, workspace, workspace_bytes, stream);
 }
 

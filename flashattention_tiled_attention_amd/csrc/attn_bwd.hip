@@ -33,6 +33,10 @@
 // for a sliding window of at most 128 keys, where no row sees more keys than the
 // first causal rows do.
 //
+// Queries and keys have D columns and values DV (the d and d_v of Eq. (1)); each
+// is 64 or 128, in any combination: Q, K, dQ and dK are D wide, V, O, dO and dV
+// are DV wide.
+//
 // Sliding window (query i sees keys i-W+1 .. i, the window of the page's
 // compressed sparse attention, Table 7): both kernels skip the tiles outside
 // the band and mask the tiles that cross either of its edges.
@@ -52,16 +56,16 @@ constexpr int kDqBQ = 128;
 constexpr int kDqBK = 64;
 constexpr int kDqThreads = 256;
 
-template <int D>
+template <int D, int DV>
 struct DqTile {
-    // K and V tiles: unpadded [64][D] bf16 in the chunk order of swz<D> (the
-    // direct copies need 1 KB contiguous runs; swz keeps the K row reads, the K
-    // transpose reads and the V row reads free of bank conflicts).
-    static constexpr int TILE = kDqBK * D;
-    static constexpr int LDS_BYTES = 4 * TILE * 2;                // 2 K slots + 2 V slots
-    static constexpr int CH = D / 8;
-    static constexpr int ROWS_PER_COPY = 64 / CH;
-    static constexpr int COPIES = kDqBK / ROWS_PER_COPY / 4;      // per wave per tensor
+    // K tiles: unpadded [64][D], V tiles [64][DV] bf16 in the chunk order of swz
+    // (the direct copies need 1 KB contiguous runs; swz keeps the K row reads,
+    // the K transpose reads and the V row reads free of bank conflicts).
+    static constexpr int KTILE = kDqBK * D;
+    static constexpr int VTILE = kDqBK * DV;
+    static constexpr int LDS_BYTES = 2 * (KTILE + VTILE) * 2;     // 2 K slots + 2 V slots
+    using KCopy = CopyPlan<D, kDqBK, kDqThreads / 64>;
+    using VCopy = CopyPlan<DV, kDqBK, kDqThreads / 64>;
 };
 
 // Work item of workgroup `bid` among nQ query-tile ranks: rank r is query tile
@@ -91,11 +95,15 @@ __device__ __forceinline__ void decode_q_item(int bid, int nQ, int qt_first, int
 
 // The PRECISE body runs the tiles whose rows need the exact path (below); the
 // plain body never touches its registers.
-template <int D, bool CAUSAL, bool PRECISE>
+template <int D, int DV, bool CAUSAL, bool PRECISE>
 __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, int hq, int qt) {
-    using T = DqTile<D>;
-    constexpr int DK = D / 16;
-    constexpr int DB = D / 32;
+    using T = DqTile<D, DV>;
+    using KC = typename T::KCopy;
+    using VC = typename T::VCopy;
+    constexpr int DK = D / 16;    // k-steps of the score product
+    constexpr int DKV = DV / 16;  // k-steps of the dP product
+    constexpr int DKM = DK > DKV ? DK : DKV;
+    constexpr int DB = D / 32;    // 32-row blocks of dQ^T
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,9 +111,9 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
     const int S = a.S;
     const int hkv = hq / a.G;
     const size_t rowbase = ((size_t)b * a.Hq + hq) * (size_t)S;
-    const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
-    const uint16_t* Kp = a.k + kvbase;
-    const uint16_t* Vp = a.v + kvbase;
+    const size_t kvrows = ((size_t)b * a.Hkv + hkv) * (size_t)S;
+    const uint16_t* Kp = a.k + kvrows * D;
+    const uint16_t* Vp = a.v + kvrows * DV;
     const int q0 = qt * kDqBQ;
     const int qrow = q0 + 32 * wave + l32;
     const bool live = qrow < S;
@@ -113,27 +121,27 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
     constexpr bool precise = PRECISE;
 
     // Q and dO rows as B operands; delta = rowsum(dO * O) from the stored O.
-    bf16x8 qf[DK], df[DK];
+    bf16x8 qf[DK], df[DKV];
     float dpart = 0.0f;
     if (live) {
-        const size_t off = (rowbase + qrow) * D + 8 * h;
-        const u32x4* qs = (const u32x4*)(a.q + off);
-        const u32x4* ds = (const u32x4*)(a.dout + off);
-        const u32x4* os = (const u32x4*)(a.o + off);
+        const u32x4* qs = (const u32x4*)(a.q + (rowbase + qrow) * D + 8 * h);
+        const u32x4* ds = (const u32x4*)(a.dout + (rowbase + qrow) * DV + 8 * h);
+        const u32x4* os = (const u32x4*)(a.o + (rowbase + qrow) * DV + 8 * h);
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) {
-            qf[dk] = __builtin_bit_cast(bf16x8, qs[2 * dk]);
-            df[dk] = __builtin_bit_cast(bf16x8, ds[2 * dk]);
-            const bf16x8 ov = __builtin_bit_cast(bf16x8, os[2 * dk]);
+        for (int dk = 0; dk < DKM; ++dk) {
+            if (dk < DK) qf[dk] = __builtin_bit_cast(bf16x8, qs[2 * dk]);
+            if (dk < DKV) {
+                df[dk] = __builtin_bit_cast(bf16x8, ds[2 * dk]);
+                const bf16x8 ov = __builtin_bit_cast(bf16x8, os[2 * dk]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dpart += (float)df[dk][e] * (float)ov[e];
+                for (int e = 0; e < 8; ++e) dpart += (float)df[dk][e] * (float)ov[e];
+            }
         }
     } else {
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) {
-            qf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-            df[dk] = qf[dk];
-        }
+        for (int dk = 0; dk < DK; ++dk) qf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int dk = 0; dk < DKV; ++dk) df[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
     float delta = halves_sum(dpart);
     const float lse2 = live ? a.lse[rowbase + qrow] * kLog2e : INFINITY;
@@ -148,29 +156,41 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
     const int wjstart = W > 0 ? max(0, row0 - W + 1) / kDqBK : 0;
 
     __bf16* const Kring = smem;
-    __bf16* const Vring = smem + 2 * T::TILE;
+    __bf16* const Vring = smem + 2 * T::KTILE;
     // Direct copies (as in the forward): rows past the end repeat row S-1; those
     // keys are masked (probability 0) on the last tile.
-    int crow[T::COPIES], ccol[T::COPIES];
+    int kcrow[KC::N], kccol[KC::N], vcrow[VC::N], vccol[VC::N];
 #pragma unroll
-    for (int n = 0; n < T::COPIES; ++n) {
-        crow[n] = (wave * T::COPIES + n) * T::ROWS_PER_COPY + lane / T::CH;
-        ccol[n] = (((lane % T::CH) ^ swz_f<D>(crow[n]))) * 8;
+    for (int n = 0; n < KC::N; ++n) {
+        kcrow[n] = (wave * KC::N + n) * KC::ROWS_PER_COPY + lane / KC::CH;
+        kccol[n] = (((lane % KC::CH) ^ swz_f<D>(kcrow[n]))) * 8;
     }
-    auto copy_tile = [&](const uint16_t* src, __bf16* dst, int j) {
+#pragma unroll
+    for (int n = 0; n < VC::N; ++n) {
+        vcrow[n] = (wave * VC::N + n) * VC::ROWS_PER_COPY + lane / VC::CH;
+        vccol[n] = (((lane % VC::CH) ^ swz_f<DV>(vcrow[n]))) * 8;
+    }
+    auto copy_kv = [&](int slot, int j) {
         const int k0 = j * kDqBK;
 #pragma unroll
-        for (int n = 0; n < T::COPIES; ++n) {
-            const int key = min(k0 + crow[n], S - 1);
-            copy16_to_lds(src + (uint32_t)(key * D + ccol[n]), dst + (wave * T::COPIES + n) * 512);
+        for (int n = 0; n < KC::N; ++n) {
+            const int key = min(k0 + kcrow[n], S - 1);
+            copy16_to_lds(Kp + (uint32_t)(key * D + kccol[n]), Kring + slot * T::KTILE + (wave * KC::N + n) * 512);
+        }
+#pragma unroll
+        for (int n = 0; n < VC::N; ++n) {
+            const int key = min(k0 + vcrow[n], S - 1);
+            copy16_to_lds(Vp + (uint32_t)(key * DV + vccol[n]), Vring + slot * T::VTILE + (wave * VC::N + n) * 512);
         }
     };
-    // Per-lane LDS offsets: K/V rows (A operands of S^T and dP^T) per k-step, and
-    // K transpose quads per 32-column block and row half (row offsets that are
-    // multiples of 16 are added as constants).
-    int roff[DK], toff[2][DB];
+    // Per-lane LDS offsets: K and V rows (A operands of S^T and dP^T) per k-step,
+    // and K transpose quads per 32-column block and row half (row offsets that
+    // are multiples of 16 are added as constants).
+    int roff[DK], rvoff[DKV], toff[2][DB];
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+#pragma unroll
+    for (int dk = 0; dk < DKV; ++dk) rvoff[dk] = swz<DV>(l32, dk * 16 + 8 * h);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -187,29 +207,26 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
     // slot while tile j is multiplied.
     for (int pass = precise ? 0 : 1; pass < 2; ++pass) {
         float dacc = 0.0f;
-        copy_tile(Kp, Kring + (jstart & 1) * T::TILE, jstart);
-        copy_tile(Vp, Vring + (jstart & 1) * T::TILE, jstart);
+        copy_kv(jstart & 1, jstart);
         wait_copies();
         __syncthreads();
         for (int j = jstart; j < jend; ++j) {
-            if (j + 1 < jend) {
-                copy_tile(Kp, Kring + ((j + 1) & 1) * T::TILE, j + 1);
-                copy_tile(Vp, Vring + ((j + 1) & 1) * T::TILE, j + 1);
-            }
+            if (j + 1 < jend) copy_kv((j + 1) & 1, j + 1);
             if (j >= wjstart && j < wjend) {
-                const __bf16* Ks = Kring + (j & 1) * T::TILE;
-                const __bf16* Vs = Vring + (j & 1) * T::TILE;
+                const __bf16* Ks = Kring + (j & 1) * T::KTILE;
+                const __bf16* Vs = Vring + (j & 1) * T::VTILE;
                 const int k0 = j * kDqBK;
                 const bool need_mask = j == wjend - 1 || (W > 0 && k0 < row0 + 32 - W);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-                    for (int dk = 0; dk < DK; ++dk) {
-                        const bf16x8 kf = lds_read8(Ks + roff[dk] + kb * 32 * D);
-                        const bf16x8 vf = lds_read8(Vs + roff[dk] + kb * 32 * D);
-                        s = mfma32(kf, qf[dk], s);
-                        dp = mfma32(vf, df[dk], dp);
+                    for (int dk = 0; dk < DKM; ++dk) {
+                        bf16x8 kf, vf;
+                        if (dk < DK) kf = lds_read8(Ks + roff[dk] + kb * 32 * D);
+                        if (dk < DKV) vf = lds_read8(Vs + rvoff[dk] + kb * 32 * DV);
+                        if (dk < DK) s = mfma32(kf, qf[dk], s);
+                        if (dk < DKV) dp = mfma32(vf, df[dk], dp);
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lse2));
@@ -276,16 +293,16 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
 
 // One launch over every query tile; tiles 0 .. a.precise_tiles-1 take the exact
 // path, so its few workgroups run in the tail of the longest-first schedule.
-template <int D, bool CAUSAL>
+template <int D, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
     const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
     int b, hq, qt;
     decode_q_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
     if (qt < a.precise_tiles)
-        dq_body<D, CAUSAL, true>(a, smem, b, hq, qt);
+        dq_body<D, DV, CAUSAL, true>(a, smem, b, hq, qt);
     else
-        dq_body<D, CAUSAL, false>(a, smem, b, hq, qt);
+        dq_body<D, DV, CAUSAL, false>(a, smem, b, hq, qt);
 }
 
 // ---------------------------------------------------------------------------
@@ -296,30 +313,37 @@ constexpr int kKvBQ = 32;      // query rows per streamed tile
 constexpr int kKvSplits = 4;   // wave pairs that split the (head, query tile) iterations
 constexpr int kKvThreads = 64 * 2 * kKvSplits;
 
-template <int D>
+template <int D, int DV>
 struct KvTile {
-    // V tile [64][D] and per-split double-buffered Q / dO tiles [32][D], all bf16
-    // in the swizzled chunk order of swz<D>; lse*log2e and delta per query row.
-    static constexpr int CH = D / 8;
-    static constexpr int ROWS_PER_COPY = 64 / CH;                    // rows per 1 KB copy
+    // V tile [64][DV] and per-split double-buffered Q [32][D] and dO [32][DV]
+    // tiles, all bf16 in the swizzled chunk order of swz; lse*log2e and delta per
+    // query row.
     static constexpr int QTILE = kKvBQ * D;                          // elements
-    static constexpr int STAGE_BYTES = 2 * QTILE * 2 + 2 * kKvBQ * 4;
+    static constexpr int DTILE = kKvBQ * DV;
+    static constexpr int STAGE_BYTES = (QTILE + DTILE) * 2 + 2 * kKvBQ * 4;
     static constexpr int SPLIT_BYTES = 2 * STAGE_BYTES;
-    static constexpr int VTILE_BYTES = kKvBK * D * 2;
+    static constexpr int VTILE_BYTES = kKvBK * DV * 2;
     static constexpr int TILE_BYTES = VTILE_BYTES + kKvSplits * SPLIT_BYTES;
     // final sum: two splits hand over dK and dV of both key halves
-    static constexpr int XCHG_BYTES = 2 * 2 * 2 * (D / 32) * 16 * 64 * 4;
+    static constexpr int XCHG_BYTES = 2 * 2 * (D / 32 + DV / 32) * 16 * 64 * 4;
     static constexpr int LDS_BYTES = TILE_BYTES > XCHG_BYTES ? TILE_BYTES : XCHG_BYTES;
-    static constexpr int QCOPIES = kKvBQ / ROWS_PER_COPY / 2;        // per wave of a pair, per tensor
-    static constexpr int VCOPIES = kKvBK / ROWS_PER_COPY / (2 * kKvSplits);  // per wave
-    static_assert(QCOPIES >= 1 && VCOPIES >= 1, "copy split");
+    using QCopy = CopyPlan<D, kKvBQ, 2>;                             // per wave of a pair
+    using DCopy = CopyPlan<DV, kKvBQ, 2>;
+    using VCopy = CopyPlan<DV, kKvBK, 2 * kKvSplits>;                // per wave
 };
 
-template <int D, bool CAUSAL>
+template <int D, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
-    using T = KvTile<D>;
-    constexpr int DK = D / 16;
-    constexpr int DB = D / 32;
+    using T = KvTile<D, DV>;
+    using QC = typename T::QCopy;
+    using DC = typename T::DCopy;
+    using VC = typename T::VCopy;
+    constexpr int DK = D / 16;     // k-steps of the score product
+    constexpr int DKV = DV / 16;   // k-steps of the dP product
+    constexpr int DKM = DK > DKV ? DK : DKV;
+    constexpr int DBK = D / 32;    // 32-row blocks of dK^T
+    constexpr int DBV = DV / 32;   // 32-row blocks of dV^T
+    constexpr int DBM = DBK > DBV ? DBK : DBV;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -357,7 +381,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     // K rows of this lane's key as B operands (zero past the end).
     bf16x8 kf[DK];
     if (key < S) {
-        const u32x4* ks = (const u32x4*)(a.k + (kvrow + key) * D + 8 * h);
+        const u32x4* ks = (const u32x4*)(a.k + (kvrow + key) * D + 8 * h);  // K is D wide
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) kf[dk] = __builtin_bit_cast(bf16x8, ks[2 * dk]);
     } else {
@@ -370,17 +394,19 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     unsigned char* const split_base = lds_raw + T::VTILE_BYTES + split * T::SPLIT_BYTES;
     auto stage_q = [&](int st) { return (__bf16*)(split_base + st * T::STAGE_BYTES); };
     auto stage_do = [&](int st) { return stage_q(st) + T::QTILE; };
-    auto stage_lse = [&](int st) { return (float*)(split_base + st * T::STAGE_BYTES + 2 * T::QTILE * 2); };
+    auto stage_lse = [&](int st) {
+        return (float*)(split_base + st * T::STAGE_BYTES + (T::QTILE + T::DTILE) * 2);
+    };
     auto stage_dl = [&](int st) { return stage_lse(st) + kKvBQ; };
 
     // V tile: every wave copies VCOPIES rows-runs (rows past the end repeat S-1;
     // those keys' columns are never stored).
 #pragma unroll
-    for (int n = 0; n < T::VCOPIES; ++n) {
-        const int row = (wave * T::VCOPIES + n) * T::ROWS_PER_COPY + lane / T::CH;
-        const int col = (((lane % T::CH) ^ swz_f<D>(row))) * 8;
+    for (int n = 0; n < VC::N; ++n) {
+        const int row = (wave * VC::N + n) * VC::ROWS_PER_COPY + lane / VC::CH;
+        const int col = (((lane % VC::CH) ^ swz_f<DV>(row))) * 8;
         const int kr = min(kv0 + row, S - 1);
-        copy16_to_lds(a.v + (kvrow + kr) * D + col, Vs + (wave * T::VCOPIES + n) * 512);
+        copy16_to_lds(a.v + (kvrow + kr) * DV + col, Vs + (wave * VC::N + n) * 512);
     }
 
     // Iterations: (g, query tile qi) for the query tiles that see some key of the
@@ -392,14 +418,19 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     const int total = G * per_g;
     const int steps = (total + kKvSplits - 1) / kKvSplits;
 
-    // Q / dO copies of a pair: copy n of wave w2 fills tile rows (w2*QCOPIES + n) *
+    // Q / dO copies of a pair: copy n of wave w2 fills tile rows (w2*N + n) *
     // ROWS_PER_COPY + lane / CH. Rows past S repeat row S-1; their lse is +inf,
     // so their probabilities, and every term they touch, are exactly 0.
-    int qcrow[T::QCOPIES], qccol[T::QCOPIES];
+    int qcrow[QC::N], qccol[QC::N], dcrow[DC::N], dccol[DC::N];
 #pragma unroll
-    for (int n = 0; n < T::QCOPIES; ++n) {
-        qcrow[n] = (w2 * T::QCOPIES + n) * T::ROWS_PER_COPY + lane / T::CH;
-        qccol[n] = (((lane % T::CH) ^ swz_f<D>(qcrow[n]))) * 8;
+    for (int n = 0; n < QC::N; ++n) {
+        qcrow[n] = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+        qccol[n] = (((lane % QC::CH) ^ swz_f<D>(qcrow[n]))) * 8;
+    }
+#pragma unroll
+    for (int n = 0; n < DC::N; ++n) {
+        dcrow[n] = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
+        dccol[n] = (((lane % DC::CH) ^ swz_f<DV>(dcrow[n]))) * 8;
     }
     float lst = 0.f, dlst = 0.f;
     auto fetch = [&](int step) {  // async copies of Q/dO + lse/delta into registers
@@ -409,11 +440,24 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
         const int g = it / per_g, qi = qi_first + it % per_g;
         const size_t rb = ((size_t)b * a.Hq + hkv * G + g) * (size_t)S;
         const int qr0 = qi * kKvBQ;
+        if (D == DV) {  // one address for both tensors
 #pragma unroll
-        for (int n = 0; n < T::QCOPIES; ++n) {
-            const size_t off = (rb + min(qr0 + qcrow[n], S - 1)) * D + qccol[n];
-            copy16_to_lds(a.q + off, stage_q(st) + (w2 * T::QCOPIES + n) * 512);
-            copy16_to_lds(a.dout + off, stage_do(st) + (w2 * T::QCOPIES + n) * 512);
+            for (int n = 0; n < QC::N; ++n) {
+                const size_t off = (rb + min(qr0 + qcrow[n], S - 1)) * D + qccol[n];
+                copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
+                copy16_to_lds(a.dout + off, stage_do(st) + (w2 * QC::N + n) * 512);
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < QC::N; ++n) {
+                const size_t off = (rb + min(qr0 + qcrow[n], S - 1)) * D + qccol[n];
+                copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
+            }
+#pragma unroll
+            for (int n = 0; n < DC::N; ++n) {
+                const size_t off = (rb + min(qr0 + dcrow[n], S - 1)) * DV + dccol[n];
+                copy16_to_lds(a.dout + off, stage_do(st) + (w2 * DC::N + n) * 512);
+            }
         }
         if (ptid < kKvBQ) {
             // raw values only: any use of a loaded value here would make the wave
@@ -433,24 +477,30 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
         }
     };
 
-    // Per-lane LDS offsets: A-operand rows (Q, dO, V) per k-step; transpose quads
-    // (Q^T, dO^T) per 32-column block and row half.
-    int roff[DK], toff[2][DB];
+    // Per-lane LDS offsets: A-operand rows (Q; dO and V) per k-step; transpose
+    // quads (Q^T; dO^T) per 32-column block and row half.
+    int roff[DK], rvoff[DKV], toff[2][DBK], tvoff[2][DBV];
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int dk = 0; dk < DKV; ++dk) rvoff[dk] = swz<DV>(l32, dk * 16 + 8 * h);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int db = 0; db < DBK; ++db)
             toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
                                   db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-
-    f32x16 dk[DB], dv[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        dk[db] = zero16();
-        dv[db] = zero16();
+        for (int db = 0; db < DBV; ++db)
+            tvoff[hf][db] = swz<DV>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                    db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     }
+
+    f32x16 dk[DBK], dv[DBV];
+#pragma unroll
+    for (int db = 0; db < DBK; ++db) dk[db] = zero16();
+#pragma unroll
+    for (int db = 0; db < DBV; ++db) dv[db] = zero16();
 
     fetch(0);
     publish(0);
@@ -474,12 +524,15 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                 const bool need_mask = (CAUSAL && qs0 < kw0 + 31) || (W > 0 && qs0 + 31 > kw0 + W - 1);
                 f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-                for (int dd = 0; dd < DK; ++dd) {
-                    const bf16x8 qa = lds_read8(Qs + roff[dd]);
-                    const bf16x8 da = lds_read8(Ds + roff[dd]);
-                    const bf16x8 vb = lds_read8(Vs + roff[dd] + w2 * 32 * D);
-                    s = mfma32(qa, kf[dd], s);
-                    dp = mfma32(da, vb, dp);
+                for (int dd = 0; dd < DKM; ++dd) {
+                    bf16x8 qa, da, vb;
+                    if (dd < DK) qa = lds_read8(Qs + roff[dd]);
+                    if (dd < DKV) {
+                        da = lds_read8(Ds + rvoff[dd]);
+                        vb = lds_read8(Vs + rvoff[dd] + w2 * 32 * DV);
+                    }
+                    if (dd < DK) s = mfma32(qa, kf[dd], s);
+                    if (dd < DKV) dp = mfma32(da, vb, dp);
                 }
                 // rows of s/dp are queries 8(r/4) + 4h + r%4; the column is this lane's key.
                 // dV^T += dO^T P and dK^T += Q^T dS over two 16-query steps.
@@ -515,16 +568,19 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                         sl = pack8(bf_lo(dsv[0]), bf_lo(dsv[1]), bf_lo(dsv[2]), bf_lo(dsv[3]), bf_lo(dsv[4]),
                                    bf_lo(dsv[5]), bf_lo(dsv[6]), bf_lo(dsv[7]));
                     }
-                    const int rb = 16 * t2 * D;
+                    const int rbk = 16 * t2 * D, rbv = 16 * t2 * DV;
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 dot = concat(lds_read_tr(Ds + toff[0][db] + rb), lds_read_tr(Ds + toff[1][db] + rb));
-                        const bf16x8 qt = concat(lds_read_tr(Qs + toff[0][db] + rb), lds_read_tr(Qs + toff[1][db] + rb));
-                        dv[db] = mfma32(dot, ph, dv[db]);
-                        dk[db] = mfma32(qt, sh, dk[db]);
+                    for (int db = 0; db < DBM; ++db) {
+                        bf16x8 dot, qt;
+                        if (db < DBV)
+                            dot = concat(lds_read_tr(Ds + tvoff[0][db] + rbv), lds_read_tr(Ds + tvoff[1][db] + rbv));
+                        if (db < DBK)
+                            qt = concat(lds_read_tr(Qs + toff[0][db] + rbk), lds_read_tr(Qs + toff[1][db] + rbk));
+                        if (db < DBV) dv[db] = mfma32(dot, ph, dv[db]);
+                        if (db < DBK) dk[db] = mfma32(qt, sh, dk[db]);
                         if (precise) {
-                            dv[db] = mfma32(dot, pl, dv[db]);
-                            dk[db] = mfma32(qt, sl, dk[db]);
+                            if (db < DBV) dv[db] = mfma32(dot, pl, dv[db]);
+                            if (db < DBK) dk[db] = mfma32(qt, sl, dk[db]);
                         }
                     }
                 }
@@ -537,64 +593,69 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
 
     // Sum the four splits' partials (same keys, disjoint iterations) in a fixed
     // order: splits 2,3 hand over to splits 0,1; then split 1 hands dK to split 0
-    // and split 0 hands dV to split 1. Layout [slot][w2][tensor][db][r][lane].
+    // and split 0 hands dV to split 1. Layout [slot][w2][dK blocks, dV blocks][r][lane].
     float* xchg = (float*)lds_raw;
     auto slot = [&](int sl, int tensor, int db, int r) {
-        return xchg + (((((sl * 2 + w2) * 2 + tensor) * DB + db) * 16 + r) * 64) + lane;
+        return xchg + ((((sl * 2 + w2) * (DBK + DBV) + tensor * DBK + db) * 16 + r) * 64) + lane;
     };
     if (split >= 2) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int r = 0; r < 16; ++r) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                *slot(split - 2, 0, db, r) = dk[db][r];
-                *slot(split - 2, 1, db, r) = dv[db][r];
-            }
+            for (int db = 0; db < DBK; ++db) *slot(split - 2, 0, db, r) = dk[db][r];
+#pragma unroll
+            for (int db = 0; db < DBV; ++db) *slot(split - 2, 1, db, r) = dv[db][r];
+        }
     }
     __syncthreads();
     if (split < 2) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int r = 0; r < 16; ++r) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                dk[db][r] += *slot(split, 0, db, r);
-                dv[db][r] += *slot(split, 1, db, r);
-            }
+            for (int db = 0; db < DBK; ++db) dk[db][r] += *slot(split, 0, db, r);
+#pragma unroll
+            for (int db = 0; db < DBV; ++db) dv[db][r] += *slot(split, 1, db, r);
+        }
     }
     __syncthreads();
     if (split == 1) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBK; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) *slot(0, 0, db, r) = dk[db][r];
     } else if (split == 0) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBV; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) *slot(1, 1, db, r) = dv[db][r];
     }
     __syncthreads();
-    if (split < 2 && key < S) {
-        float* out = (split == 0 ? a.dk : a.dv) + (kvrow + key) * D;
-        const float sc = split == 0 ? a.scale : 1.0f;
+    if (split == 0 && key < S) {  // dK = scale * (own + split 1's), D wide
+        float* out = a.dk + (kvrow + key) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBK; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 f32x4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g4 + e;
-                    const float mine = split == 0 ? dk[db][r] : dv[db][r];
-                    const float other = split == 0 ? *slot(0, 0, db, r) : *slot(1, 1, db, r);
-                    v[e] = (mine + other) * sc;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = (dk[db][4 * g4 + e] + *slot(0, 0, db, 4 * g4 + e)) * a.scale;
+                *(f32x4*)(out + db * 32 + 8 * g4 + 4 * h) = v;
+            }
+    } else if (split == 1 && key < S) {  // dV = own + split 0's, DV wide
+        float* out = a.dv + (kvrow + key) * DV;
+#pragma unroll
+        for (int db = 0; db < DBV; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = dv[db][4 * g4 + e] + *slot(1, 1, db, 4 * g4 + e);
                 *(f32x4*)(out + db * 32 + 8 * g4 + 4 * h) = v;
             }
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int DV, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& args, int stages, hipStream_t stream) {
     BwdArgs a = args;
     if (stages & 1) {
@@ -603,16 +664,16 @@ hipError_t launch_bwd_t(const BwdArgs& args, int stages, hipStream_t stream) {
         const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
         a.precise_tiles = a.precise_all ? nQ : (CAUSAL || a.S <= kPreciseRows) ? 1 : 0;
         const long long blocks = (long long)a.B * a.Hq * nQ;
-        hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kDqThreads),
-                           DqTile<D>::LDS_BYTES, stream, a);
+        constexpr int lds = DqTile<D, DV>::LDS_BYTES;
+        hipLaunchKernelGGL((dq_kernel<D, DV, CAUSAL>), dim3((unsigned)blocks), dim3(kDqThreads), lds, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (stages & 2) {
         const int nKB = (a.S + kKvBK - 1) / kKvBK;
         const long long kvblocks = (long long)a.B * a.Hkv * nKB;
-        hipLaunchKernelGGL((dkv_kernel<D, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKvThreads),
-                           KvTile<D>::LDS_BYTES, stream, a);
+        constexpr int lds = KvTile<D, DV>::LDS_BYTES;
+        hipLaunchKernelGGL((dkv_kernel<D, DV, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKvThreads), lds, stream, a);
         return hipGetLastError();
     }
     return hipSuccess;
@@ -623,24 +684,33 @@ hipError_t set_lds(K kernel, int bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <int D, int DV>
+hipError_t setup_pair() {
+    hipError_t e;
+    if ((e = set_lds(dq_kernel<D, DV, false>, DqTile<D, DV>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_kernel<D, DV, true>, DqTile<D, DV>::LDS_BYTES))) return e;
+    if ((e = set_lds(dkv_kernel<D, DV, false>, KvTile<D, DV>::LDS_BYTES))) return e;
+    return set_lds(dkv_kernel<D, DV, true>, KvTile<D, DV>::LDS_BYTES);
+}
+
+template <int D, int DV>
+hipError_t launch_pair(const BwdArgs& a, int stages, hipStream_t stream) {
+    return a.causal ? launch_bwd_t<D, DV, true>(a, stages, stream) : launch_bwd_t<D, DV, false>(a, stages, stream);
+}
+
 }  // namespace
 
 hipError_t bwd_setup_device() {
     hipError_t e;
-    if ((e = set_lds(dq_kernel<64, false>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<64, true>, DqTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, false>, DqTile<128>::LDS_BYTES))) return e;
-    if ((e = set_lds(dq_kernel<128, true>, DqTile<128>::LDS_BYTES))) return e;
-    if ((e = set_lds(dkv_kernel<64, false>, KvTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dkv_kernel<64, true>, KvTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(dkv_kernel<128, false>, KvTile<128>::LDS_BYTES))) return e;
-    return set_lds(dkv_kernel<128, true>, KvTile<128>::LDS_BYTES);
+    if ((e = setup_pair<64, 64>())) return e;
+    if ((e = setup_pair<128, 128>())) return e;
+    if ((e = setup_pair<64, 128>())) return e;
+    return setup_pair<128, 64>();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int D, int stages, hipStream_t stream) {
-    if (D == 64)
-        return a.causal ? launch_bwd_t<64, true>(a, stages, stream) : launch_bwd_t<64, false>(a, stages, stream);
-    return a.causal ? launch_bwd_t<128, true>(a, stages, stream) : launch_bwd_t<128, false>(a, stages, stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, int DV, int stages, hipStream_t stream) {
+    if (D == 64) return DV == 64 ? launch_pair<64, 64>(a, stages, stream) : launch_pair<64, 128>(a, stages, stream);
+    return DV == 128 ? launch_pair<128, 128>(a, stages, stream) : launch_pair<128, 64>(a, stages, stream);
 }
 
 }  // namespace attn

@@ -39,6 +39,9 @@
 // bodies live in one launch, so the few exact-path workgroups run in the tail
 // of the longest-first schedule instead of in a launch of their own.
 //
+// Queries and keys have D columns and values DV (the d and d_v of Eq. (1)); each
+// is 64 or 128, in any combination.
+//
 // With a sliding window of W keys (query i sees keys i-W+1 .. i, the window of
 // the page's compressed sparse attention, Table 7) the tiles entirely below the
 // band are skipped as well, and a wave also masks the tiles that cross the
@@ -55,16 +58,16 @@ constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kLook = 4;        // LDS operand reads in flight ahead of the MFMAs
 
-template <int D>
+template <int D, int DV>
 struct FwdTile {
-    // K and V tiles are unpadded [64][D] bf16 in the chunk order of swz<D>, so
-    // each 1 KB run of rows is contiguous, as the direct copies need.
-    static constexpr int TILE = kFwdBK * D;                       // elements
-    static constexpr int LDS_BYTES = 4 * TILE * 2;                // 2 K slots + 2 V slots
-    static constexpr int CH = D / 8;                              // 16-byte chunks per row
-    static constexpr int ROWS_PER_COPY = 64 / CH;                 // rows per wave copy (1 KB)
-    static constexpr int COPIES = kFwdBK / ROWS_PER_COPY / kFwdWaves;  // per wave per tensor
-    static_assert(COPIES >= 1, "copy split");
+    // K tiles are unpadded [64][D] and V tiles [64][DV] bf16, in the chunk order
+    // of swz<D> and swz<DV>, so each 1 KB run of rows is contiguous, as the
+    // direct copies need.
+    static constexpr int KTILE = kFwdBK * D;                      // elements
+    static constexpr int VTILE = kFwdBK * DV;
+    static constexpr int LDS_BYTES = 2 * (KTILE + VTILE) * 2;     // 2 K slots + 2 V slots
+    using KCopy = CopyPlan<D, kFwdBK, kFwdWaves>;
+    using VCopy = CopyPlan<DV, kFwdBK, kFwdWaves>;
 };
 
 // Work item of workgroup `bid` among nQ query-tile ranks: rank r is query tile
@@ -94,11 +97,13 @@ __device__ __forceinline__ void decode_item(int bid, int nQ, int qt_first, int B
     hq = (c % Hkv) * G + g;
 }
 
-template <int D, bool CAUSAL, bool PRECISE>
+template <int D, int DV, bool CAUSAL, bool PRECISE>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, int hq, int qt) {
-    using T = FwdTile<D>;
-    constexpr int DK = D / 16;  // k-steps of the score product
-    constexpr int DB = D / 32;  // 32-row blocks of O^T
+    using T = FwdTile<D, DV>;
+    using KC = typename T::KCopy;
+    using VC = typename T::VCopy;
+    constexpr int DK = D / 16;   // k-steps of the score product
+    constexpr int DB = DV / 32;  // 32-row blocks of O^T
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,10 +111,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     const int h = lane >> 5, l32 = lane & 31;
     const int S = a.S;
     const int hkv = hq / a.G;
-    const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
-    const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
-    const uint16_t* Kp = a.k + kvbase;
-    const uint16_t* Vp = a.v + kvbase;
+    const size_t qrows = ((size_t)b * a.Hq + hq) * (size_t)S;
+    const size_t kvrows = ((size_t)b * a.Hkv + hkv) * (size_t)S;
+    const size_t qbase = qrows * D;
+    const uint16_t* Kp = a.k + kvrows * D;
+    const uint16_t* Vp = a.v + kvrows * DV;
     const int q0 = qt * kFwdBQ;
     // Rows interleave between the groups (group 0: 0-31, 64-95, ...; group 1:
     // 32-63, 96-127, ...) so both see the same number of causal tiles.
@@ -143,24 +149,37 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     const int wjstart = W > 0 ? max(0, row0 - W + 1) / kFwdBK : 0;
 
     __bf16* const Kring = smem;
-    __bf16* const Vring = smem + 2 * T::TILE;
+    __bf16* const Vring = smem + 2 * T::KTILE;
 
-    // Direct copies: copy n of this wave fills tile rows (wave*COPIES + n) *
+    // Direct copies: copy n of this wave fills tile rows (wave*N + n) *
     // ROWS_PER_COPY + lane / CH, physical chunk lane % CH, which holds logical
     // chunk (lane % CH) ^ swz_f(row). Rows past the end repeat row S-1: their
     // scores are masked and their probabilities are exactly 0.
-    int crow[T::COPIES], ccol[T::COPIES];
+    int kcrow[KC::N], kccol[KC::N], vcrow[VC::N], vccol[VC::N];
 #pragma unroll
-    for (int n = 0; n < T::COPIES; ++n) {
-        crow[n] = (wave * T::COPIES + n) * T::ROWS_PER_COPY + lane / T::CH;
-        ccol[n] = (((lane % T::CH) ^ swz_f<D>(crow[n]))) * 8;
+    for (int n = 0; n < KC::N; ++n) {
+        kcrow[n] = (wave * KC::N + n) * KC::ROWS_PER_COPY + lane / KC::CH;
+        kccol[n] = (((lane % KC::CH) ^ swz_f<D>(kcrow[n]))) * 8;
     }
-    auto copy_tile = [&](const uint16_t* src, __bf16* dst, int j) {
+#pragma unroll
+    for (int n = 0; n < VC::N; ++n) {
+        vcrow[n] = (wave * VC::N + n) * VC::ROWS_PER_COPY + lane / VC::CH;
+        vccol[n] = (((lane % VC::CH) ^ swz_f<DV>(vcrow[n]))) * 8;
+    }
+    auto copy_k = [&](__bf16* dst, int j) {
         const int k0 = j * kFwdBK;
 #pragma unroll
-        for (int n = 0; n < T::COPIES; ++n) {
-            const int key = min(k0 + crow[n], S - 1);
-            copy16_to_lds(src + (uint32_t)(key * D + ccol[n]), dst + (wave * T::COPIES + n) * 512);
+        for (int n = 0; n < KC::N; ++n) {
+            const int key = min(k0 + kcrow[n], S - 1);
+            copy16_to_lds(Kp + (uint32_t)(key * D + kccol[n]), dst + (wave * KC::N + n) * 512);
+        }
+    };
+    auto copy_v = [&](__bf16* dst, int j) {
+        const int k0 = j * kFwdBK;
+#pragma unroll
+        for (int n = 0; n < VC::N; ++n) {
+            const int key = min(k0 + vcrow[n], S - 1);
+            copy16_to_lds(Vp + (uint32_t)(key * DV + vccol[n]), dst + (wave * VC::N + n) * 512);
         }
     };
     // Per-lane read offsets (elements) into a slot: K rows (b128, A operand) for
@@ -173,8 +192,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            voff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
-                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+            voff[hf][db] = swz<DV>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                   db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -191,14 +210,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     auto matrix_phase = [&](int j) {
         __builtin_amdgcn_s_setprio(1);
         if (j - 1 >= wjstart && j - 1 < wjend) {
-            const __bf16* Vs = Vring + ((j - 1) & 1) * T::TILE;
+            const __bf16* Vs = Vring + ((j - 1) & 1) * T::VTILE;
             constexpr int MPER = PRECISE ? 2 : 1;  // MFMAs per V^T operand
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x4 v1 = lds_read_tr(Vs + voff[0][db] + 16 * t * D);
-                    const bf16x4 v2 = lds_read_tr(Vs + voff[1][db] + 16 * t * D);
+                    const bf16x4 v1 = lds_read_tr(Vs + voff[0][db] + 16 * t * DV);
+                    const bf16x4 v2 = lds_read_tr(Vs + voff[1][db] + 16 * t * DV);
                     const bf16x8 vt = concat(v1, v2);
                     oacc[db] = mfma32(vt, pk[t], oacc[db]);
                     if (PRECISE) oacc[db] = mfma32(vt, pl[t], oacc[db]);
@@ -215,7 +234,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             __builtin_amdgcn_sched_barrier(0);
         }
         if (j >= wjstart && j < wjend) {
-            const __bf16* Ks = Kring + (j & 1) * T::TILE;
+            const __bf16* Ks = Kring + (j & 1) * T::KTILE;
             sc[0] = zero16();
             sc[1] = zero16();
 #pragma unroll
@@ -294,9 +313,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
 
     // Prologue: tile j sits in slot j & 1 of its ring; the first two K tiles and
     // the first V tile.
-    copy_tile(Kp, Kring + (jstart & 1) * T::TILE, jstart);
-    if (jstart + 1 < jend) copy_tile(Kp, Kring + ((jstart + 1) & 1) * T::TILE, jstart + 1);
-    copy_tile(Vp, Vring + (jstart & 1) * T::TILE, jstart);
+    copy_k(Kring + (jstart & 1) * T::KTILE, jstart);
+    if (jstart + 1 < jend) copy_k(Kring + ((jstart + 1) & 1) * T::KTILE, jstart + 1);
+    copy_v(Vring + (jstart & 1) * T::VTILE, jstart);
     wait_copies();
     __syncthreads();
 
@@ -311,8 +330,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     // in their late phases.
     auto refill = [&](int s) {
         if (s > jstart) {
-            if (s + 1 < jend) copy_tile(Kp, Kring + ((s - 1) & 1) * T::TILE, s + 1);
-            if (s < jend) copy_tile(Vp, Vring + (s & 1) * T::TILE, s);
+            if (s + 1 < jend) copy_k(Kring + ((s - 1) & 1) * T::KTILE, s + 1);
+            if (s < jend) copy_v(Vring + (s & 1) * T::VTILE, s);
         }
     };
     if (grp == 0) {
@@ -338,7 +357,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     const float lt = halves_sum(l);
     if (qrow < S) {
         const float inv = 1.0f / lt;
-        uint16_t* op = a.o + qbase + (size_t)qrow * D;
+        uint16_t* op = a.o + (qrows + qrow) * DV;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -353,19 +372,19 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
 }
 
 // Query tiles 0 .. a.precise_tiles-1 take the exact P V product.
-template <int D, bool CAUSAL>
+template <int D, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
     const int nQ = (a.S + kFwdBQ - 1) / kFwdBQ;
     int b, hq, qt;
     decode_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
     if (qt < a.precise_tiles)
-        fwd_body<D, CAUSAL, true>(a, smem, b, hq, qt);
+        fwd_body<D, DV, CAUSAL, true>(a, smem, b, hq, qt);
     else
-        fwd_body<D, CAUSAL, false>(a, smem, b, hq, qt);
+        fwd_body<D, DV, CAUSAL, false>(a, smem, b, hq, qt);
 }
 
-template <int D, bool CAUSAL>
+template <int D, int DV, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
     // Rows that see at most 128 keys take the exact P V product: every tile of a
     // window of <= 128 keys, else tile 0 of a causal problem (rows 0..255 see at
@@ -375,8 +394,8 @@ hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
     FwdArgs a = args;
     a.precise_tiles = (CAUSAL && a.window > 0 && a.window <= 128) ? nQ : (CAUSAL || a.S <= 128) ? 1 : 0;
     const long long blocks = (long long)a.B * a.Hq * nQ;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kFwdThreads),
-                       FwdTile<D>::LDS_BYTES, stream, a);
+    constexpr int lds = FwdTile<D, DV>::LDS_BYTES;
+    hipLaunchKernelGGL((fwd_kernel<D, DV, CAUSAL>), dim3((unsigned)blocks), dim3(kFwdThreads), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -385,20 +404,31 @@ hipError_t set_lds(K kernel, int bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <int D, int DV>
+hipError_t setup_pair() {
+    hipError_t e = set_lds(fwd_kernel<D, DV, false>, FwdTile<D, DV>::LDS_BYTES);
+    return e ? e : set_lds(fwd_kernel<D, DV, true>, FwdTile<D, DV>::LDS_BYTES);
+}
+
+template <int D, int DV>
+hipError_t launch_pair(const FwdArgs& a, hipStream_t stream) {
+    return a.causal ? launch_fwd_t<D, DV, true>(a, stream) : launch_fwd_t<D, DV, false>(a, stream);
+}
+
 }  // namespace
 
 // Raise the dynamic-LDS limit of every forward instance on the current device.
 hipError_t fwd_setup_device() {
     hipError_t e;
-    if ((e = set_lds(fwd_kernel<64, false>, FwdTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(fwd_kernel<64, true>, FwdTile<64>::LDS_BYTES))) return e;
-    if ((e = set_lds(fwd_kernel<128, false>, FwdTile<128>::LDS_BYTES))) return e;
-    return set_lds(fwd_kernel<128, true>, FwdTile<128>::LDS_BYTES);
+    if ((e = setup_pair<64, 64>())) return e;
+    if ((e = setup_pair<128, 128>())) return e;
+    if ((e = setup_pair<64, 128>())) return e;
+    return setup_pair<128, 64>();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t stream) {
-    if (D == 64) return a.causal ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
-    return a.causal ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
+hipError_t launch_fwd(const FwdArgs& a, int D, int DV, hipStream_t stream) {
+    if (D == 64) return DV == 64 ? launch_pair<64, 64>(a, stream) : launch_pair<64, 128>(a, stream);
+    return DV == 128 ? launch_pair<128, 128>(a, stream) : launch_pair<128, 64>(a, stream);
 }
 
 }  // namespace attn

@@ -94,6 +94,16 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * D + ((((col >> 3) ^ swz_f<D>(row))) << 3) + (col & 7);
 }
 
+// Split of the direct copies of a [ROWS][W] bf16 tile (swz<W> order) over WAVES
+// waves: one copy instruction moves 64 lanes x 16 bytes, a 1 KB run of whole rows.
+template <int W, int ROWS, int WAVES>
+struct CopyPlan {
+    static constexpr int CH = W / 8;                        // 16-byte chunks per row
+    static constexpr int ROWS_PER_COPY = 64 / CH;
+    static constexpr int N = ROWS / ROWS_PER_COPY / WAVES;  // copies per wave
+    static_assert(N >= 1 && N * ROWS_PER_COPY * WAVES == ROWS, "copy split");
+};
+
 // Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
 // lane i's 16 bytes land at lds_wave_base + 16 i. lds_wave_base must be the same
 // for every lane of the wave. Completion is tracked by vmcnt only: the caller

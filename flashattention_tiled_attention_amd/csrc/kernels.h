@@ -41,8 +41,9 @@ struct BwdArgs {
 };
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
-hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t stream);
+// D: query/key head dimension, DV: value head dimension (each 64 or 128).
+hipError_t launch_fwd(const FwdArgs& a, int D, int DV, hipStream_t stream);
 // stages: bit 0 = dQ and delta, bit 1 = dK/dV (in that order when both are set)
-hipError_t launch_bwd(const BwdArgs& a, int D, int stages, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, int DV, int stages, hipStream_t stream);
 
 }  // namespace attn

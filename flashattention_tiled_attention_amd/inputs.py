@@ -41,7 +41,8 @@ def qkv(B, Hq, Hkv, S, D, seed=0, with_dout=False, Dv=None):
     return q, k, v, dout
 
 
-# The workloads the benchmark and the parity tests run: (name, B, Hq, Hkv, S, D, causal, pass).
+# The workloads the benchmark and the parity tests run: (name, B, Hq, Hkv, S, D, causal, pass;
+# optional window and value head dimension Dv, which defaults to D).
 CONFIGS = {
     "single_head_s128_d64": dict(B=1, Hq=1, Hkv=1, S=128, D=64, causal=False, bwd=False),
     "llama8b_causal_gqa_s4096": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, bwd=False),
@@ -50,4 +51,6 @@ CONFIGS = {
     "llama8b_causal_gqa_s4096_bwd": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, bwd=True),
     # causal sliding window of 128 keys (the window of the compressed sparse attention, Table 7)
     "llama8b_window128_s4096": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, window=128, bwd=True),
+    # value head dimension d_v != d (Eq. 1): 128-wide queries/keys, 64-wide values
+    "gqa_dqk128_dv64_s4096": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, Dv=64, causal=True, bwd=True),
 }

@@ -44,15 +44,15 @@ extern "C" {
 enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,          /* a required pointer is NULL */
-    ATTN_ERR_SHAPE = 2,         /* B, Hq, Hkv, S or D < 1, or B*Hq*S*D >= 2^40 */
+    ATTN_ERR_SHAPE = 2,         /* B, Hq, Hkv, S, D or Dv < 1, or B*Hq*S*max(D, Dv) >= 2^40 */
     ATTN_ERR_GQA = 3,           /* Hq is not a multiple of Hkv */
-    ATTN_ERR_UNSUPPORTED_D = 4, /* D is neither 64 nor 128 */
+    ATTN_ERR_UNSUPPORTED_D = 4, /* D (or Dv) is neither 64 nor 128 */
     ATTN_ERR_ALIGN = 5,         /* a tensor or workspace pointer is not 16-byte aligned */
     ATTN_ERR_WORKSPACE = 6,     /* workspace is NULL or smaller than attn_bwd_workspace_bytes() */
     ATTN_ERR_SCALE = 7,         /* scale is NaN or infinite */
     ATTN_ERR_HIP = 8,           /* the HIP runtime failed (no device, launch error) */
     ATTN_ERR_DEVICE = 9,        /* the current device is not a gfx950 GPU */
-    ATTN_ERR_WINDOW = 10        /* a sliding window of fewer than 1 key */
+    ATTN_ERR_WINDOW = 10        /* a sliding window of fewer than 1 key (vdim: < 0, or set without causal) */
 };
 
 /*
@@ -138,6 +138,30 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
                     const void* dout, float* dq, float* dk, float* dv,
                     int B, int Hq, int Hkv, int S, int D, int window, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Separate value head dimension: Eq. (1) (section 2.1) gives queries and keys
+ * d columns and values d_v columns, which need not be equal. Here d = D and
+ * d_v = Dv, each 64 or 128 (else ATTN_ERR_UNSUPPORTED_D), in any combination:
+ *   q, dq   [B][Hq][S][D]     k, dk   [B][Hkv][S][D]
+ *   o, dout [B][Hq][S][Dv]    v, dv   [B][Hkv][S][Dv]      lse [B][Hq][S]
+ * causal and window combine as in the entry points above: window = 0 means no
+ * window; window >= 1 needs causal != 0 (else, or for window < 0,
+ * ATTN_ERR_WINDOW). Scores are q . k over D columns, so the usual scale is
+ * 1/sqrt(D). attn_bwd_vdim's workspace is attn_bwd_workspace_bytes(B, Hq, Hkv,
+ * S, D, causal) bytes (delta has one value per query row whatever Dv is), and it
+ * needs o and lse from attn_fwd_vdim with the same arguments. With Dv == D these
+ * are attn_fwd / attn_bwd (window = 0) and attn_fwd_window / attn_bwd_window.
+ * Every other rule, layout and error is that of attn_fwd and attn_bwd, with
+ * B*Hq*S*max(D, Dv) < 2^40.
+ */
+int attn_fwd_vdim(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int S, int D, int Dv, int causal, int window,
+                  float scale, void* stream);
+int attn_bwd_vdim(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, float* dq, float* dk, float* dv,
+                  int B, int Hq, int Hkv, int S, int D, int Dv, int causal, int window,
+                  float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

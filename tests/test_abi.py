@@ -142,6 +142,39 @@ def test_window_validates_like_the_plain_entry_points():
     assert bwd_window(S=0) == fa.ATTN_ERR_SHAPE
 
 
+def fwd_vdim(*, window=0, causal=1, o=P, B=1, Hq=4, Hkv=2, S=128, D=128, Dv=64, scale=0.088):
+    return fa.load_library().attn_fwd_vdim(P, P, P, o, P, B, Hq, Hkv, S, D, Dv, causal, window, scale, None)
+
+
+def bwd_vdim(*, window=0, causal=1, dv=P, B=1, Hq=4, Hkv=2, S=128, D=128, Dv=64, scale=0.088, wsb=None):
+    lib = fa.load_library()
+    if wsb is None:
+        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal)
+    return lib.attn_bwd_vdim(P, P, P, P, P, P, P, P, dv, B, Hq, Hkv, S, D, Dv, causal, window, scale, P, wsb,
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Dv=96), fa.ATTN_ERR_UNSUPPORTED_D), (dict(Dv=256), fa.ATTN_ERR_UNSUPPORTED_D),
+    (dict(D=192), fa.ATTN_ERR_UNSUPPORTED_D), (dict(Dv=0), fa.ATTN_ERR_SHAPE),
+    (dict(window=-1), fa.ATTN_ERR_WINDOW), (dict(window=8, causal=0), fa.ATTN_ERR_WINDOW),
+    (dict(Hq=6, Hkv=4), fa.ATTN_ERR_GQA), (dict(scale=math.nan), fa.ATTN_ERR_SCALE),
+    # the size limit counts the wider of the two head dimensions
+    (dict(B=1 << 19, Hq=1 << 10, Hkv=1 << 10, S=1 << 12, D=64, Dv=128), fa.ATTN_ERR_SHAPE),
+])
+def test_vdim_rejects(kw, code):
+    assert fwd_vdim(**kw) == code
+    assert bwd_vdim(**kw) == code
+
+
+def test_vdim_validates_pointers_and_workspace():
+    assert fwd_vdim(o=None) == fa.ATTN_ERR_NULL
+    assert fwd_vdim(o=MIS) == fa.ATTN_ERR_ALIGN
+    assert bwd_vdim(dv=None) == fa.ATTN_ERR_NULL
+    assert bwd_vdim(dv=MIS) == fa.ATTN_ERR_ALIGN
+    assert bwd_vdim(wsb=16) == fa.ATTN_ERR_WORKSPACE
+
+
 def test_no_gpu_reports_hip_error():
     """Valid arguments on a machine without a usable gfx950 device end in a HIP or device
     error from the set-up step, never in a launch."""
@@ -150,3 +183,5 @@ def test_no_gpu_reports_hip_error():
         pytest.skip("a GPU is present")
     assert fwd() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
     assert fwd_window() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
+    assert fwd_vdim() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
+    assert fwd_vdim(D=64, Dv=128, window=16) in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)

@@ -24,9 +24,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # kernels (mangled-name fragments) whose tile loops must be clean: every instance the
 # benchmarked workloads launch
 HOT = {
-    "attn_fwd.hip": ["fwd_kernelILi128ELb1E", "fwd_kernelILi64ELb0E", "fwd_kernelILi64ELb1E"],
-    "attn_bwd.hip": ["dq_kernelILi128ELb1E", "dq_kernelILi128ELb0E", "dkv_kernelILi128ELb1E",
-                     "dkv_kernelILi128ELb0E", "dq_kernelILi64ELb0E", "dkv_kernelILi64ELb0E"],
+    "attn_fwd.hip": ["fwd_kernelILi128ELi128ELb1E", "fwd_kernelILi64ELi64ELb0E", "fwd_kernelILi64ELi64ELb1E",
+                     "fwd_kernelILi128ELi64ELb1E"],
+    "attn_bwd.hip": ["dq_kernelILi128ELi128ELb1E", "dq_kernelILi128ELi128ELb0E", "dkv_kernelILi128ELi128ELb1E",
+                     "dkv_kernelILi128ELi128ELb0E", "dq_kernelILi64ELi64ELb0E", "dkv_kernelILi64ELi64ELb0E",
+                     "dq_kernelILi128ELi64ELb1E", "dkv_kernelILi128ELi64ELb1E"],
 }
 
 
