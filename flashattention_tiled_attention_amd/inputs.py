@@ -41,6 +41,43 @@ def qkv(B, Hq, Hkv, S, D, seed=0, with_dout=False, Dv=None):
     return q, k, v, dout
 
 
+def sparse_qkv(B, Hq, Hkv, S, N, D, seed=0, with_dout=False):
+    """Q [B,Hq,S,D], K and V [B,Hkv,N,D] over N key/value rows (and dO like Q), as bf16
+    bits, iid N(0,1), drawn in the order Q, K, V, dO."""
+    rng = np.random.default_rng(seed)
+    q = bf16_bits(rng.standard_normal((B, Hq, S, D), dtype=np.float32))
+    k = bf16_bits(rng.standard_normal((B, Hkv, N, D), dtype=np.float32))
+    v = bf16_bits(rng.standard_normal((B, Hkv, N, D), dtype=np.float32))
+    if not with_dout:
+        return q, k, v
+    dout = bf16_bits(rng.standard_normal((B, Hq, S, D), dtype=np.float32))
+    return q, k, v, dout
+
+
+def csa_index_lists(B, S, window, ratio, pool_topk, seed=0):
+    """Per-token key/value row lists shaped like the compressed sparse attention of
+    Table 7 (window + top-k of a compressed pool), with random picks standing in for a
+    trained indexer. Rows 0..S-1 are the raw tokens, rows S .. S + S//ratio - 1 the
+    pool. Token i lists its window rows max(0, i-window+1) .. i in ascending order, then
+    min(pool_topk, P_i) pool rows drawn uniformly without replacement (in draw order)
+    from the P_i = (i+1)//ratio pool rows whose block of `ratio` tokens ends at or
+    before i; unused slots are -1. Returns (idx int32 [B][S][window+pool_topk], N)."""
+    rng = np.random.default_rng(seed)
+    npool = S // ratio if ratio else 0
+    topk = window + (pool_topk if ratio else 0)
+    idx = np.full((B, S, topk), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(S):
+            w0 = max(0, i - window + 1)
+            idx[b, i, :i - w0 + 1] = np.arange(w0, i + 1, dtype=np.int32)
+            if ratio:
+                vis = min((i + 1) // ratio, npool)
+                m = min(pool_topk, vis)
+                if m:
+                    idx[b, i, window:window + m] = S + rng.choice(vis, size=m, replace=False)
+    return idx, S + npool
+
+
 # The workloads the benchmark and the parity tests run: (name, B, Hq, Hkv, S, D, causal, pass;
 # optional window and value head dimension Dv, which defaults to D).
 CONFIGS = {
@@ -53,4 +90,9 @@ CONFIGS = {
     "llama8b_window128_s4096": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, causal=True, window=128, bwd=True),
     # value head dimension d_v != d (Eq. 1): 128-wide queries/keys, 64-wide values
     "gqa_dqk128_dv64_s4096": dict(B=1, Hq=32, Hkv=8, S=4096, D=128, Dv=64, causal=True, bwd=True),
+    # index-gather sparse attention in the cr4 shape of the compressed sparse attention
+    # (Table 7, "Flash" family: 64 heads, top-k 640 = 128-token window + top-512 of S/4
+    # pool rows), one K/V head shared by all query heads, synthetic lists
+    "csa_cr4_flash_s4096": dict(B=1, Hq=64, Hkv=1, S=4096, D=128, causal=False, sparse=True, window=128,
+                                ratio=4, pool_topk=512, bwd=True),
 }

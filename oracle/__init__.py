@@ -74,8 +74,11 @@ class Oracle:
         lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, Dbl]
         lib.oracle_attn_bwd_rows.argtypes = [P, P, P, P, P, I64, P, P, I64, P, P,
                                              I, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_sparse_fwd_rows.argtypes = [P, P, P, P, P, I64, P, P, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_sparse_bwd_rows.argtypes = [P, P, P, P, P, P, I64, P, P, I64, P, P,
+                                               I, I, I, I, I, I, I, Dbl]
         for f in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_attn_bwd,
-                  lib.oracle_attn_bwd_rows):
+                  lib.oracle_attn_bwd_rows, lib.oracle_sparse_fwd_rows, lib.oracle_sparse_bwd_rows):
             f.restype = I
         self.lib = lib
         self.path = path
@@ -139,6 +142,79 @@ class Oracle:
         return dq, dk, dv
 
 
+    # ------------------------------------------------------------ sparse attention
+
+    def sparse_fwd(self, q, k, v, idx, scale, rows=None):
+        """Attention over per-token index lists. q [B,Hq,S,D]; k, v [B,Hkv,N,D]; idx
+        [B,S,topk] int32 (entries outside [0, N) are empty slots). O [B,Hq,S,D] and lse
+        [B,Hq,S] (-inf for a token with no non-empty slot), or, with rows (flat query rows
+        (b*Hq + hq)*S + i), O [n,D] and lse [n]."""
+        B, Hq, Hkv, S, N, D, topk = _sparse_shapes(q, k, v, idx)
+        if rows is None:
+            o = np.empty((B, Hq, S, D), np.float64)
+            lse = np.empty((B, Hq, S), np.float64)
+            rp, n = None, 0
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            o = np.empty((rows.size, D), np.float64)
+            lse = np.empty((rows.size,), np.float64)
+            rp, n = _ptr(rows), rows.size
+        rc = self.lib.oracle_sparse_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), rp, n, _ptr(o), _ptr(lse),
+                                             B, Hq, Hkv, S, N, D, topk, float(scale))
+        if rc:
+            raise ValueError("oracle_sparse_fwd_rows failed: %d" % rc)
+        return o, lse
+
+    def sparse_bwd(self, q, k, v, dout, idx, scale, qrows=None, kvrows=None):
+        """Gradients of sparse_fwd: dQ [B,Hq,S,D], dK and dV [B,Hkv,N,D] (summed over every
+        (token, slot) that names the row and over the group's heads); with qrows / kvrows
+        (flat (b*Hkv + hkv)*N + j), only those rows, as [n,D] arrays."""
+        B, Hq, Hkv, S, N, D, topk = _sparse_shapes(q, k, v, idx, dout)
+        if qrows is None:
+            dq = np.empty((B, Hq, S, D), np.float64)
+            qp, nq = None, 0
+        else:
+            qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+            dq = np.empty((qrows.size, D), np.float64)
+            qp, nq = _ptr(qrows), qrows.size
+        if kvrows is None:
+            dk = np.empty((B, Hkv, N, D), np.float64)
+            dv = np.empty((B, Hkv, N, D), np.float64)
+            kp, nkv = None, 0
+        else:
+            kvrows = np.ascontiguousarray(kvrows, dtype=np.int64)
+            dk = np.empty((kvrows.size, D), np.float64)
+            dv = np.empty((kvrows.size, D), np.float64)
+            kp, nkv = _ptr(kvrows), kvrows.size
+        rc = self.lib.oracle_sparse_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(idx), qp, nq,
+                                             _ptr(dq), kp, nkv, _ptr(dk), _ptr(dv), B, Hq, Hkv, S, N, D, topk,
+                                             float(scale))
+        if rc:
+            raise ValueError("oracle_sparse_bwd_rows failed: %d" % rc)
+        return dq, dk, dv
+
+
+def _sparse_shapes(q, k, v, idx, dout=None):
+    for name, a in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        if a is None:
+            continue
+        if a.dtype != np.uint16 or a.ndim != 4 or not a.flags.c_contiguous:
+            raise ValueError("%s must be a C-contiguous uint16 array of bf16 bits" % name)
+    if idx.dtype != np.int32 or idx.ndim != 3 or not idx.flags.c_contiguous:
+        raise ValueError("idx must be a C-contiguous int32 [B][S][topk] array")
+    B, Hq, S, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, N, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B][Hkv][N][D]")
+    if idx.shape[:2] != (B, S):
+        raise ValueError("idx must be [B][S][topk]")
+    if dout is not None and dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, S, N, D, idx.shape[2]
+
+
 _default = None
 
 
@@ -170,3 +246,11 @@ def bwd(q, k, v, dout, causal, scale, window=0):
 
 def bwd_rows(q, k, v, dout, qrows, kvrows, causal, scale, window=0):
     return default().bwd_rows(q, k, v, dout, qrows, kvrows, causal, scale, window)
+
+
+def sparse_fwd(q, k, v, idx, scale, rows=None):
+    return default().sparse_fwd(q, k, v, idx, scale, rows)
+
+
+def sparse_bwd(q, k, v, dout, idx, scale, qrows=None, kvrows=None):
+    return default().sparse_bwd(q, k, v, dout, idx, scale, qrows, kvrows)

@@ -336,3 +336,281 @@ int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
     free(delta);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------
+ * Sparse attention over per-token index lists.
+ *
+ * The page's compressed sparse attention (section 2.1; Table 7 for its shapes)
+ * gives every query token a top-k list of key/value row indices: a sliding
+ * window of recent tokens plus rows of a compressed pool. The forward gathers
+ * the listed rows, scores them and streams their values into the output; the
+ * backward gathers the same rows for dQ, forms one dK/dV contribution per
+ * (token, list slot) and reduces those by the inverse of the index map.
+ * Readings of the page where it is silent:
+ *   - idx is [B][S][topk] int32, shared by every query head of a token; entry s
+ *     of token i names row idx[b][i][s] of the N key/value rows of each K/V head
+ *     (k, v: [B][Hkv][N][D]); an entry outside [0, N) is an empty slot;
+ *   - attention runs over slots: Eq. (1) with the scores of token i's non-empty
+ *     slots, so a row listed twice counts twice; the lists carry any causal or
+ *     window structure, nothing else masks;
+ *   - a token with no non-empty slot gets O = 0, lse = -inf, dQ = 0 and adds
+ *     nothing to dK/dV;
+ *   - query heads map to K/V heads as in the dense functions (hq / (Hq/Hkv)).
+ * -------------------------------------------------------------------------- */
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    const int32_t* idx;
+    int B, Hq, Hkv, S, N, D, G, topk;
+    double scale;
+} sctx_t;
+
+static int check_sparse(int B, int Hq, int Hkv, int S, int N, int D, int topk) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || N <= 0 || D <= 0 || topk <= 0) return -1;
+    if (Hq % Hkv != 0) return -2;
+    return 0;
+}
+
+/* Key/value row of slot s of token i, or -1 for an empty slot. */
+static int slot_row(const sctx_t* c, int b, int i, int s) {
+    const int32_t j = c->idx[((size_t)b * c->S + i) * c->topk + s];
+    return (j >= 0 && j < c->N) ? (int)j : -1;
+}
+
+static const uint16_t* sq_row(const sctx_t* c, const uint16_t* base, int b, int hq, int i) {
+    return base + (((size_t)b * c->Hq + hq) * c->S + i) * (size_t)c->D;
+}
+static const uint16_t* skv_row(const sctx_t* c, const uint16_t* base, int b, int hkv, int j) {
+    return base + (((size_t)b * c->Hkv + hkv) * c->N + j) * (size_t)c->D;
+}
+
+/*
+ * One query row over its token's slots: p[s] = softmax_s(scale q_i . k_idx[s]) on
+ * non-empty slots (0 on empty ones), optionally O_i, lse_i, and with dout the
+ * backward quantities dP_s = dO_i . v_idx[s], delta_i = sum_s p_s dP_s and
+ * dQ_i = scale sum_s p_s (dP_s - delta_i) k_idx[s]. p and dp: caller scratch of
+ * length topk. Returns the number of non-empty slots.
+ */
+static int sparse_row(const sctx_t* c, int b, int hq, int i, double* p, double* dp, double* o_out,
+                      double* lse_out, double* delta_out, double* dq_out) {
+    const int D = c->D, hkv = hq / c->G;
+    const uint16_t* qi = sq_row(c, c->q, b, hq, i);
+    double m = -INFINITY;
+    int n = 0;
+    for (int s = 0; s < c->topk; ++s) {
+        const int j = slot_row(c, b, i, s);
+        if (j < 0) { p[s] = 0.0; continue; }
+        p[s] = c->scale * dot_bf16(qi, skv_row(c, c->k, b, hkv, j), D);
+        if (p[s] > m) m = p[s];
+        ++n;
+    }
+    if (o_out) for (int d = 0; d < D; ++d) o_out[d] = 0.0;
+    if (dq_out) for (int d = 0; d < D; ++d) dq_out[d] = 0.0;
+    if (n == 0) {
+        if (lse_out) *lse_out = -INFINITY;
+        if (delta_out) *delta_out = 0.0;
+        return 0;
+    }
+    double l = 0.0;
+    for (int s = 0; s < c->topk; ++s) {
+        if (slot_row(c, b, i, s) < 0) continue;
+        p[s] = exp(p[s] - m);
+        l += p[s];
+    }
+    for (int s = 0; s < c->topk; ++s)
+        if (slot_row(c, b, i, s) >= 0) p[s] /= l;
+    if (lse_out) *lse_out = m + log(l);
+    if (o_out) {
+        for (int s = 0; s < c->topk; ++s) {
+            const int j = slot_row(c, b, i, s);
+            if (j < 0) continue;
+            const uint16_t* vj = skv_row(c, c->v, b, hkv, j);
+            for (int d = 0; d < D; ++d) o_out[d] += p[s] * widen(vj[d]);
+        }
+    }
+    if (c->dout && (delta_out || dq_out)) {
+        const uint16_t* doi = sq_row(c, c->dout, b, hq, i);
+        double delta = 0.0;
+        for (int s = 0; s < c->topk; ++s) {
+            const int j = slot_row(c, b, i, s);
+            if (j < 0) { dp[s] = 0.0; continue; }
+            dp[s] = dot_bf16(doi, skv_row(c, c->v, b, hkv, j), D);
+            delta += p[s] * dp[s];
+        }
+        if (delta_out) *delta_out = delta;
+        if (dq_out) {
+            for (int s = 0; s < c->topk; ++s) {
+                const int j = slot_row(c, b, i, s);
+                if (j < 0) continue;
+                const double ds = p[s] * (dp[s] - delta);
+                const uint16_t* kj = skv_row(c, c->k, b, hkv, j);
+                for (int d = 0; d < D; ++d) dq_out[d] += c->scale * ds * widen(kj[d]);
+            }
+        }
+    }
+    return n;
+}
+
+static void init_sctx(sctx_t* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dout, const int32_t* idx, int B, int Hq, int Hkv, int S,
+                      int N, int D, int topk, double scale) {
+    c->q = q; c->k = k; c->v = v; c->dout = dout; c->idx = idx;
+    c->B = B; c->Hq = Hq; c->Hkv = Hkv; c->S = S; c->N = N; c->D = D; c->G = Hq / Hkv;
+    c->topk = topk;
+    c->scale = scale;
+}
+
+/* Sparse forward for the flat query rows rows[0..n) ((b*Hq + hq)*S + i), or for
+ * every row when rows is NULL: o [n][D] (or [B][Hq][S][D]), lse [n]. */
+int oracle_sparse_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* idx, const int64_t* rows, int64_t n, double* o,
+                           double* lse, int B, int Hq, int Hkv, int S, int N, int D, int topk,
+                           double scale) {
+    int rc = check_sparse(B, Hq, Hkv, S, N, D, topk);
+    if (rc) return rc;
+    if (!rows) n = (int64_t)B * Hq * S;
+    for (int64_t t = 0; rows && t < n; ++t)
+        if (rows[t] < 0 || rows[t] >= (int64_t)B * Hq * S) return -3;
+    sctx_t c;
+    init_sctx(&c, q, k, v, NULL, idx, B, Hq, Hkv, S, N, D, topk, scale);
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)topk);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < n; ++t) {
+            const int64_t r = rows ? rows[t] : t;
+            const int i = (int)(r % S), bh = (int)(r / S);
+            sparse_row(&c, bh / Hq, bh % Hq, i, p, NULL, o + (size_t)t * D, lse + t, NULL, NULL);
+        }
+        free(p);
+    }
+    return 0;
+}
+
+/* Per-row lse and delta of every query row: [B][Hq][S] each. */
+static void sparse_row_stats(const sctx_t* c, double* lse, double* delta) {
+    const long long rows = (long long)c->B * c->Hq * c->S;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)c->topk);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)c->topk);
+#pragma omp for schedule(dynamic, 16)
+        for (long long r = 0; r < rows; ++r) {
+            const int i = (int)(r % c->S), bh = (int)(r / c->S);
+            sparse_row(c, bh / c->Hq, bh % c->Hq, i, p, dp, NULL, lse + r, delta + r, NULL);
+        }
+        free(p);
+        free(dp);
+    }
+}
+
+/*
+ * dK and dV of key/value row j of head group (b, hkv): the contributions of every
+ * (token i, slot s) whose entry names row j, taken in token order through the
+ * inverse of the index map (ent[0..ne): flat i*topk + s of batch b), each summed
+ * over the group's query heads:
+ *   P = exp(scale q.k_j - lse),  dV_j += P dO,  dK_j += scale P (dO.v_j - delta) q.
+ */
+static void sparse_key(const sctx_t* c, int b, int hkv, int j, const int64_t* ent, int64_t ne,
+                       const double* lse, const double* delta, double* dk_out, double* dv_out) {
+    const int D = c->D, S = c->S;
+    const uint16_t* kj = skv_row(c, c->k, b, hkv, j);
+    const uint16_t* vj = skv_row(c, c->v, b, hkv, j);
+    for (int d = 0; d < D; ++d) { dk_out[d] = 0.0; dv_out[d] = 0.0; }
+    for (int64_t e = 0; e < ne; ++e) {
+        const int i = (int)(ent[e] / c->topk);
+        for (int g = 0; g < c->G; ++g) {
+            const int hq = hkv * c->G + g;
+            const size_t r = ((size_t)b * c->Hq + hq) * S + i;
+            const uint16_t* qi = sq_row(c, c->q, b, hq, i);
+            const uint16_t* doi = sq_row(c, c->dout, b, hq, i);
+            const double pij = exp(c->scale * dot_bf16(qi, kj, D) - lse[r]);
+            const double ds = pij * (dot_bf16(doi, vj, D) - delta[r]);
+            for (int d = 0; d < D; ++d) {
+                dv_out[d] += pij * widen(doi[d]);
+                dk_out[d] += c->scale * ds * widen(qi[d]);
+            }
+        }
+    }
+}
+
+/* Inverse of batch b's index map: for each row j, the entries naming it, in
+ * increasing flat order i*topk + s. start [N+1], ent [count of non-empty slots]. */
+static int64_t* invert_map(const sctx_t* c, int b, int64_t* start) {
+    const int N = c->N;
+    for (int j = 0; j <= N; ++j) start[j] = 0;
+    for (int64_t e = 0; e < (int64_t)c->S * c->topk; ++e) {
+        const int j = slot_row(c, b, (int)(e / c->topk), (int)(e % c->topk));
+        if (j >= 0) start[j + 1]++;
+    }
+    for (int j = 0; j < N; ++j) start[j + 1] += start[j];
+    int64_t* ent = (int64_t*)malloc(sizeof(int64_t) * (size_t)(start[N] > 0 ? start[N] : 1));
+    int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (!ent || !fill) { free(ent); free(fill); return NULL; }
+    for (int j = 0; j < N; ++j) fill[j] = start[j];
+    for (int64_t e = 0; e < (int64_t)c->S * c->topk; ++e) {
+        const int j = slot_row(c, b, (int)(e / c->topk), (int)(e % c->topk));
+        if (j >= 0) ent[fill[j]++] = e;
+    }
+    free(fill);
+    return ent;
+}
+
+/*
+ * Sparse backward. dq_rows gets dQ of the flat query rows qrows[0..nq) (every
+ * row, [B][Hq][S][D], when qrows is NULL); dk_rows, dv_rows get dK, dV of the flat
+ * key/value rows kvrows[0..nkv) ((b*Hkv + hkv)*N + j; every row, [B][Hkv][N][D],
+ * when kvrows is NULL). Every query row's lse and delta are computed first.
+ */
+int oracle_sparse_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* dout, const int32_t* idx, const int64_t* qrows,
+                           int64_t nq, double* dq_rows, const int64_t* kvrows, int64_t nkv,
+                           double* dk_rows, double* dv_rows, int B, int Hq, int Hkv, int S,
+                           int N, int D, int topk, double scale) {
+    int rc = check_sparse(B, Hq, Hkv, S, N, D, topk);
+    if (rc) return rc;
+    if (!qrows) nq = (int64_t)B * Hq * S;
+    if (!kvrows) nkv = (int64_t)B * Hkv * N;
+    for (int64_t t = 0; qrows && t < nq; ++t)
+        if (qrows[t] < 0 || qrows[t] >= (int64_t)B * Hq * S) return -3;
+    for (int64_t t = 0; kvrows && t < nkv; ++t)
+        if (kvrows[t] < 0 || kvrows[t] >= (int64_t)B * Hkv * N) return -3;
+    sctx_t c;
+    init_sctx(&c, q, k, v, dout, idx, B, Hq, Hkv, S, N, D, topk, scale);
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)topk);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)topk);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < nq; ++t) {
+            const int64_t r = qrows ? qrows[t] : t;
+            const int i = (int)(r % S), bh = (int)(r / S);
+            sparse_row(&c, bh / Hq, bh % Hq, i, p, dp, NULL, NULL, NULL, dq_rows + (size_t)t * D);
+        }
+        free(p);
+        free(dp);
+    }
+    if (nkv == 0) return 0;
+    const size_t nrows = (size_t)B * Hq * S;
+    double* lse = (double*)malloc(sizeof(double) * nrows);
+    double* delta = (double*)malloc(sizeof(double) * nrows);
+    int64_t* start = (int64_t*)malloc(sizeof(int64_t) * ((size_t)N + 1));
+    if (!lse || !delta || !start) { free(lse); free(delta); free(start); return -4; }
+    sparse_row_stats(&c, lse, delta);
+    for (int b = 0; b < B; ++b) {
+        int64_t* ent = invert_map(&c, b, start);
+        if (!ent) { free(lse); free(delta); free(start); return -4; }
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t t = 0; t < nkv; ++t) {
+            const int64_t r = kvrows ? kvrows[t] : t;
+            const int j = (int)(r % N), bh = (int)(r / N);
+            if (bh / Hkv != b) continue;
+            sparse_key(&c, b, bh % Hkv, j, ent + start[j], start[j + 1] - start[j], lse, delta,
+                       dk_rows + (size_t)t * D, dv_rows + (size_t)t * D);
+        }
+        free(ent);
+    }
+    free(lse);
+    free(delta);
+    free(start);
+    return 0;
+}

@@ -5,7 +5,8 @@ when the oracle disagrees with the fact. The facts come from section 2.1 of
 Rao et al., "Scheduling Data to Compute: Hierarchical Data Pipelining for LLM
 Training on AMD GPUs" (Eq. (1): O = softmax(Q K^T / sqrt(d)) V), the sliding
 window of its Table 7 (query i sees the keys i-W+1 .. i), the separate value
-width d_v that Eq. (1) allows, and from
+width d_v that Eq. (1) allows, the per-token index lists of its compressed sparse
+attention (section 2.1, Table 7), and from
 mathematics: an independent brute force on tiny inputs, closed forms,
 invariants, torch's float64 CPU attention and autograd as a library routine,
 and central finite differences for the gradient.
@@ -18,7 +19,7 @@ import math
 import numpy as np
 import torch
 
-from flashattention_tiled_attention_amd.inputs import bf16_bits, bf16_to_f32, qkv
+from flashattention_tiled_attention_amd.inputs import bf16_bits, bf16_to_f32, qkv, sparse_qkv
 
 
 def _f64(bits):
@@ -467,10 +468,212 @@ def pin_value_dim(orc):
     _fd_check(orc, 1, 2, 1, 5, 3, 2, True, 0.6, 49, window=2)
 
 
+# ------------------------------------------------ sparse (index-list) attention
+
+def _lists(S, causal=True, window=0, holes=0, seed=None):
+    """idx [1,S,topk] naming each visible key of a dense pattern in ascending order,
+    with `holes` empty slots (-1) scattered among them when seed is given."""
+    rows = [list(_visible(causal, S, i, window)) for i in range(S)]
+    if seed is not None:
+        rng = np.random.default_rng(seed)
+        for r in rows:
+            for _ in range(holes):
+                r.insert(int(rng.integers(0, len(r) + 1)), -1)
+    topk = max(len(r) for r in rows)
+    idx = np.full((1, S, topk), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        idx[0, i, :len(r)] = r
+    return idx
+
+
+def _sparse_brute(q, k, v, idx, scale):
+    """Slot-by-slot pure-Python evaluation: softmax over a token's non-empty slots."""
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    B, Hq, S, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, S, D))
+    lse = np.full((B, Hq, S), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                js = [int(j) for j in idx[b, i] if 0 <= j < N]
+                if not js:
+                    continue
+                e = [math.exp(scale * math.fsum(qf[b, h, i, d] * kf[b, h // G, j, d] for d in range(D)))
+                     for j in js]
+                z = math.fsum(e)
+                lse[b, h, i] = math.log(z)
+                for d in range(D):
+                    o[b, h, i, d] = math.fsum(e[t] / z * vf[b, h // G, j, d] for t, j in enumerate(js))
+    return o, lse
+
+
+def _sparse_loss_py(qf, kf, vf, dof, idx, scale, G):
+    """L = sum(O * dO) of slot-wise sparse attention, pure Python out."""
+    B, Hq, S, D = qf.shape
+    N = kf.shape[2]
+    total = []
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                js = [int(j) for j in idx[b, i] if 0 <= j < N]
+                if not js:
+                    continue
+                sc = [scale * float(np.dot(qf[b, h, i], kf[b, h // G, j])) for j in js]
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                z = math.fsum(e)
+                for t, j in enumerate(js):
+                    total.append(e[t] / z * float(np.dot(vf[b, h // G, j], dof[b, h, i])))
+    return math.fsum(total)
+
+
+def pin_sparse_matches_dense(orc):
+    """Lists naming exactly the keys a dense pattern shows (causal, sliding window or all,
+    with empty slots scattered in) give the dense oracle's O, lse, dQ, dK and dV."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 13, 8
+    q, k, v, do = qkv(B, Hq, Hkv, S, D, 50, with_dout=True)
+    for causal, window, holes in ((True, 0, 0), (False, 0, 2), (True, 4, 3), (True, 1, 1)):
+        idx = _lists(S, causal, window, holes, seed=51 if holes else None)
+        o, lse = orc.sparse_fwd(q, k, v, idx, 0.4)
+        od, ld = orc.fwd(q, k, v, causal, 0.4, window)
+        _close(o, od, 1e-13, "sparse vs dense O %s" % ((causal, window, holes),))
+        _close(lse, ld, 1e-13, "sparse vs dense lse")
+        dq, dk, dv = orc.sparse_bwd(q, k, v, do, idx, 0.4)
+        rq, rk, rv = orc.bwd(q, k, v, do, causal, 0.4, window)
+        _close(dq, rq, 1e-13, "sparse vs dense dQ")
+        _close(dk, rk, 1e-13, "sparse vs dense dK")
+        _close(dv, rv, 1e-13, "sparse vs dense dV")
+
+
+def pin_sparse_torch(orc):
+    """Random duplicate-free lists over N != S rows equal torch float64 attention (and
+    autograd) with the lists passed as a boolean [S, N] mask."""
+    B, Hq, Hkv, S, N, D = 2, 4, 2, 11, 17, 8
+    rng = np.random.default_rng(52)
+    q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, 53, with_dout=True)
+    topk = 7
+    idx = np.full((B, S, topk), -1, dtype=np.int32)
+    mask = np.zeros((B, 1, S, N), dtype=bool)
+    for b in range(B):
+        for i in range(S):
+            m = int(rng.integers(1, topk + 1))
+            js = rng.choice(N, size=m, replace=False)
+            slots = rng.choice(topk, size=m, replace=False)
+            idx[b, i, slots] = js
+            mask[b, 0, i, js] = True
+    tq = torch.from_numpy(_f64(q)).requires_grad_(True)
+    tk = torch.from_numpy(_f64(k)).requires_grad_(True)
+    tv = torch.from_numpy(_f64(v)).requires_grad_(True)
+    ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask),
+                                                          scale=0.3, enable_gqa=True)
+    ot.backward(torch.from_numpy(_f64(do)))
+    o, _ = orc.sparse_fwd(q, k, v, idx, 0.3)
+    dq, dk, dv = orc.sparse_bwd(q, k, v, do, idx, 0.3)
+    _close(o, ot.detach().numpy(), 1e-12, "sparse O vs torch masked sdpa")
+    _close(dq, tq.grad.numpy(), 1e-12, "sparse dQ vs torch autograd")
+    _close(dk, tk.grad.numpy(), 1e-12, "sparse dK vs torch autograd")
+    _close(dv, tv.grad.numpy(), 1e-12, "sparse dV vs torch autograd")
+
+
+def pin_sparse_brute_force(orc):
+    """Pure-Python slot-wise evaluation on tiny shapes, with rows listed twice, empty
+    slots, out-of-range entries and a token whose list is empty."""
+    B, Hq, Hkv, S, N, D = 1, 4, 2, 6, 9, 5
+    q, k, v = sparse_qkv(B, Hq, Hkv, S, N, D, 54)
+    idx = np.array([[[3, -1, 3, 8], [-1, -1, -1, -1], [0, 1, 2, 9], [8, 7, 6, 5],
+                     [4, -7, 4, 4], [2, 2, 100, 0]]], dtype=np.int32)
+    o, lse = orc.sparse_fwd(q, k, v, idx, 0.6)
+    ob, lb = _sparse_brute(q, k, v, idx, 0.6)
+    _close(o, ob, 1e-12, "sparse O vs brute force")
+    assert np.array_equal(np.isinf(lse), np.isinf(lb)), "sparse lse -inf pattern"
+    fin = np.isfinite(lb)
+    _close(lse[fin], lb[fin], 1e-12, "sparse lse vs brute force")
+
+
+def pin_sparse_closed_forms(orc):
+    """Empty list: O = 0, lse = -inf, dQ = 0. One non-empty slot: O = V_j,
+    lse = scale q.k_j, dQ = 0. A row listed twice where it stands alone: same O, lse
+    larger by ln 2. Permuting a token's slots changes nothing. Rows no list names get
+    dK = dV = 0."""
+    B, Hq, Hkv, S, N, D = 1, 2, 1, 4, 6, 8
+    q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, 55, with_dout=True)
+    idx = np.array([[[-1, -1, -1], [4, -1, -1], [-1, 2, 2], [1, 3, 0]]], dtype=np.int32)
+    o, lse = orc.sparse_fwd(q, k, v, idx, 0.5)
+    dq, dk, dv = orc.sparse_bwd(q, k, v, do, idx, 0.5)
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    _close(o[0, :, 0], np.zeros((Hq, D)), 0.0, "empty list O")
+    assert np.all(np.isneginf(lse[0, :, 0])), "empty list lse"
+    _close(dq[0, :, 0], np.zeros((Hq, D)), 0.0, "empty list dQ")
+    _close(o[0, :, 1], np.broadcast_to(vf[0, 0, 4], (Hq, D)), 1e-15, "single slot O")
+    _close(lse[0, :, 1], 0.5 * qf[0, :, 1] @ kf[0, 0, 4], 1e-13, "single slot lse")
+    _close(dq[0, :, 1], np.zeros((Hq, D)), 1e-14, "single slot dQ")
+    _close(o[0, :, 2], np.broadcast_to(vf[0, 0, 2], (Hq, D)), 1e-15, "doubled slot O")
+    _close(lse[0, :, 2], 0.5 * qf[0, :, 2] @ kf[0, 0, 2] + math.log(2.0), 1e-13, "doubled slot lse")
+    _close(dk[0, 0, 5], np.zeros(D), 0.0, "unnamed row dK")
+    _close(dv[0, 0, 5], np.zeros(D), 0.0, "unnamed row dV")
+    perm = idx.copy()
+    perm[0, 3] = [0, 1, 3]
+    o2, l2 = orc.sparse_fwd(q, k, v, perm, 0.5)
+    g2 = orc.sparse_bwd(q, k, v, do, perm, 0.5)
+    _close(o2, o, 1e-14, "slot permutation O")
+    assert np.array_equal(np.isneginf(l2), np.isneginf(lse)), "slot permutation lse -inf pattern"
+    _close(l2[np.isfinite(lse)], lse[np.isfinite(lse)], 1e-14, "slot permutation lse")
+    for a, b_, n in zip(g2, (dq, dk, dv), ("dQ", "dK", "dV")):
+        _close(a, b_, 1e-14, "slot permutation " + n)
+
+
+def pin_sparse_gradients(orc):
+    """Central differences of L = sum(O * dO) (pure-Python slot-wise forward) match the
+    gradients, with duplicates and an empty list; rows of P sum to 1 and rows of dS to
+    0, so sum_j dV_j = sum of dO over tokens with a non-empty list and sum_j dK_j = 0;
+    the sampled-row forms agree with the full ones."""
+    h = 1e-6
+    B, Hq, Hkv, S, N, D = 1, 2, 1, 4, 5, 3
+    q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, 56, with_dout=True)
+    idx = np.array([[[2, 2, 0], [-1, -1, -1], [4, 1, -1], [0, 3, 4]]], dtype=np.int32)
+    dq, dk, dv = orc.sparse_bwd(q, k, v, do, idx, 0.8)
+    base = [_f64(q), _f64(k), _f64(v)]
+    dof = _f64(do)
+    for which, grad in enumerate((dq, dk, dv)):
+        for ix in np.ndindex(*base[which].shape):
+            plus = [a.copy() for a in base]
+            minus = [a.copy() for a in base]
+            plus[which][ix] += h
+            minus[which][ix] -= h
+            fd = (_sparse_loss_py(*plus, dof, idx, 0.8, Hq // Hkv)
+                  - _sparse_loss_py(*minus, dof, idx, 0.8, Hq // Hkv)) / (2 * h)
+            assert abs(fd - grad[ix]) <= 1e-7 * max(1.0, abs(fd)), \
+                "sparse finite difference %s%s: fd %.9f analytic %.9f" % ("qkv"[which], ix, fd, grad[ix])
+    B, Hq, Hkv, S, N, D = 2, 4, 2, 9, 14, 8
+    q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, 57, with_dout=True)
+    rng = np.random.default_rng(58)
+    idx = rng.integers(-3, N, size=(B, S, 6)).astype(np.int32)
+    idx[0, 4] = -1
+    dq, dk, dv = orc.sparse_bwd(q, k, v, do, idx, 0.45)
+    live = (idx >= 0).any(axis=2)                                   # [B][S]
+    dof = _f64(do) * live[:, None, :, None]
+    _close(dv.sum(axis=2), dof.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=(2, 3)), 1e-12, "sparse sum dV")
+    _close(dk.sum(axis=2), np.zeros((B, Hkv, D)), 1e-12, "sparse sum dK")
+    rows = np.array([0, 4, 13, 40, 71])
+    kvr = np.array([0, 5, 13, 27, 30, 55])
+    o, lse = orc.sparse_fwd(q, k, v, idx, 0.45)
+    o_r, l_r = orc.sparse_fwd(q, k, v, idx, 0.45, rows=rows)
+    _close(o_r, o.reshape(-1, D)[rows], 0.0, "sparse fwd rows")
+    assert np.array_equal(l_r, lse.reshape(-1)[rows]), "sparse fwd rows lse"
+    dq_r, dk_r, dv_r = orc.sparse_bwd(q, k, v, do, idx, 0.45, qrows=rows, kvrows=kvr)
+    _close(dq_r, dq.reshape(-1, D)[rows], 0.0, "sparse dq rows")
+    _close(dk_r, dk.reshape(-1, D)[kvr], 0.0, "sparse dk rows")
+    _close(dv_r, dv.reshape(-1, D)[kvr], 0.0, "sparse dv rows")
+
+
 FORWARD_PINS = [pin_brute_force, pin_torch_sdpa, pin_single_key, pin_zero_query,
                 pin_causal_first_row, pin_permutation, pin_gqa_is_repeated_mha, pin_sharp_softmax,
                 pin_rows_match_full]
 BACKWARD_PINS = [pin_finite_differences, pin_torch_autograd, pin_backward_invariants, pin_equal_keys]
 WINDOW_PINS = [pin_window_brute_force, pin_window_torch, pin_window_closed_forms, pin_window_gradients]
 VALUE_DIM_PINS = [pin_value_dim]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + WINDOW_PINS + VALUE_DIM_PINS
+SPARSE_PINS = [pin_sparse_matches_dense, pin_sparse_torch, pin_sparse_brute_force, pin_sparse_closed_forms,
+               pin_sparse_gradients]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + WINDOW_PINS + VALUE_DIM_PINS + SPARSE_PINS
