@@ -13,7 +13,9 @@ when Dv = D; softmax and exp work is not counted.
 
 --workload picks another entry of inputs.CONFIGS (the default is the headline
 workload above); a config with a "window" runs attn_fwd_window/attn_bwd_window,
-one with a value head dimension "Dv" other than D runs attn_fwd_vdim/attn_bwd_vdim.
+one with a value head dimension "Dv" other than D runs attn_fwd_vdim/attn_bwd_vdim,
+and a "sparse" one runs attn_sparse_fwd/attn_sparse_bwd on synthetic index lists
+(FLOPs counted per non-empty list slot of every query head).
 """
 import argparse
 import json
@@ -100,6 +102,48 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
         secs += t_b
         sample += "; backward: row statistics of 1 of %d kv groups + dK/dV of %d of its %d keys" % (
             B * Hkv, nk, S)
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": sample, "seconds": round(secs, 2)}
+
+
+def cpu_baseline_sparse(q, k, v, dout, idx, cfg, target_s, with_bwd):
+    """The fp64 oracle on a bounded sample of the sparse workload: forward query rows
+    (~half the budget), then the backward of a sample of key/value rows (which first
+    needs every query row's lse and delta); TFLOP/s in the bench's convention."""
+    import numpy as np
+    import oracle
+    B, Hq, Hkv, S, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"]
+    N = k.shape[2]
+    scale = 1.0 / math.sqrt(D)
+    rng = np.random.default_rng(123)
+    nval = (idx >= 0).sum(axis=2)                                  # [B][S]
+
+    def row_flops(rows):
+        bh, i = rows // S, rows % S
+        return float(np.sum(4.0 * D * nval[bh // Hq, i]))
+
+    cal = rng.integers(0, B * Hq * S, size=256)
+    t = time.perf_counter()
+    oracle.sparse_fwd(q, k, v, idx, scale, rows=cal)
+    per_flop = (time.perf_counter() - t) / row_flops(cal)
+    budget = target_s * (0.5 if with_bwd else 1.0)
+    n = int(min(B * Hq * S, max(256, budget / per_flop / (row_flops(cal) / cal.size))))
+    rows = rng.choice(B * Hq * S, size=n, replace=False)
+    t = time.perf_counter()
+    oracle.sparse_fwd(q, k, v, idx, scale, rows=rows)
+    secs = time.perf_counter() - t
+    flops = row_flops(rows)
+    sample = "forward: %d of %d query rows (uniform without replacement)" % (n, B * Hq * S)
+    if with_bwd:
+        keys = np.sort(rng.choice(B * Hkv * N, size=16, replace=False)).astype(np.int64)
+        t = time.perf_counter()
+        oracle.sparse_bwd(q, k, v, dout, idx, scale, qrows=np.zeros(0, np.int64), kvrows=keys)
+        secs += time.perf_counter() - t
+        # every query row's scores and dP (the row statistics), then 8*D per (entry, head)
+        # for each sampled key
+        entries = sum(int(np.sum(idx[(r // N) // Hkv] == r % N)) for r in keys)
+        flops += 4.0 * D * Hq * float(nval.sum()) + 8.0 * D * (Hq // Hkv) * entries
+        sample += "; backward: all row statistics + dK/dV of 16 of %d key/value rows" % (B * Hkv * N)
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": sample, "seconds": round(secs, 2)}
 
@@ -195,47 +239,75 @@ def main():
     W = cfg.get("window", 0)
     Dv = cfg.get("Dv", D)
     scale = 1.0 / math.sqrt(D)
-    q, k, v, dout = qkv(B, Hq, Hkv, S, D, seed=0, with_dout=True, Dv=Dv)
-    dq_, dk_, dv_, ddo = to_dev(q), to_dev(k), to_dev(v), to_dev(dout)
-    o = torch.empty((B, Hq, S, Dv), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
-    gq = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
-    gk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
-    gv = torch.empty((B, Hkv, S, Dv), dtype=torch.float32, device="cuda")
-    ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal),), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     with_bwd = not args.fwd_only
+    sparse = cfg.get("sparse", False)
+    if sparse:
+        from flashattention_tiled_attention_amd.inputs import csa_index_lists, sparse_qkv
+        idx, N = csa_index_lists(B, S, W, cfg["ratio"], cfg["pool_topk"], seed=0)
+        q, k, v, dout = sparse_qkv(B, Hq, Hkv, S, N, D, seed=0, with_dout=True)
+        topk = idx.shape[2]
+        tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(dout)
+        ti = torch.from_numpy(idx).to("cuda")
+        o = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        gq = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+        gk = torch.empty((B, Hkv, N, D), dtype=torch.float32, device="cuda")
+        gv = torch.empty((B, Hkv, N, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty((fa.attn_sparse_bwd_workspace_bytes(B, Hq, Hkv, S, N, D, topk),), dtype=torch.uint8,
+                         device="cuda")
 
-    bargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws, stream)
-    wargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, W, scale, ws, stream)
-    if Dv != D:
         def run_fwd():
-            fa.attn_fwd_vdim(dq_, dk_, dv_, o, lse, causal, W, scale, stream)
+            fa.attn_sparse_fwd(tq, tk, tv, ti, o, lse, scale, stream)
 
         def run_bwd():
-            fa.attn_bwd_vdim(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, W, scale, ws, stream)
+            fa.attn_sparse_bwd(tq, tk, tv, ti, o, lse, tdo, gq, gk, gv, scale, ws, stream)
         calls = {"fwd_kernel": run_fwd}
         if with_bwd:
             calls["bwd_kernels"] = run_bwd
-    elif W:
-        def run_fwd():
-            fa.attn_fwd_window(dq_, dk_, dv_, o, lse, W, scale, stream)
-
-        def run_bwd():
-            fa.attn_bwd_window(*wargs)
-        calls = {"fwd_kernel": run_fwd}
-        if with_bwd:
-            calls["bwd_kernels"] = run_bwd
+        # every query head of a token sees the token's non-empty slots
+        pairs = float(Hq) * float((idx >= 0).sum())
     else:
-        def run_fwd():
-            fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream)
+        pairs = B * Hq * visible_pairs(S, causal, W)
+        q, k, v, dout = qkv(B, Hq, Hkv, S, D, seed=0, with_dout=True, Dv=Dv)
+        dq_, dk_, dv_, ddo = to_dev(q), to_dev(k), to_dev(v), to_dev(dout)
+        o = torch.empty((B, Hq, S, Dv), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        gq = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+        gk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
+        gv = torch.empty((B, Hkv, S, Dv), dtype=torch.float32, device="cuda")
+        ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal),), dtype=torch.uint8, device="cuda")
 
-        def run_bwd():
-            fa.attn_bwd(*bargs)
-        calls = {"fwd_kernel": run_fwd}
-        if with_bwd:
-            calls["dq_kernel"] = lambda: fa.attn_bwd_dq(*bargs)
-            calls["dkv_kernel"] = lambda: fa.attn_bwd_dkdv(*bargs)
+        bargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws, stream)
+        wargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, W, scale, ws, stream)
+        if Dv != D:
+            def run_fwd():
+                fa.attn_fwd_vdim(dq_, dk_, dv_, o, lse, causal, W, scale, stream)
+
+            def run_bwd():
+                fa.attn_bwd_vdim(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, W, scale, ws, stream)
+            calls = {"fwd_kernel": run_fwd}
+            if with_bwd:
+                calls["bwd_kernels"] = run_bwd
+        elif W:
+            def run_fwd():
+                fa.attn_fwd_window(dq_, dk_, dv_, o, lse, W, scale, stream)
+
+            def run_bwd():
+                fa.attn_bwd_window(*wargs)
+            calls = {"fwd_kernel": run_fwd}
+            if with_bwd:
+                calls["bwd_kernels"] = run_bwd
+        else:
+            def run_fwd():
+                fa.attn_fwd(dq_, dk_, dv_, o, lse, causal, scale, stream)
+
+            def run_bwd():
+                fa.attn_bwd(*bargs)
+            calls = {"fwd_kernel": run_fwd}
+            if with_bwd:
+                calls["dq_kernel"] = lambda: fa.attn_bwd_dq(*bargs)
+                calls["dkv_kernel"] = lambda: fa.attn_bwd_dkdv(*bargs)
 
     def step():
         run_fwd()
@@ -271,7 +343,6 @@ def main():
 
     # FLOP convention (pair_flops): each launch's products over the visible pairs; the
     # step's algorithmic work is the forward plus the backward's five products.
-    pairs = B * Hq * visible_pairs(S, causal, W)
     pf = pair_flops(D, Dv)
     f_fwd = pf["fwd"] * pairs
     f_bwd = pf["bwd"] * pairs
@@ -300,6 +371,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name + ("" if with_bwd else "_fwd_only"), "B": B, "Hq": Hq, "Hkv": Hkv,
                    "S": S, "D": D, "Dv": Dv, "causal": bool(causal), "window": W or None,
+                   "sparse_lists": ({"topk": int(topk), "N": int(N), "pool_ratio": cfg["ratio"],
+                                     "pool_topk": cfg["pool_topk"], "nonempty_slots": int((idx >= 0).sum())}
+                                    if sparse else None),
                    "pass": "fwd+bwd" if with_bwd else "fwd", "seed": 0},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd": {"tflops": kernels["fwd_kernel"]["tflops"], "ms": kernels["fwd_kernel"]["ms"],
@@ -313,7 +387,10 @@ def main():
                          "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (~%.0f s)" % args.cpu_seconds)
-        result["cpu_baseline"] = cpu_baseline(q, k, v, dout, cfg, args.cpu_seconds, with_bwd)
+        if sparse:
+            result["cpu_baseline"] = cpu_baseline_sparse(q, k, v, dout, idx, cfg, args.cpu_seconds, with_bwd)
+        else:
+            result["cpu_baseline"] = cpu_baseline(q, k, v, dout, cfg, args.cpu_seconds, with_bwd)
     print(json.dumps(result), flush=True)
 
 

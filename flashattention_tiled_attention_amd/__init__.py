@@ -7,8 +7,9 @@ There is no fallback: if ``libattn.so`` is missing, every call raises.
 
 Entry points with the C names (``attn_fwd``, ``attn_bwd``, ``attn_bwd_dq``,
 ``attn_bwd_dkdv``, ``attn_fwd_window``, ``attn_bwd_window``, ``attn_fwd_vdim``,
-``attn_bwd_vdim``, ``attn_bwd_workspace_bytes``, ``attn_status_str``) take
-caller-allocated tensors; ``fwd`` and ``bwd`` allocate their outputs with torch.
+``attn_bwd_vdim``, ``attn_bwd_workspace_bytes``, ``attn_sparse_fwd``, ``attn_sparse_bwd``,
+``attn_sparse_bwd_workspace_bytes``, ``attn_status_str``) take caller-allocated tensors;
+``fwd``, ``bwd``, ``sparse_fwd`` and ``sparse_bwd`` allocate their outputs with torch.
 """
 import ctypes
 import math
@@ -30,10 +31,11 @@ ATTN_ERR_SCALE = 7
 ATTN_ERR_HIP = 8
 ATTN_ERR_DEVICE = 9
 ATTN_ERR_WINDOW = 10
+ATTN_ERR_SPARSE = 11
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_window",
                     "attn_bwd_window", "attn_fwd_vdim", "attn_bwd_vdim", "attn_bwd_workspace_bytes",
-                    "attn_status_str")
+                    "attn_sparse_fwd", "attn_sparse_bwd", "attn_sparse_bwd_workspace_bytes", "attn_status_str")
 
 
 class AttnError(RuntimeError):
@@ -69,6 +71,12 @@ def load_library(path=None):
     lib.attn_fwd_vdim.restype = I
     lib.attn_bwd_vdim.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, I, F, V, Z, V]
     lib.attn_bwd_vdim.restype = I
+    lib.attn_sparse_fwd.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, I, F, V]
+    lib.attn_sparse_fwd.restype = I
+    lib.attn_sparse_bwd.argtypes = [V, V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, F, V, Z, V]
+    lib.attn_sparse_bwd.restype = I
+    lib.attn_sparse_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_sparse_bwd_workspace_bytes.restype = Z
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_status_str.argtypes = [I]
@@ -238,4 +246,83 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, window=0):
         attn_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, window, scale, ws)
     else:
         attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, ws)
+    return dq, dk, dv
+
+
+# ------------------------------------------------------------------ sparse attention
+
+def _sparse_dims(q, k, idx):
+    if q.dim() != 4 or k.dim() != 4 or idx.dim() != 3:
+        raise ValueError("q, k must be [B][H][rows][D] and idx [B][S][topk]")
+    B, Hq, S, D = q.shape
+    return B, Hq, k.shape[1], S, k.shape[2], D, idx.shape[2]
+
+
+def _sparse_check(q, k, v, idx, tensors):
+    import torch
+    B, Hq, Hkv, S, N, D, topk = _sparse_dims(q, k, idx)
+    _check(q, "q", torch.bfloat16, (B, Hq, S, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, N, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, N, D))
+    _check(idx, "idx", torch.int32, (B, S, topk))
+    shapes = {"o": ((B, Hq, S, D), torch.bfloat16), "lse": ((B, Hq, S), torch.float32),
+              "dout": ((B, Hq, S, D), torch.bfloat16), "dq": ((B, Hq, S, D), torch.float32),
+              "dk": ((B, Hkv, N, D), torch.float32), "dv": ((B, Hkv, N, D), torch.float32)}
+    for name, t in tensors.items():
+        _check(t, name, shapes[name][1], shapes[name][0])
+    return B, Hq, Hkv, S, N, D, topk
+
+
+def attn_sparse_fwd(q, k, v, idx, o, lse, scale, stream=None):
+    """C attn_sparse_fwd: q [B,Hq,S,D], k/v [B,Hkv,N,D] bf16, idx [B,S,topk] int32 (entries
+    outside [0, N) are empty slots); writes o (bf16) and lse (fp32)."""
+    dims = _sparse_check(q, k, v, idx, {"o": o, "lse": lse})
+    rc = load_library().attn_sparse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), *dims,
+                                        float(scale), _stream(stream))
+    if rc:
+        raise AttnError(rc, "attn_sparse_fwd")
+
+
+def attn_sparse_bwd_workspace_bytes(B, Hq, Hkv, S, N, D, topk):
+    return int(load_library().attn_sparse_bwd_workspace_bytes(B, Hq, Hkv, S, N, D, topk))
+
+
+def attn_sparse_bwd(q, k, v, idx, o, lse, dout, dq, dk, dv, scale, workspace, stream=None):
+    """C attn_sparse_bwd: gradients of attn_sparse_fwd (dq, dk, dv fp32); workspace is a
+    uint8 GPU tensor of attn_sparse_bwd_workspace_bytes() bytes."""
+    dims = _sparse_check(q, k, v, idx, {"o": o, "lse": lse, "dout": dout, "dq": dq, "dk": dk, "dv": dv})
+    if workspace.device.type != "cuda":
+        raise TypeError("workspace must be a GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load_library().attn_sparse_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), _ptr(dout),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), *dims, float(scale), _ptr(workspace),
+                                        nbytes, _stream(stream))
+    if rc:
+        raise AttnError(rc, "attn_sparse_bwd")
+
+
+def sparse_fwd(q, k, v, idx, scale=None):
+    """Allocate o and lse and run attn_sparse_fwd. scale defaults to 1/sqrt(D)."""
+    import torch
+    B, Hq, Hkv, S, N, D, topk = _sparse_dims(q, k, idx)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    attn_sparse_fwd(q, k, v, idx, o, lse, scale)
+    return o, lse
+
+
+def sparse_bwd(q, k, v, idx, o, lse, dout, scale=None):
+    """Allocate dq/dk/dv (fp32) and the workspace and run attn_sparse_bwd."""
+    import torch
+    B, Hq, Hkv, S, N, D, topk = _sparse_dims(q, k, idx)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, N, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, N, D), dtype=torch.float32, device=q.device)
+    ws = torch.empty((attn_sparse_bwd_workspace_bytes(B, Hq, Hkv, S, N, D, topk),), dtype=torch.uint8,
+                     device=q.device)
+    attn_sparse_bwd(q, k, v, idx, o, lse, dout, dq, dk, dv, scale, ws)
     return dq, dk, dv

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_sparse.hip"]
 LDS_LIB = os.path.join(HERE, "liblds_transpose.so")
 LDS_SOURCES = ["lds_transpose.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

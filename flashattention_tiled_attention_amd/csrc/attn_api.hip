@@ -13,6 +13,9 @@
 namespace attn {
 hipError_t fwd_setup_device();
 hipError_t bwd_setup_device();
+hipError_t sparse_setup_device();
+int sparse_tokens_per_chunk();
+int sparse_max_heads_per_kv();
 }  // namespace attn
 
 namespace {
@@ -41,7 +44,8 @@ int setup_current_device() {
             g_dev_status[dev] = ATTN_ERR_DEVICE;
             return;
         }
-        if (attn::fwd_setup_device() != hipSuccess || attn::bwd_setup_device() != hipSuccess) {
+        if (attn::fwd_setup_device() != hipSuccess || attn::bwd_setup_device() != hipSuccess ||
+            attn::sparse_setup_device() != hipSuccess) {
             (void)hipGetLastError();
             g_dev_status[dev] = ATTN_ERR_HIP;
             return;
@@ -69,6 +73,46 @@ size_t delta_bytes(int B, int Hq, int S) {
     return (((size_t)B * Hq * S * sizeof(float)) + 255) & ~(size_t)255;
 }
 
+constexpr int kSparseMaxTopk = 4096;
+
+// Sizes of the sparse entry points: D is the head dimension of q, k, v; N the
+// number of key/value rows; topk the list length.
+int check_sparse_sizes(int B, int Hq, int Hkv, int S, int N, int D, int topk) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || N < 1 || D < 1 || topk < 1) return ATTN_ERR_SHAPE;
+    if ((double)B * Hq * S * D >= 1099511627776.0 || (double)B * Hkv * N * D >= 1099511627776.0)
+        return ATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_GQA;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
+    if (topk > kSparseMaxTopk || Hq / Hkv > attn::sparse_max_heads_per_kv()) return ATTN_ERR_SPARSE;
+    // 32-bit row offsets within a head, 32-bit list entries, 32-bit grids
+    if ((double)N * D >= 2147483647.0 || (double)S * topk >= 2147483647.0) return ATTN_ERR_SPARSE;
+    if ((double)B * S * Hq * ((topk + 127) / 128 + 2) >= 2147483647.0) return ATTN_ERR_SPARSE;
+    if ((double)B * Hkv * N >= 2147483647.0) return ATTN_ERR_SPARSE;
+    return ATTN_OK;
+}
+
+// Backward workspace: delta, the two per-(token, slot) contribution arrays, and
+// the inverse of the index map (chunk counts, row starts, entry list).
+struct SparseWs {
+    size_t delta, inter_k, inter_v, cnt, rowstart, list, total;
+    int nchunks;
+};
+
+SparseWs sparse_ws(int B, int Hq, int Hkv, int S, int N, int D, int topk) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    SparseWs w;
+    w.nchunks = (S + attn::sparse_tokens_per_chunk() - 1) / attn::sparse_tokens_per_chunk();
+    size_t off = 0;
+    w.delta = off;    off += al((size_t)B * Hq * S * 4);
+    w.inter_k = off;  off += al((size_t)B * Hkv * S * topk * D * 4);
+    w.inter_v = off;  off += al((size_t)B * Hkv * S * topk * D * 4);
+    w.cnt = off;      off += al((size_t)B * w.nchunks * N * 4);
+    w.rowstart = off; off += al((size_t)B * (N + 1) * 4);
+    w.list = off;     off += al((size_t)B * S * topk * 4);
+    w.total = off;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,6 +130,8 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_HIP: return "HIP runtime error";
         case ATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
         case ATTN_ERR_WINDOW: return "window must be >= 1 (>= 0 and causal for the vdim entry points)";
+        case ATTN_ERR_SPARSE:
+            return "sparse sizes out of range: topk <= 4096, Hq/Hkv <= 128, N*D and S*topk < 2^31";
         default: return "unknown attn status";
     }
 }
@@ -230,6 +276,80 @@ int attn_bwd_vdim(const void* q, const void* k, const void* v, const void* o, co
     if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_WINDOW;
     return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, Dv, causal,
                       window >= S ? 0 : window, scale, workspace, workspace_bytes, stream);
+}
+
+int attn_sparse_fwd(const void* q, const void* k, const void* v, const int* idx, void* o, float* lse,
+                    int B, int Hq, int Hkv, int S, int N, int D, int topk, float scale,
+                    void* stream) {
+    if (!q || !k || !v || !idx || !o || !lse) return ATTN_ERR_NULL;
+    int rc = check_sparse_sizes(B, Hq, Hkv, S, N, D, topk);
+    if (rc) return rc;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(idx) || misaligned(o) ||
+        misaligned(lse))
+        return ATTN_ERR_ALIGN;
+    if ((rc = setup_current_device())) return rc;
+    attn::SparseArgs a = {};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.idx = (const int32_t*)idx;
+    a.out = (uint16_t*)o;
+    a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.N = N; a.G = Hq / Hkv; a.topk = topk;
+    a.scale = scale;
+    a.scale_log2 = fmaxf(fabsf(scale) * 1.4426950408889634f, 7.888609052210118e-31f);
+    a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
+    a.precise_all = fabsf(scale) * sqrtf((float)D) > 2.0f ? 1 : 0;
+    if (attn::launch_sparse_fwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+size_t attn_sparse_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int N, int D, int topk) {
+    if (check_sparse_sizes(B, Hq, Hkv, S, N, D, topk) != ATTN_OK) return 0;
+    return sparse_ws(B, Hq, Hkv, S, N, D, topk).total;
+}
+
+int attn_sparse_bwd(const void* q, const void* k, const void* v, const int* idx, const void* o,
+                    const float* lse, const void* dout, float* dq, float* dk, float* dv, int B,
+                    int Hq, int Hkv, int S, int N, int D, int topk, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !idx || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    int rc = check_sparse_sizes(B, Hq, Hkv, S, N, D, topk);
+    if (rc) return rc;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    const SparseWs w = sparse_ws(B, Hq, Hkv, S, N, D, topk);
+    if (!workspace || workspace_bytes < w.total) return ATTN_ERR_WORKSPACE;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(idx) || misaligned(o) ||
+        misaligned(lse) || misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
+        misaligned(workspace))
+        return ATTN_ERR_ALIGN;
+    if ((rc = setup_current_device())) return rc;
+    attn::SparseArgs a = {};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.idx = (const int32_t*)idx;
+    a.o = (const uint16_t*)o;
+    a.dout = (const uint16_t*)dout;
+    a.lse = (float*)lse;  // read only by the backward kernels
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    unsigned char* ws = (unsigned char*)workspace;
+    a.delta = (float*)(ws + w.delta);
+    a.inter_k = (float*)(ws + w.inter_k);
+    a.inter_v = (float*)(ws + w.inter_v);
+    a.cnt = (int*)(ws + w.cnt);
+    a.rowstart = (int*)(ws + w.rowstart);
+    a.list = (int*)(ws + w.list);
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.N = N; a.G = Hq / Hkv; a.topk = topk;
+    a.nchunks = w.nchunks;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.precise_all = fabsf(scale) * sqrtf((float)D) > 2.0f ? 1 : 0;
+    if (attn::launch_sparse_bwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,777 @@
+// Sparse attention over per-token index lists, for gfx950 (MI355X).
+//
+// The compressed sparse attention of Rao et al., "Scheduling Data to Compute:
+// Hierarchical Data Pipelining for LLM Training on AMD GPUs" (section 2.1;
+// Table 7 for its shapes), gives every query token a top-k list of key/value
+// rows: a sliding window of recent tokens plus rows of a compressed pool. The
+// forward gathers the listed rows, scores them and streams their values into the
+// output accumulator (Eq. (1) over the listed rows). The backward gathers the
+// same rows to form dQ, produces one dK/dV contribution per (token, list slot),
+// and reduces those contributions by the inverse of the index map. The kernels
+// here follow that data flow:
+//
+//   sparse_fwd_kernel     one workgroup per (b, token, kv head, block of 64 query
+//                         heads). The token's list is compacted into LDS (empty
+//                         slots dropped, order kept); 32-row K/V tiles are
+//                         gathered from HBM straight into double-buffered,
+//                         swizzled LDS tiles by per-lane global_load_lds
+//                         addresses (MI355X has no gather engine, so each lane
+//                         names its own row); S^T = K Q^T, online softmax and
+//                         O^T += V^T P^T as in the dense forward.
+//   sparse_dq_kernel      the same gather; dP^T = V dO^T, dS = P (dP - delta),
+//                         dQ^T += K^T dS^T; writes delta for the next stage.
+//   sparse_kv_partial     one workgroup per (b, token, kv head, 128 list slots):
+//                         the token's query heads are the rows of one Q and one
+//                         dO tile in LDS, each lane owns one slot; it writes
+//                         scale dS^T Q and P^T dO for every non-empty slot.
+//   sp_count, sp_scan_chunks, sp_scan_rows, sp_scatter
+//                         the inverse of the index map: for every key/value row,
+//                         the (token, slot) entries that name it, in token order
+//                         (deterministic: counts are order-free, and positions
+//                         are handed out chunk by chunk, token by token).
+//   sp_reduce             dK, dV of every row: the sum of its entries'
+//                         contributions in that order, in a fixed association.
+//
+// The sum over a token's query heads happens inside the partial kernel's MFMAs
+// (the heads are their contraction index), so the per-slot contribution is one
+// D-vector per kv head. Rows that see few keys (at most 256 non-empty slots)
+// take the exact path of the dense kernels: P and dS split into a bf16 high
+// part and a bf16 remainder, and delta recomputed as sum_s P dP.
+#include "device.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSpBK = 32;            // list slots per gathered K/V tile
+constexpr int kSpRows = 64;          // query heads per forward / dQ workgroup
+constexpr int kSpThreads = 128;      // 2 waves x 32 heads
+constexpr int kSpPreciseSlots = 256; // tokens with at most this many keys take the exact path
+constexpr int kSpSlotsPerWG = 128;   // partial kernel: list slots per workgroup (4 waves x 32)
+constexpr int kSpPartThreads = 256;
+constexpr int kSpMaxG = 128;         // query heads per kv head
+constexpr int kSpChunk = 16;         // tokens per inverse-map chunk
+
+__device__ __forceinline__ bool slot_valid(int j, int N) { return j >= 0 && j < N; }
+
+// Work item of workgroup `bid` among `total` items ordered (b, token, kv head,
+// block): when total divides by 8, each XCD takes a contiguous range of items,
+// so neighbouring tokens (whose windows overlap) share one L2.
+__device__ __forceinline__ int xcd_item(int bid, int total) {
+    if ((total & 7) == 0) return (bid & 7) * (total >> 3) + (bid >> 3);
+    return bid;
+}
+
+// Compact the token's list into LDS: the non-empty entries in slot order.
+// Returns their number (the same in every lane). 128 threads; red: 2 LDS ints.
+__device__ __forceinline__ int compact_list(const int32_t* src, int topk, int N, int* out, int* red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int total = 0;
+    for (int base = 0; base < topk; base += kSpThreads) {
+        const int s = base + tid;
+        const int j = s < topk ? src[s] : -1;
+        const bool ok = slot_valid(j, N);
+        const unsigned long long m = __ballot(ok);
+        const int before = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) red[wave] = __popcll(m);
+        __syncthreads();
+        const int c0 = red[0], c1 = red[1];
+        if (ok) out[total + (wave ? c0 : 0) + before] = j;
+        total += c0 + c1;
+        __syncthreads();
+    }
+    return total;
+}
+
+template <int D>
+struct SpTile {
+    static constexpr int TILE = kSpBK * D;                     // elements
+    static constexpr int KV_BYTES = 4 * TILE * 2;             // 2 K slots + 2 V slots
+    using Copy = CopyPlan<D, kSpBK, 2>;
+    static int lds_bytes(int topk) { return KV_BYTES + ((topk * 4 + 15) & ~15) + 16; }
+};
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a) {
+    using T = SpTile<D>;
+    using C = typename T::Copy;
+    constexpr int DK = D / 16;
+    constexpr int DB = D / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    __bf16* const Kring = (__bf16*)lds_raw;
+    __bf16* const Vring = Kring + 2 * T::TILE;
+    int* const list = (int*)(lds_raw + T::KV_BYTES);
+    int* const red = list + ((a.topk + 3) & ~3);
+
+    const int nHB = (a.G + kSpRows - 1) / kSpRows;
+    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nHB);
+    const int hb = w % nHB; w /= nHB;
+    const int hkv = w % a.Hkv; w /= a.Hkv;
+    const int i = w % a.S;
+    const int b = w / a.S;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int head = hb * kSpRows + 32 * wave + l32;
+    const bool live = head < a.G;
+    const int hq = hkv * a.G + head;
+    const size_t row = ((size_t)b * a.Hq + hq) * a.S + i;   // flat query row (when live)
+    const float c = a.scale_log2;
+
+    const int n = compact_list(a.idx + ((size_t)b * a.S + i) * a.topk, a.topk, a.N, list, red);
+    const bool precise = a.precise_all || n <= kSpPreciseSlots;
+
+    bf16x8 qf[DK];
+    if (live) {
+        const u32x4* src = (const u32x4*)(a.q + row * D + 8 * h);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            u32x4 t = src[2 * dk];
+            t ^= a.q_sign;
+            qf[dk] = __builtin_bit_cast(bf16x8, t);
+        }
+    } else {
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) qf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+
+    const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
+    const uint16_t* Kp = a.k + kvbase;
+    const uint16_t* Vp = a.v + kvbase;
+    // Gathered copies: copy m of this wave fills tile rows (wave*N + m) * ROWS_PER_COPY
+    // + lane / CH with the row its compacted slot names; slots past the end repeat
+    // the last one (their scores are masked, their probabilities exactly 0).
+    int crow[C::N], ccol[C::N];
+#pragma unroll
+    for (int m = 0; m < C::N; ++m) {
+        crow[m] = (wave * C::N + m) * C::ROWS_PER_COPY + lane / C::CH;
+        ccol[m] = (((lane % C::CH) ^ swz_f<D>(crow[m]))) * 8;
+    }
+    auto copy_tile = [&](int slot, int t) {
+#pragma unroll
+        for (int m = 0; m < C::N; ++m) {
+            const int j = list[min(t * kSpBK + crow[m], n - 1)];
+            const uint32_t off = (uint32_t)j * D + ccol[m];
+            copy16_to_lds(Kp + off, Kring + slot * T::TILE + (wave * C::N + m) * 512);
+            copy16_to_lds(Vp + off, Vring + slot * T::TILE + (wave * C::N + m) * 512);
+        }
+    };
+    int koff[DK], voff[2][DB];
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) koff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            voff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = zero16();
+    float m = -1e30f, l = 0.0f;
+
+    const int nT = (n + kSpBK - 1) / kSpBK;
+    if (nT > 0) {
+        copy_tile(0, 0);
+        wait_copies();
+        __syncthreads();
+    }
+    for (int t = 0; t < nT; ++t) {
+        if (t + 1 < nT) copy_tile((t + 1) & 1, t + 1);
+        const __bf16* Ks = Kring + (t & 1) * T::TILE;
+        const __bf16* Vs = Vring + (t & 1) * T::TILE;
+        f32x16 sc = zero16();
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) sc = mfma32(lds_read8(Ks + koff[dk]), qf[dk], sc);
+        if (t == nT - 1) {  // slot t*32 + 4h + off exists iff off < lim
+            const int lim = n - t * kSpBK - 4 * h;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
+        }
+        float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        const float mnew = fmaxf(m, halves_max(mx) * c);  // c > 0
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        bf16x8 pk[2], pl[2];
+        float rs = 0.0f;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(fmaf(sc[8 * t2 + e], c, -m));
+                rs += p[e];
+            }
+            pk[t2] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            pl[t2] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
+                           bf_lo(p[6]), bf_lo(p[7]));
+        }
+        l += rs;
+        // O^T += V^T P^T over two 16-slot steps; V^T through transpose loads.
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 vt = concat(lds_read_tr(Vs + voff[0][db] + 16 * t2 * D),
+                                         lds_read_tr(Vs + voff[1][db] + 16 * t2 * D));
+                oacc[db] = mfma32(vt, pk[t2], oacc[db]);
+                if (precise) oacc[db] = mfma32(vt, pl[t2], oacc[db]);
+            }
+        wait_copies();
+        __syncthreads();
+    }
+
+    const float lt = halves_sum(l);
+    if (live) {
+        uint16_t* op = a.out + row * D;
+        const float inv = n > 0 ? 1.0f / lt : 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = db * 32 + 8 * g4 + 4 * h;
+                *(bf16x4*)(op + d) = pack4(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
+                                           oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+            }
+        if (h == 0) a.lse[row] = n > 0 ? (m + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (+ delta)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) {
+    using T = SpTile<D>;
+    using C = typename T::Copy;
+    constexpr int DK = D / 16;
+    constexpr int DB = D / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    __bf16* const Kring = (__bf16*)lds_raw;
+    __bf16* const Vring = Kring + 2 * T::TILE;
+    int* const list = (int*)(lds_raw + T::KV_BYTES);
+    int* const red = list + ((a.topk + 3) & ~3);
+
+    const int nHB = (a.G + kSpRows - 1) / kSpRows;
+    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nHB);
+    const int hb = w % nHB; w /= nHB;
+    const int hkv = w % a.Hkv; w /= a.Hkv;
+    const int i = w % a.S;
+    const int b = w / a.S;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int head = hb * kSpRows + 32 * wave + l32;
+    const bool live = head < a.G;
+    const int hq = hkv * a.G + head;
+    const size_t row = ((size_t)b * a.Hq + hq) * a.S + i;
+    const float c = a.scale_log2;  // signed
+
+    const int n = compact_list(a.idx + ((size_t)b * a.S + i) * a.topk, a.topk, a.N, list, red);
+    const bool precise = a.precise_all || n <= kSpPreciseSlots;
+
+    // Q and dO rows as B operands; delta = rowsum(dO * O) from the stored O.
+    bf16x8 qf[DK], df[DK];
+    float dpart = 0.0f;
+    if (live) {
+        const u32x4* qs = (const u32x4*)(a.q + row * D + 8 * h);
+        const u32x4* ds = (const u32x4*)(a.dout + row * D + 8 * h);
+        const u32x4* os = (const u32x4*)(a.o + row * D + 8 * h);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            qf[dk] = __builtin_bit_cast(bf16x8, qs[2 * dk]);
+            df[dk] = __builtin_bit_cast(bf16x8, ds[2 * dk]);
+            const bf16x8 ov = __builtin_bit_cast(bf16x8, os[2 * dk]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dpart += (float)df[dk][e] * (float)ov[e];
+        }
+    } else {
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            qf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+            df[dk] = qf[dk];
+        }
+    }
+    float delta = halves_sum(dpart);
+    const float lse2 = (live && n > 0) ? a.lse[row] * kLog2e : INFINITY;
+
+    const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
+    const uint16_t* Kp = a.k + kvbase;
+    const uint16_t* Vp = a.v + kvbase;
+    int crow[C::N], ccol[C::N];
+#pragma unroll
+    for (int m = 0; m < C::N; ++m) {
+        crow[m] = (wave * C::N + m) * C::ROWS_PER_COPY + lane / C::CH;
+        ccol[m] = (((lane % C::CH) ^ swz_f<D>(crow[m]))) * 8;
+    }
+    auto copy_tile = [&](int slot, int t) {
+#pragma unroll
+        for (int m = 0; m < C::N; ++m) {
+            const int j = list[min(t * kSpBK + crow[m], n - 1)];
+            const uint32_t off = (uint32_t)j * D + ccol[m];
+            copy16_to_lds(Kp + off, Kring + slot * T::TILE + (wave * C::N + m) * 512);
+            copy16_to_lds(Vp + off, Vring + slot * T::TILE + (wave * C::N + m) * 512);
+        }
+    };
+    int roff[DK], toff[2][DB];
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero16();
+
+    // Pass 0 (exact path only) accumulates delta = sum_s P dP; the last pass forms
+    // dS and accumulates dQ^T += K^T dS^T.
+    const int nT = (n + kSpBK - 1) / kSpBK;
+    for (int pass = precise ? 0 : 1; pass < 2; ++pass) {
+        float dacc = 0.0f;
+        if (nT > 0) {
+            copy_tile(0, 0);
+            wait_copies();
+            __syncthreads();
+        }
+        for (int t = 0; t < nT; ++t) {
+            if (t + 1 < nT) copy_tile((t + 1) & 1, t + 1);
+            const __bf16* Ks = Kring + (t & 1) * T::TILE;
+            const __bf16* Vs = Vring + (t & 1) * T::TILE;
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int dk = 0; dk < DK; ++dk) {
+                s = mfma32(lds_read8(Ks + roff[dk]), qf[dk], s);
+                dp = mfma32(lds_read8(Vs + roff[dk]), df[dk], dp);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lse2));
+            if (t == nT - 1) {
+                const int lim = n - t * kSpBK - 4 * h;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) >= lim) ? 0.0f : s[r];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (precise) dacc += s[r] * dp[r];  // used by pass 0 only
+                s[r] = s[r] * (dp[r] - delta);
+            }
+            if (pass == 1) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const int r0 = 8 * t2;
+                    const bf16x8 hi = pack8(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5],
+                                            s[r0 + 6], s[r0 + 7]);
+                    const bf16x8 lo = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
+                                            bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]),
+                                            bf_lo(s[r0 + 7]));
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const bf16x8 kt = concat(lds_read_tr(Ks + toff[0][db] + 16 * t2 * D),
+                                                 lds_read_tr(Ks + toff[1][db] + 16 * t2 * D));
+                        dq[db] = mfma32(kt, hi, dq[db]);
+                        if (precise) dq[db] = mfma32(kt, lo, dq[db]);
+                    }
+                }
+            }
+            wait_copies();
+            __syncthreads();
+        }
+        if (pass == 0) delta = halves_sum(dacc);
+    }
+
+    if (live) {
+        if (h == 0) a.delta[row] = delta;
+        float* dst = a.dq + row * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = dq[db][4 * g4 + e] * a.scale;
+                *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * h) = v;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// per-(token, slot) dK / dV contributions
+// ---------------------------------------------------------------------------
+template <int D>
+struct PartTile {
+    // Q and dO tiles [Gp][D] of the token's query heads, the V rows of the
+    // workgroup's 128 slots [128][D], all in swz<D> order; lse*log2e and delta
+    // per head.
+    static int lds_bytes(int Gp) { return (2 * Gp * D + kSpSlotsPerWG * D) * 2 + 2 * Gp * 4 + 16; }
+};
+
+template <int D>
+__global__ void __launch_bounds__(kSpPartThreads, 1) sparse_kv_partial_kernel(SparseArgs a) {
+    constexpr int DK = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int CH = D / 8, RPC = 64 / CH;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    const int G = a.G, Gp = (G + 31) & ~31;
+    __bf16* const Qt = (__bf16*)lds_raw;
+    __bf16* const Dt = Qt + Gp * D;
+    __bf16* const Vt = Dt + Gp * D;
+    float* const Ls = (float*)(Vt + kSpSlotsPerWG * D);
+    float* const Dl = Ls + Gp;
+    int* const cnt = (int*)(Dl + Gp);
+
+    const int nSB = (a.topk + kSpSlotsPerWG - 1) / kSpSlotsPerWG;
+    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nSB);
+    const int sb = w % nSB; w /= nSB;
+    const int hkv = w % a.Hkv; w /= a.Hkv;
+    const int i = w % a.S;
+    const int b = w / a.S;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int32_t* lst = a.idx + ((size_t)b * a.S + i) * a.topk;
+    const int slot = sb * kSpSlotsPerWG + 32 * wave + l32;   // this lane's list slot
+    const int jraw = slot < a.topk ? lst[slot] : -1;
+    const bool valid = slot_valid(jraw, a.N);
+    const int j = valid ? jraw : 0;
+
+    // number of non-empty slots of the token (for the exact-path choice)
+    if (tid == 0) *cnt = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int s = tid; s < a.topk; s += kSpPartThreads) mine += slot_valid(lst[s], a.N) ? 1 : 0;
+    if (mine) atomicAdd(cnt, mine);
+
+    // Q / dO rows of the token's heads (rows past G repeat head G-1; their lse is
+    // +inf, so they add exactly 0), and the V rows of this workgroup's slots.
+    const size_t qrow0 = ((size_t)b * a.Hq + hkv * G) * a.S + i;   // head g at qrow0 + g*S
+    for (int cpy = wave; cpy < Gp / RPC; cpy += 4) {
+        const int r = cpy * RPC + lane / CH;
+        const int col = (((lane % CH) ^ swz_f<D>(r))) * 8;
+        const size_t src = (qrow0 + (size_t)min(r, G - 1) * a.S) * D + col;
+        copy16_to_lds(a.q + src, Qt + cpy * 512);
+        copy16_to_lds(a.dout + src, Dt + cpy * 512);
+    }
+    const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
+    for (int cpy = wave; cpy < kSpSlotsPerWG / RPC; cpy += 4) {
+        const int r = cpy * RPC + lane / CH;
+        const int col = (((lane % CH) ^ swz_f<D>(r))) * 8;
+        const int s2 = sb * kSpSlotsPerWG + r;
+        const int jr = s2 < a.topk ? lst[s2] : -1;
+        copy16_to_lds(a.v + kvbase + (size_t)(slot_valid(jr, a.N) ? jr : 0) * D + col, Vt + cpy * 512);
+    }
+    for (int g = tid; g < Gp; g += kSpPartThreads) {
+        const size_t r = qrow0 + (size_t)g * a.S;
+        Ls[g] = g < G ? a.lse[r] * kLog2e : INFINITY;
+        Dl[g] = g < G ? a.delta[r] : 0.0f;
+    }
+    // this lane's K row as B operands
+    bf16x8 kf[DK];
+    {
+        const u32x4* ks = (const u32x4*)(a.k + kvbase + (size_t)j * D + 8 * h);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) kf[dk] = __builtin_bit_cast(bf16x8, ks[2 * dk]);
+    }
+    wait_copies();
+    __syncthreads();
+    const bool precise = a.precise_all || *cnt <= kSpPreciseSlots;
+    const float c = a.scale_log2;  // signed
+
+    if (__ballot(valid) == 0) return;  // no non-empty slot in this wave
+
+    int roff[DK], toff[2][DB];
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dk[db] = zero16();
+        dv[db] = zero16();
+    }
+    for (int hs = 0; hs < Gp / 32; ++hs) {
+        // S and dP of 32 heads x this wave's 32 slots; rows are heads
+        // 32 hs + 8(r/4) + 4h + r%4, the column is this lane's slot.
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int dd = 0; dd < DK; ++dd) {
+            const bf16x8 qa = lds_read8(Qt + hs * 32 * D + roff[dd]);
+            const bf16x8 da = lds_read8(Dt + hs * 32 * D + roff[dd]);
+            const bf16x8 vb = lds_read8(Vt + wave * 32 * D + roff[dd]);
+            s = mfma32(qa, kf[dd], s);
+            dp = mfma32(da, vb, dp);
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            float pv[8], dsv[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int rg = 2 * t2 + half;
+                const f32x4 l4 = *(const f32x4*)(Ls + hs * 32 + 8 * rg + 4 * h);
+                const f32x4 d4 = *(const f32x4*)(Dl + hs * 32 + 8 * rg + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = valid ? fast_exp2(fmaf(s[4 * rg + e], c, -l4[e])) : 0.0f;
+                    pv[4 * half + e] = p;
+                    dsv[4 * half + e] = p * (dp[4 * rg + e] - d4[e]);
+                }
+            }
+            const bf16x8 ph = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+            const bf16x8 sh = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+            const bf16x8 pl = pack8(bf_lo(pv[0]), bf_lo(pv[1]), bf_lo(pv[2]), bf_lo(pv[3]), bf_lo(pv[4]),
+                                    bf_lo(pv[5]), bf_lo(pv[6]), bf_lo(pv[7]));
+            const bf16x8 sl = pack8(bf_lo(dsv[0]), bf_lo(dsv[1]), bf_lo(dsv[2]), bf_lo(dsv[3]),
+                                    bf_lo(dsv[4]), bf_lo(dsv[5]), bf_lo(dsv[6]), bf_lo(dsv[7]));
+            const int rb = (hs * 32 + 16 * t2) * D;
+            // dV^T += dO^T P and dK^T += Q^T dS over 16 heads; dO^T, Q^T by transpose loads
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 dot = concat(lds_read_tr(Dt + toff[0][db] + rb), lds_read_tr(Dt + toff[1][db] + rb));
+                const bf16x8 qt = concat(lds_read_tr(Qt + toff[0][db] + rb), lds_read_tr(Qt + toff[1][db] + rb));
+                dv[db] = mfma32(dot, ph, dv[db]);
+                dk[db] = mfma32(qt, sh, dk[db]);
+                if (precise) {
+                    dv[db] = mfma32(dot, pl, dv[db]);
+                    dk[db] = mfma32(qt, sl, dk[db]);
+                }
+            }
+        }
+    }
+    if (valid) {
+        const size_t e = (((size_t)b * a.Hkv + hkv) * a.S + i) * a.topk + slot;
+        float* ok = a.inter_k + e * D;
+        float* ov = a.inter_v + e * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 vk, vv;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    vk[q] = dk[db][4 * g4 + q] * a.scale;
+                    vv[q] = dv[db][4 * g4 + q];
+                }
+                *(f32x4*)(ok + db * 32 + 8 * g4 + 4 * h) = vk;
+                *(f32x4*)(ov + db * 32 + 8 * g4 + 4 * h) = vv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// inverse of the index map
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) sp_fill_zero(int* p, size_t n) {
+    for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) p[x] = 0;
+}
+
+// cnt[b][c][j] = number of entries of chunk c (tokens 16c .. 16c+15) naming row j.
+__global__ void __launch_bounds__(256) sp_count(SparseArgs a) {
+    const int b = blockIdx.x / a.nchunks, ch = blockIdx.x % a.nchunks;
+    int* cnt = a.cnt + ((size_t)b * a.nchunks + ch) * a.N;
+    const int i1 = min(a.S, (ch + 1) * kSpChunk);
+    for (int i = ch * kSpChunk; i < i1; ++i) {
+        const int32_t* lst = a.idx + ((size_t)b * a.S + i) * a.topk;
+        for (int s = threadIdx.x; s < a.topk; s += 256) {
+            const int j = lst[s];
+            if (slot_valid(j, a.N)) atomicAdd(cnt + j, 1);
+        }
+    }
+}
+
+// Per row j: chunk counts -> exclusive chunk bases (in place); row totals.
+__global__ void __launch_bounds__(256) sp_scan_chunks(SparseArgs a) {
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (size_t)a.B * a.N) return;
+    const int b = (int)(x / a.N), j = (int)(x % a.N);
+    int run = 0;
+    for (int ch = 0; ch < a.nchunks; ++ch) {
+        int* p = a.cnt + ((size_t)b * a.nchunks + ch) * a.N + j;
+        const int v = *p;
+        *p = run;
+        run += v;
+    }
+    a.rowstart[(size_t)b * (a.N + 1) + j] = run;
+}
+
+// rowstart[b][0..N] = exclusive prefix sum of the row totals (one workgroup per b).
+__global__ void __launch_bounds__(1024) sp_scan_rows(SparseArgs a) {
+    __shared__ int buf[1024];
+    int* rs = a.rowstart + (size_t)blockIdx.x * (a.N + 1);
+    int base = 0;
+    for (int j0 = 0; j0 < a.N; j0 += 1024) {
+        const int j = j0 + threadIdx.x;
+        const int v = j < a.N ? rs[j] : 0;
+        buf[threadIdx.x] = v;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+            const int add = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+            __syncthreads();
+            buf[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (j < a.N) rs[j] = base + buf[threadIdx.x] - v;
+        base += buf[1023];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) rs[a.N] = base;
+}
+
+// list[b][rowstart[j] + k] = the k-th entry (i*topk + s, in token order) naming
+// row j. A workgroup walks its chunk's tokens in order; a returning atomic on the
+// chunk base of row j gives each entry its place.
+__global__ void __launch_bounds__(256) sp_scatter(SparseArgs a) {
+    const int b = blockIdx.x / a.nchunks, ch = blockIdx.x % a.nchunks;
+    int* cur = a.cnt + ((size_t)b * a.nchunks + ch) * a.N;
+    const int* rs = a.rowstart + (size_t)b * (a.N + 1);
+    int* out = a.list + (size_t)b * a.S * a.topk;
+    const int i1 = min(a.S, (ch + 1) * kSpChunk);
+    for (int i = ch * kSpChunk; i < i1; ++i) {
+        const int32_t* lst = a.idx + ((size_t)b * a.S + i) * a.topk;
+        for (int s = threadIdx.x; s < a.topk; s += 256) {
+            const int j = lst[s];
+            if (slot_valid(j, a.N)) out[rs[j] + atomicAdd(cur + j, 1)] = i * a.topk + s;
+        }
+        __syncthreads();  // token i's places are taken before token i+1's
+    }
+}
+
+// dK, dV of row (b, hkv, j): the sum of its entries' contributions in list order.
+// Wave w sums entries w, w+4, ... (four at a time in flight); the four partial
+// sums are then added in wave order. Lane l holds columns 2l, 2l+1.
+template <int D>
+__global__ void __launch_bounds__(256) sp_reduce(SparseArgs a) {
+    typedef float fv __attribute__((ext_vector_type(2)));
+    constexpr int PER = 2;
+    __shared__ fv part[2][4][64];
+    const int j = blockIdx.x % a.N;
+    const int bh = blockIdx.x / a.N;   // b * Hkv + hkv
+    const int b = bh / a.Hkv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool on = lane < D / PER;  // D = 64 uses 32 lanes of each wave
+    const int* rs = a.rowstart + (size_t)b * (a.N + 1);
+    const int* ent = a.list + (size_t)b * a.S * a.topk;
+    const int e0 = rs[j], e1 = rs[j + 1];
+    const float* ik = a.inter_k + (size_t)bh * a.S * a.topk * D + lane * PER;
+    const float* iv = a.inter_v + (size_t)bh * a.S * a.topk * D + lane * PER;
+    fv sk = {}, sv = {};
+    int e = on ? e0 + wave : e1;
+    for (; e + 12 < e1; e += 16) {
+        fv k4[4], v4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const size_t x = (size_t)ent[e + 4 * u] * D;
+            k4[u] = *(const fv*)(ik + x);
+            v4[u] = *(const fv*)(iv + x);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            sk += k4[u];
+            sv += v4[u];
+        }
+    }
+    for (; e < e1; e += 4) {
+        const size_t x = (size_t)ent[e] * D;
+        sk += *(const fv*)(ik + x);
+        sv += *(const fv*)(iv + x);
+    }
+    part[0][wave][lane] = sk;
+    part[1][wave][lane] = sv;
+    __syncthreads();
+    if (wave < 2 && on) {
+        fv r = part[wave][0][lane];
+        r += part[wave][1][lane];
+        r += part[wave][2][lane];
+        r += part[wave][3][lane];
+        float* dst = (wave == 0 ? a.dk : a.dv) + ((size_t)bh * a.N + j) * D + lane * PER;
+        *(fv*)dst = r;
+    }
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, int bytes) {
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D>
+hipError_t launch_fwd_t(const SparseArgs& a, hipStream_t stream) {
+    const int nHB = (a.G + kSpRows - 1) / kSpRows;
+    const long long blocks = (long long)a.B * a.S * a.Hkv * nHB;
+    const int lds = SpTile<D>::lds_bytes(a.topk);
+    hipLaunchKernelGGL((sparse_fwd_kernel<D>), dim3((unsigned)blocks), dim3(kSpThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_t(const SparseArgs& a, hipStream_t stream) {
+    hipError_t e;
+    const size_t ncnt = (size_t)a.B * a.nchunks * a.N;
+    hipLaunchKernelGGL(sp_fill_zero, dim3((unsigned)min((size_t)4096, (ncnt + 255) / 256)), dim3(256), 0, stream,
+                       a.cnt, ncnt);
+    const int nHB = (a.G + kSpRows - 1) / kSpRows;
+    const long long qblocks = (long long)a.B * a.S * a.Hkv * nHB;
+    const int qlds = SpTile<D>::lds_bytes(a.topk);
+    hipLaunchKernelGGL((sparse_dq_kernel<D>), dim3((unsigned)qblocks), dim3(kSpThreads), qlds, stream, a);
+    const int nSB = (a.topk + kSpSlotsPerWG - 1) / kSpSlotsPerWG;
+    const long long pblocks = (long long)a.B * a.S * a.Hkv * nSB;
+    const int plds = PartTile<D>::lds_bytes((a.G + 31) & ~31);
+    hipLaunchKernelGGL((sparse_kv_partial_kernel<D>), dim3((unsigned)pblocks), dim3(kSpPartThreads), plds, stream,
+                       a);
+    hipLaunchKernelGGL(sp_count, dim3((unsigned)(a.B * a.nchunks)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sp_scan_chunks, dim3((unsigned)(((size_t)a.B * a.N + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sp_scan_rows, dim3((unsigned)a.B), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(sp_scatter, dim3((unsigned)(a.B * a.nchunks)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sp_reduce<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.N)), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return hipSuccess;
+}
+
+}  // namespace
+
+int sparse_tokens_per_chunk() { return kSpChunk; }
+int sparse_max_heads_per_kv() { return kSpMaxG; }
+
+// Raise the dynamic-LDS limit of every sparse instance on the current device.
+hipError_t sparse_setup_device() {
+    hipError_t e;
+    if ((e = set_lds(sparse_fwd_kernel<64>, 65536))) return e;
+    if ((e = set_lds(sparse_fwd_kernel<128>, 65536))) return e;
+    if ((e = set_lds(sparse_dq_kernel<64>, 65536))) return e;
+    if ((e = set_lds(sparse_dq_kernel<128>, 65536))) return e;
+    if ((e = set_lds(sparse_kv_partial_kernel<64>, PartTile<64>::lds_bytes(kSpMaxG)))) return e;
+    return set_lds(sparse_kv_partial_kernel<128>, PartTile<128>::lds_bytes(kSpMaxG));
+}
+
+hipError_t launch_sparse_fwd(const SparseArgs& a, int D, hipStream_t stream) {
+    return D == 64 ? launch_fwd_t<64>(a, stream) : launch_fwd_t<128>(a, stream);
+}
+
+hipError_t launch_sparse_bwd(const SparseArgs& a, int D, hipStream_t stream) {
+    return D == 64 ? launch_bwd_t<64>(a, stream) : launch_bwd_t<128>(a, stream);
+}
+
+}  // namespace attn

@@ -40,10 +40,40 @@ struct BwdArgs {
     int precise_tiles;   // dQ query tiles 0 .. precise_tiles-1 take that exact path (set by launch_bwd)
 };
 
+// Sparse attention over per-token index lists (attn_sparse_* entry points).
+struct SparseArgs {
+    const uint16_t* q;       // [B][Hq][S][D]
+    const uint16_t* k;       // [B][Hkv][N][D]
+    const uint16_t* v;       // [B][Hkv][N][D]
+    const int32_t* idx;      // [B][S][topk]; entries outside [0, N) are empty slots
+    const uint16_t* o;       // backward: the forward's output
+    const uint16_t* dout;    // backward: [B][Hq][S][D]
+    uint16_t* out;           // forward output [B][Hq][S][D]
+    float* lse;              // [B][Hq][S] (written by the forward, read by the backward)
+    float* dq;               // [B][Hq][S][D]
+    float* dk;               // [B][Hkv][N][D]
+    float* dv;
+    // backward workspace
+    float* delta;            // [B][Hq][S]
+    float* inter_k;          // [B][Hkv][S][topk][D]: scale * dS^T Q per (token, slot)
+    float* inter_v;          // [B][Hkv][S][topk][D]: P^T dO per (token, slot)
+    int* cnt;                // [B][nchunks][N]: per-chunk row counts, then chunk bases
+    int* rowstart;           // [B][N+1]: start of each row's entries in `list`
+    int* list;               // [B][S*topk]: entries i*topk + s grouped by row, token order
+    int B, Hq, Hkv, S, N, G, topk, nchunks;
+    float scale;             // signed scale (backward)
+    float scale_log2;        // forward: max(|scale| * log2(e), 2^-100); backward: scale * log2(e)
+    uint32_t q_sign;         // forward: 0x80008000 when scale < 0, else 0
+    int precise_all;         // every workgroup takes the exact (split P / dS) path
+};
+
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 // D: query/key head dimension, DV: value head dimension (each 64 or 128).
 hipError_t launch_fwd(const FwdArgs& a, int D, int DV, hipStream_t stream);
 // stages: bit 0 = dQ and delta, bit 1 = dK/dV (in that order when both are set)
 hipError_t launch_bwd(const BwdArgs& a, int D, int DV, int stages, hipStream_t stream);
+// D: head dimension (64 or 128); G = Hq / Hkv <= 128.
+hipError_t launch_sparse_fwd(const SparseArgs& a, int D, hipStream_t stream);
+hipError_t launch_sparse_bwd(const SparseArgs& a, int D, hipStream_t stream);
 
 }  // namespace attn

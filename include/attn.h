@@ -52,7 +52,8 @@ enum attn_status {
     ATTN_ERR_SCALE = 7,         /* scale is NaN or infinite */
     ATTN_ERR_HIP = 8,           /* the HIP runtime failed (no device, launch error) */
     ATTN_ERR_DEVICE = 9,        /* the current device is not a gfx950 GPU */
-    ATTN_ERR_WINDOW = 10        /* a sliding window of fewer than 1 key (vdim: < 0, or set without causal) */
+    ATTN_ERR_WINDOW = 10,       /* a sliding window of fewer than 1 key (vdim: < 0, or set without causal) */
+    ATTN_ERR_SPARSE = 11        /* sparse: topk > 4096, Hq/Hkv > 128, N*D or S*topk >= 2^31 */
 };
 
 /*
@@ -162,6 +163,44 @@ int attn_bwd_vdim(const void* q, const void* k, const void* v, const void* o, co
                   const void* dout, float* dq, float* dk, float* dv,
                   int B, int Hq, int Hkv, int S, int D, int Dv, int causal, int window,
                   float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse attention over per-token index lists: the compressed sparse attention
+ * of the same page (section 2.1; Table 7 gives its list shapes) gives every
+ * query token a top-k list of key/value rows, a sliding window of recent tokens
+ * plus rows of a compressed pool. The forward gathers the listed rows, scores
+ * them and streams their values into the output: Eq. (1) restricted to the
+ * token's list, one term per list slot. The backward gathers the same rows for
+ * dQ, forms one dK/dV contribution per (token, slot), and reduces those by the
+ * inverse of the index map (section 2.1's description of the CSA backward).
+ *   q, o, dout, dq [B][Hq][S][D]   (o, dout bf16; dq fp32)
+ *   k, v           [B][Hkv][N][D] bf16: N key/value rows per kv head (for the
+ *                  compressed attention, the S raw tokens followed by the pool)
+ *   dk, dv         [B][Hkv][N][D] fp32: every row is written (0 where no list
+ *                  names it), summed over the query heads of its group
+ *   idx            [B][S][topk] int32, device memory, shared by all query heads
+ *                  of a token; entry s of token i names row idx[b][i][s]; an
+ *                  entry outside [0, N) is an empty slot. A row listed twice
+ *                  counts twice. The lists carry every causal or window
+ *                  restriction; nothing else masks.
+ *   lse            [B][Hq][S] fp32 (natural log); -inf for a token whose list is
+ *                  empty, whose O row is 0 (and whose dQ row is 0)
+ * D is 64 or 128, topk in [1, 4096], Hq/Hkv <= 128, N*D and S*topk < 2^31
+ * (ATTN_ERR_SPARSE otherwise). attn_sparse_bwd needs o and lse from
+ * attn_sparse_fwd with the same arguments, and a workspace of
+ * attn_sparse_bwd_workspace_bytes() bytes: delta, the per-(token, slot)
+ * contributions (2 * B*Hkv*S*topk*D fp32) and the inverse map; its contents on
+ * entry do not matter. Results are deterministic (no floating-point atomics).
+ * Every other rule is that of attn_fwd / attn_bwd.
+ */
+int attn_sparse_fwd(const void* q, const void* k, const void* v, const int* idx, void* o, float* lse,
+                    int B, int Hq, int Hkv, int S, int N, int D, int topk, float scale,
+                    void* stream);
+size_t attn_sparse_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int N, int D, int topk);
+int attn_sparse_bwd(const void* q, const void* k, const void* v, const int* idx, const void* o,
+                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                    int B, int Hq, int Hkv, int S, int N, int D, int topk, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

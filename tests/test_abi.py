@@ -50,7 +50,7 @@ def test_lds_transpose_library_exports_its_header():
 
 
 def test_status_strings():
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = fa.attn_status_str(code)
         assert isinstance(s, str) and s
     assert fa.attn_status_str(0) == "ok"
@@ -175,6 +175,43 @@ def test_vdim_validates_pointers_and_workspace():
     assert bwd_vdim(wsb=16) == fa.ATTN_ERR_WORKSPACE
 
 
+def sp_fwd(*, idx=P, B=1, Hq=8, Hkv=1, S=256, N=320, D=128, topk=64, scale=0.088):
+    return fa.load_library().attn_sparse_fwd(P, P, P, idx, P, P, B, Hq, Hkv, S, N, D, topk, scale, None)
+
+
+def sp_bwd(*, dk=P, B=1, Hq=8, Hkv=1, S=256, N=320, D=128, topk=64, scale=0.088, wsb=None, ws=P):
+    lib = fa.load_library()
+    if wsb is None:
+        wsb = lib.attn_sparse_bwd_workspace_bytes(B, Hq, Hkv, S, N, D, topk)
+    return lib.attn_sparse_bwd(P, P, P, P, P, P, P, P, dk, P, B, Hq, Hkv, S, N, D, topk, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), fa.ATTN_ERR_SHAPE), (dict(topk=0), fa.ATTN_ERR_SHAPE), (dict(S=0), fa.ATTN_ERR_SHAPE),
+    (dict(D=96), fa.ATTN_ERR_UNSUPPORTED_D), (dict(Hq=6, Hkv=4), fa.ATTN_ERR_GQA),
+    (dict(topk=4097), fa.ATTN_ERR_SPARSE), (dict(Hq=256, Hkv=1), fa.ATTN_ERR_SPARSE),
+    (dict(N=1 << 24), fa.ATTN_ERR_SPARSE), (dict(S=1 << 20, topk=4096), fa.ATTN_ERR_SPARSE),
+    (dict(scale=math.inf), fa.ATTN_ERR_SCALE),
+])
+def test_sparse_rejects(kw, code):
+    assert sp_fwd(**kw) == code
+    assert sp_bwd(**kw) == code
+
+
+def test_sparse_validates_pointers_and_workspace():
+    lib = fa.load_library()
+    assert sp_fwd(idx=None) == fa.ATTN_ERR_NULL
+    assert sp_fwd(idx=MIS) == fa.ATTN_ERR_ALIGN
+    assert sp_bwd(dk=None) == fa.ATTN_ERR_NULL
+    assert sp_bwd(dk=MIS) == fa.ATTN_ERR_ALIGN
+    need = lib.attn_sparse_bwd_workspace_bytes(1, 8, 1, 256, 320, 128, 64)
+    # delta, two contribution arrays of S*topk*D fp32, the inverse map
+    assert need >= 8 * 256 * 4 + 2 * 256 * 64 * 128 * 4 + 256 * 64 * 4
+    assert sp_bwd(wsb=need - 1) == fa.ATTN_ERR_WORKSPACE
+    assert sp_bwd(ws=None) == fa.ATTN_ERR_WORKSPACE
+    assert lib.attn_sparse_bwd_workspace_bytes(1, 8, 1, 256, 320, 128, 0) == 0
+
+
 def test_no_gpu_reports_hip_error():
     """Valid arguments on a machine without a usable gfx950 device end in a HIP or device
     error from the set-up step, never in a launch."""
@@ -185,3 +222,4 @@ def test_no_gpu_reports_hip_error():
     assert fwd_window() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
     assert fwd_vdim() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
     assert fwd_vdim(D=64, Dv=128, window=16) in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
+    assert sp_fwd() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
