@@ -418,23 +418,119 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
 // ---------------------------------------------------------------------------
 template <int D>
 struct PartTile {
-    // Q and dO tiles [Gp][D] of the token's query heads, the V rows of the
+    // Q and dO tiles [Gp][D] of the token's query heads and the V rows of the
     // workgroup's 128 slots [128][D], all in swz<D> order; lse*log2e and delta
     // per head.
-    static int lds_bytes(int Gp) { return (2 * Gp * D + kSpSlotsPerWG * D) * 2 + 2 * Gp * 4 + 16; }
+    __host__ __device__ static int tile_bytes(int Gp) { return (2 * Gp * D + kSpSlotsPerWG * D) * 2; }
+    __host__ __device__ static int lds_bytes(int Gp) { return tile_bytes(Gp) + 2 * Gp * 4 + 16; }
 };
 
-template <int D>
-__global__ void __launch_bounds__(kSpPartThreads, 1) sparse_kv_partial_kernel(SparseArgs a) {
-    constexpr int DK = D / 16;
+// One of the two products of this wave's 32 slots, summed over every head of the
+// token, as a [slot][d] accumulator (lane = column d, registers = slots
+// 8(r/4) + 4h + r%4):
+//   DK = false:  dV = P^T dO
+//   DK = true:   dK = dS^T Q   (without the scale)
+// Each pass recomputes S (and dP for dK) for the token's heads in groups of 32:
+// two accumulators do not fit in the registers of two waves per SIMD, one does.
+// P^T / dS^T are the A operands straight from the score registers (lane = slot,
+// heads as contraction index in the order the score layout gives); dO / Q are
+// the B operands, read with transpose loads in that same head order.
+template <int D, bool PRECISE, bool DK>
+__device__ __forceinline__ void part_product(const __bf16* Qt, const __bf16* Dt, const __bf16* Vt,
+                                             const float* Ls, const float* Dl, const bf16x8 (&kf)[D / 16],
+                                             bool valid, int wave, int lane, int Gp, float c,
+                                             f32x16 (&acc)[D / 32]) {
+    constexpr int NK = D / 16;
     constexpr int DB = D / 32;
+    const int h = lane >> 5, l32 = lane & 31;
+    int roff[NK], toff[2][DB];
+#pragma unroll
+    for (int d = 0; d < NK; ++d) roff[d] = swz<D>(l32, d * 16 + 8 * h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = zero16();
+    const __bf16* Bt = DK ? Qt : Dt;   // B operand tile of the product
+    for (int hs = 0; hs < Gp / 32; ++hs) {
+        // rows of s / dp are heads 32 hs + 8(r/4) + 4h + r%4; the column is this lane's slot
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int dd = 0; dd < NK; ++dd) {
+            s = mfma32(lds_read8(Qt + hs * 32 * D + roff[dd]), kf[dd], s);
+            if (DK) dp = mfma32(lds_read8(Dt + hs * 32 * D + roff[dd]), lds_read8(Vt + wave * 32 * D + roff[dd]), dp);
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            float x[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int rg = 2 * t2 + half;
+                const f32x4 l4 = *(const f32x4*)(Ls + hs * 32 + 8 * rg + 4 * h);
+                f32x4 d4;
+                if (DK) d4 = *(const f32x4*)(Dl + hs * 32 + 8 * rg + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = valid ? fast_exp2(fmaf(s[4 * rg + e], c, -l4[e])) : 0.0f;
+                    x[4 * half + e] = DK ? p * (dp[4 * rg + e] - d4[e]) : p;
+                }
+            }
+            const bf16x8 xh = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+            bf16x8 xl;
+            if (PRECISE)
+                xl = pack8(bf_lo(x[0]), bf_lo(x[1]), bf_lo(x[2]), bf_lo(x[3]), bf_lo(x[4]), bf_lo(x[5]),
+                           bf_lo(x[6]), bf_lo(x[7]));
+            const int rb = (hs * 32 + 16 * t2) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 bt = concat(lds_read_tr(Bt + toff[0][db] + rb), lds_read_tr(Bt + toff[1][db] + rb));
+                acc[db] = mfma32(xh, bt, acc[db]);
+                if (PRECISE) acc[db] = mfma32(xl, bt, acc[db]);
+            }
+        }
+    }
+}
+
+// Store a [slot][d] accumulator (lane = column) times `mul` into rows
+// dst[slot][0..D) for slots < nslots: each store writes two 128-byte row pieces.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mul, float* dst, int nslots,
+                                           int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int slot = 8 * (r >> 2) + 4 * h + (r & 3);
+        if (slot < nslots) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) dst[(size_t)slot * D + db * 32 + l32] = acc[db][r] * mul;
+        }
+    }
+}
+
+template <int D, bool PRECISE>
+__device__ __forceinline__ void part_both(const __bf16* Qt, const __bf16* Dt, const __bf16* Vt, const float* Ls,
+                                          const float* Dl, const bf16x8 (&kf)[D / 16], bool valid, int wave,
+                                          int lane, int Gp, const SparseArgs& a, size_t e0, int nslots) {
+    f32x16 acc[D / 32];
+    part_product<D, PRECISE, false>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a.scale_log2, acc);
+    store_rows<D>(acc, 1.0f, a.inter_v + e0 * D, nslots, lane);
+    part_product<D, PRECISE, true>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a.scale_log2, acc);
+    store_rows<D>(acc, a.scale, a.inter_k + e0 * D, nslots, lane);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(SparseArgs a) {
+    constexpr int NK = D / 16;
     constexpr int CH = D / 8, RPC = 64 / CH;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     const int G = a.G, Gp = (G + 31) & ~31;
     __bf16* const Qt = (__bf16*)lds_raw;
     __bf16* const Dt = Qt + Gp * D;
     __bf16* const Vt = Dt + Gp * D;
-    float* const Ls = (float*)(Vt + kSpSlotsPerWG * D);
+    float* const Ls = (float*)(lds_raw + PartTile<D>::tile_bytes(Gp));
     float* const Dl = Ls + Gp;
     int* const cnt = (int*)(Dl + Gp);
 
@@ -449,7 +545,8 @@ __global__ void __launch_bounds__(kSpPartThreads, 1) sparse_kv_partial_kernel(Sp
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int32_t* lst = a.idx + ((size_t)b * a.S + i) * a.topk;
-    const int slot = sb * kSpSlotsPerWG + 32 * wave + l32;   // this lane's list slot
+    const int slot0 = sb * kSpSlotsPerWG + 32 * wave;        // this wave's first list slot
+    const int slot = slot0 + l32;                            // this lane's list slot
     const int jraw = slot < a.topk ? lst[slot] : -1;
     const bool valid = slot_valid(jraw, a.N);
     const int j = valid ? jraw : 0;
@@ -458,7 +555,7 @@ __global__ void __launch_bounds__(kSpPartThreads, 1) sparse_kv_partial_kernel(Sp
     if (tid == 0) *cnt = 0;
     __syncthreads();
     int mine = 0;
-    for (int s = tid; s < a.topk; s += kSpPartThreads) mine += slot_valid(lst[s], a.N) ? 1 : 0;
+    for (int s2 = tid; s2 < a.topk; s2 += kSpPartThreads) mine += slot_valid(lst[s2], a.N) ? 1 : 0;
     if (mine) atomicAdd(cnt, mine);
 
     // Q / dO rows of the token's heads (rows past G repeat head G-1; their lse is
@@ -485,101 +582,23 @@ __global__ void __launch_bounds__(kSpPartThreads, 1) sparse_kv_partial_kernel(Sp
         Dl[g] = g < G ? a.delta[r] : 0.0f;
     }
     // this lane's K row as B operands
-    bf16x8 kf[DK];
+    bf16x8 kf[NK];
     {
         const u32x4* ks = (const u32x4*)(a.k + kvbase + (size_t)j * D + 8 * h);
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) kf[dk] = __builtin_bit_cast(bf16x8, ks[2 * dk]);
+        for (int d = 0; d < NK; ++d) kf[d] = __builtin_bit_cast(bf16x8, ks[2 * d]);
     }
     wait_copies();
     __syncthreads();
     const bool precise = a.precise_all || *cnt <= kSpPreciseSlots;
-    const float c = a.scale_log2;  // signed
+    if (__ballot(valid) == 0) return;  // no non-empty slot in this wave (no barrier follows)
 
-    if (__ballot(valid) == 0) return;  // no non-empty slot in this wave
-
-    int roff[DK], toff[2][DB];
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
-                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-
-    f32x16 dk[DB], dv[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        dk[db] = zero16();
-        dv[db] = zero16();
-    }
-    for (int hs = 0; hs < Gp / 32; ++hs) {
-        // S and dP of 32 heads x this wave's 32 slots; rows are heads
-        // 32 hs + 8(r/4) + 4h + r%4, the column is this lane's slot.
-        f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int dd = 0; dd < DK; ++dd) {
-            const bf16x8 qa = lds_read8(Qt + hs * 32 * D + roff[dd]);
-            const bf16x8 da = lds_read8(Dt + hs * 32 * D + roff[dd]);
-            const bf16x8 vb = lds_read8(Vt + wave * 32 * D + roff[dd]);
-            s = mfma32(qa, kf[dd], s);
-            dp = mfma32(da, vb, dp);
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-            float pv[8], dsv[8];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int rg = 2 * t2 + half;
-                const f32x4 l4 = *(const f32x4*)(Ls + hs * 32 + 8 * rg + 4 * h);
-                const f32x4 d4 = *(const f32x4*)(Dl + hs * 32 + 8 * rg + 4 * h);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = valid ? fast_exp2(fmaf(s[4 * rg + e], c, -l4[e])) : 0.0f;
-                    pv[4 * half + e] = p;
-                    dsv[4 * half + e] = p * (dp[4 * rg + e] - d4[e]);
-                }
-            }
-            const bf16x8 ph = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-            const bf16x8 sh = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-            const bf16x8 pl = pack8(bf_lo(pv[0]), bf_lo(pv[1]), bf_lo(pv[2]), bf_lo(pv[3]), bf_lo(pv[4]),
-                                    bf_lo(pv[5]), bf_lo(pv[6]), bf_lo(pv[7]));
-            const bf16x8 sl = pack8(bf_lo(dsv[0]), bf_lo(dsv[1]), bf_lo(dsv[2]), bf_lo(dsv[3]),
-                                    bf_lo(dsv[4]), bf_lo(dsv[5]), bf_lo(dsv[6]), bf_lo(dsv[7]));
-            const int rb = (hs * 32 + 16 * t2) * D;
-            // dV^T += dO^T P and dK^T += Q^T dS over 16 heads; dO^T, Q^T by transpose loads
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16x8 dot = concat(lds_read_tr(Dt + toff[0][db] + rb), lds_read_tr(Dt + toff[1][db] + rb));
-                const bf16x8 qt = concat(lds_read_tr(Qt + toff[0][db] + rb), lds_read_tr(Qt + toff[1][db] + rb));
-                dv[db] = mfma32(dot, ph, dv[db]);
-                dk[db] = mfma32(qt, sh, dk[db]);
-                if (precise) {
-                    dv[db] = mfma32(dot, pl, dv[db]);
-                    dk[db] = mfma32(qt, sl, dk[db]);
-                }
-            }
-        }
-    }
-    if (valid) {
-        const size_t e = (((size_t)b * a.Hkv + hkv) * a.S + i) * a.topk + slot;
-        float* ok = a.inter_k + e * D;
-        float* ov = a.inter_v + e * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                f32x4 vk, vv;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    vk[q] = dk[db][4 * g4 + q] * a.scale;
-                    vv[q] = dv[db][4 * g4 + q];
-                }
-                *(f32x4*)(ok + db * 32 + 8 * g4 + 4 * h) = vk;
-                *(f32x4*)(ov + db * 32 + 8 * g4 + 4 * h) = vv;
-            }
-    }
+    const int nslots = min(32, a.topk - slot0);  // rows of this wave inside the token's list
+    const size_t e0 = (((size_t)b * a.Hkv + hkv) * a.S + i) * a.topk + slot0;
+    if (precise)
+        part_both<D, true>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a, e0, nslots);
+    else
+        part_both<D, false>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a, e0, nslots);
 }
 
 // ---------------------------------------------------------------------------
@@ -608,11 +627,22 @@ __global__ void __launch_bounds__(256) sp_scan_chunks(SparseArgs a) {
     const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (x >= (size_t)a.B * a.N) return;
     const int b = (int)(x / a.N), j = (int)(x % a.N);
+    int* col = a.cnt + (size_t)b * a.nchunks * a.N + j;   // chunk ch at col[ch * N]
     int run = 0;
-    for (int ch = 0; ch < a.nchunks; ++ch) {
-        int* p = a.cnt + ((size_t)b * a.nchunks + ch) * a.N + j;
-        const int v = *p;
-        *p = run;
+    int ch = 0;
+    for (; ch + 16 <= a.nchunks; ch += 16) {  // sixteen loads in flight, then the running sum
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = col[(size_t)(ch + u) * a.N];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            col[(size_t)(ch + u) * a.N] = run;
+            run += v[u];
+        }
+    }
+    for (; ch < a.nchunks; ++ch) {
+        const int v = col[(size_t)ch * a.N];
+        col[(size_t)ch * a.N] = run;
         run += v;
     }
     a.rowstart[(size_t)b * (a.N + 1) + j] = run;
