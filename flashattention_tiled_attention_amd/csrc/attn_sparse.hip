@@ -284,6 +284,7 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
 
     const int n = compact_list(a.idx + ((size_t)b * a.S + i) * a.topk, a.topk, a.N, list, red);
     const bool precise = a.precise_all || n <= kSpPreciseSlots;
+    if (hb == 0 && hkv == 0 && tid == 0) a.ntok[(size_t)b * a.S + i] = n;  // for the next stage
 
     // Q and dO rows as B operands; delta = rowsum(dO * O) from the stored O.
     bf16x8 qf[DK], df[DK];
@@ -422,7 +423,7 @@ struct PartTile {
     // workgroup's 128 slots [128][D], all in swz<D> order; lse*log2e and delta
     // per head.
     __host__ __device__ static int tile_bytes(int Gp) { return (2 * Gp * D + kSpSlotsPerWG * D) * 2; }
-    __host__ __device__ static int lds_bytes(int Gp) { return tile_bytes(Gp) + 2 * Gp * 4 + 16; }
+    __host__ __device__ static int lds_bytes(int Gp) { return tile_bytes(Gp) + 2 * Gp * 4; }
 };
 
 // One of the two products of this wave's 32 slots, summed over every head of the
@@ -532,7 +533,6 @@ __global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(Sp
     __bf16* const Vt = Dt + Gp * D;
     float* const Ls = (float*)(lds_raw + PartTile<D>::tile_bytes(Gp));
     float* const Dl = Ls + Gp;
-    int* const cnt = (int*)(Dl + Gp);
 
     const int nSB = (a.topk + kSpSlotsPerWG - 1) / kSpSlotsPerWG;
     int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nSB);
@@ -551,12 +551,8 @@ __global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(Sp
     const bool valid = slot_valid(jraw, a.N);
     const int j = valid ? jraw : 0;
 
-    // number of non-empty slots of the token (for the exact-path choice)
-    if (tid == 0) *cnt = 0;
-    __syncthreads();
-    int mine = 0;
-    for (int s2 = tid; s2 < a.topk; s2 += kSpPartThreads) mine += slot_valid(lst[s2], a.N) ? 1 : 0;
-    if (mine) atomicAdd(cnt, mine);
+    // the token's number of non-empty slots (from the dQ stage) picks the exact path
+    const bool precise = a.precise_all || a.ntok[(size_t)b * a.S + i] <= kSpPreciseSlots;
 
     // Q / dO rows of the token's heads (rows past G repeat head G-1; their lse is
     // +inf, so they add exactly 0), and the V rows of this workgroup's slots.
@@ -590,7 +586,6 @@ __global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(Sp
     }
     wait_copies();
     __syncthreads();
-    const bool precise = a.precise_all || *cnt <= kSpPreciseSlots;
     if (__ballot(valid) == 0) return;  // no non-empty slot in this wave (no barrier follows)
 
     const int nslots = min(32, a.topk - slot0);  // rows of this wave inside the token's list
@@ -691,8 +686,11 @@ __global__ void __launch_bounds__(256) sp_scatter(SparseArgs a) {
 }
 
 // dK, dV of row (b, hkv, j): the sum of its entries' contributions in list order.
-// Wave w sums entries w, w+4, ... (four at a time in flight); the four partial
-// sums are then added in wave order. Lane l holds columns 2l, 2l+1.
+// The row's entries are split into four contiguous quarters, one per wave; a wave
+// reads 64 entry numbers at once (one per lane) and then walks them eight at a
+// time, the entry number broadcast from a scalar register, so sixteen row loads
+// are in flight. The four partial sums are added in wave order. Lane l holds
+// columns 2l, 2l+1.
 template <int D>
 __global__ void __launch_bounds__(256) sp_reduce(SparseArgs a) {
     typedef float fv __attribute__((ext_vector_type(2)));
@@ -701,33 +699,40 @@ __global__ void __launch_bounds__(256) sp_reduce(SparseArgs a) {
     const int j = blockIdx.x % a.N;
     const int bh = blockIdx.x / a.N;   // b * Hkv + hkv
     const int b = bh / a.Hkv;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool on = lane < D / PER;  // D = 64 uses 32 lanes of each wave
     const int* rs = a.rowstart + (size_t)b * (a.N + 1);
     const int* ent = a.list + (size_t)b * a.S * a.topk;
     const int e0 = rs[j], e1 = rs[j + 1];
-    const float* ik = a.inter_k + (size_t)bh * a.S * a.topk * D + lane * PER;
-    const float* iv = a.inter_v + (size_t)bh * a.S * a.topk * D + lane * PER;
+    const int quarter = (e1 - e0 + 3) / 4;
+    const int w0 = min(e1, e0 + wave * quarter), w1 = min(e1, w0 + quarter);
+    const float* ik = a.inter_k + (size_t)bh * a.S * a.topk * D + (on ? lane * PER : 0);
+    const float* iv = a.inter_v + (size_t)bh * a.S * a.topk * D + (on ? lane * PER : 0);
     fv sk = {}, sv = {};
-    int e = on ? e0 + wave : e1;
-    for (; e + 12 < e1; e += 16) {
-        fv k4[4], v4[4];
+    for (int base = w0; base < w1; base += 64) {
+        const int cntb = min(64, w1 - base);
+        const int mine = lane < cntb ? ent[base + lane] : 0;
+        int u = 0;
+        for (; u + 8 <= cntb; u += 8) {
+            fv k8[8], v8[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const size_t x = (size_t)ent[e + 4 * u] * D;
-            k4[u] = *(const fv*)(ik + x);
-            v4[u] = *(const fv*)(iv + x);
-        }
+            for (int t = 0; t < 8; ++t) {
+                const size_t x = (size_t)__builtin_amdgcn_readlane(mine, u + t) * D;
+                k8[t] = *(const fv*)(ik + x);
+                v8[t] = *(const fv*)(iv + x);
+            }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            sk += k4[u];
-            sv += v4[u];
+            for (int t = 0; t < 8; ++t) {
+                sk += k8[t];
+                sv += v8[t];
+            }
         }
-    }
-    for (; e < e1; e += 4) {
-        const size_t x = (size_t)ent[e] * D;
-        sk += *(const fv*)(ik + x);
-        sv += *(const fv*)(iv + x);
+        for (; u < cntb; ++u) {
+            const size_t x = (size_t)__builtin_amdgcn_readlane(mine, u) * D;
+            sk += *(const fv*)(ik + x);
+            sv += *(const fv*)(iv + x);
+        }
     }
     part[0][wave][lane] = sk;
     part[1][wave][lane] = sv;
