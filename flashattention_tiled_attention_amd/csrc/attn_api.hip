@@ -91,11 +91,10 @@ int check_sparse_sizes(int B, int Hq, int Hkv, int S, int N, int D, int topk) {
     return ATTN_OK;
 }
 
-// Backward workspace: delta, the two per-(token, slot) contribution arrays, the
-// inverse of the index map (chunk counts, row starts, entry list) and the
-// per-token count of non-empty slots.
+// Backward workspace: delta, the two per-(token, slot) contribution arrays, and
+// the inverse of the index map (chunk counts, row starts, entry list).
 struct SparseWs {
-    size_t delta, inter_k, inter_v, cnt, rowstart, list, ntok, total;
+    size_t delta, inter_k, inter_v, cnt, rowstart, list, total;
     int nchunks;
 };
 
@@ -110,7 +109,6 @@ SparseWs sparse_ws(int B, int Hq, int Hkv, int S, int N, int D, int topk) {
     w.cnt = off;      off += al((size_t)B * w.nchunks * N * 4);
     w.rowstart = off; off += al((size_t)B * (N + 1) * 4);
     w.list = off;     off += al((size_t)B * S * topk * 4);
-    w.ntok = off;     off += al((size_t)B * S * 4);
     w.total = off;
     return w;
 }
@@ -345,7 +343,6 @@ int attn_sparse_bwd(const void* q, const void* k, const void* v, const int* idx,
     a.cnt = (int*)(ws + w.cnt);
     a.rowstart = (int*)(ws + w.rowstart);
     a.list = (int*)(ws + w.list);
-    a.ntok = (int*)(ws + w.ntok);
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.N = N; a.G = Hq / Hkv; a.topk = topk;
     a.nchunks = w.nchunks;
     a.scale = scale;

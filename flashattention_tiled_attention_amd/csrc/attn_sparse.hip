@@ -34,9 +34,10 @@
 //
 // The sum over a token's query heads happens inside the partial kernel's MFMAs
 // (the heads are their contraction index), so the per-slot contribution is one
-// D-vector per kv head. Rows that see few keys (at most 256 non-empty slots)
-// take the exact path of the dense kernels: P and dS split into a bf16 high
-// part and a bf16 remainder, and delta recomputed as sum_s P dP.
+// D-vector per kv head. In the forward and dQ kernels, rows that see few keys (at
+// most 256 non-empty slots) take the exact path of the dense kernels: P and dS
+// split into a bf16 high part and a bf16 remainder, and delta recomputed as
+// sum_s P dP. The per-slot contributions always take the split P and dS.
 #include "device.h"
 #include "kernels.h"
 
@@ -64,21 +65,33 @@ __device__ __forceinline__ int xcd_item(int bid, int total) {
 }
 
 // Compact the token's list into LDS: the non-empty entries in slot order.
-// Returns their number (the same in every lane). 128 threads; red: 2 LDS ints.
+// Returns their number (the same in every lane). 128 threads; red: 16 LDS ints.
+// Entries are read eight 128-entry rounds at a time, all loads in flight together;
+// each round's two wave counts go to LDS, and one barrier per batch publishes them.
 __device__ __forceinline__ int compact_list(const int32_t* src, int topk, int N, int* out, int* red) {
+    constexpr int R = 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int total = 0;
-    for (int base = 0; base < topk; base += kSpThreads) {
-        const int s = base + tid;
-        const int j = s < topk ? src[s] : -1;
-        const bool ok = slot_valid(j, N);
-        const unsigned long long m = __ballot(ok);
-        const int before = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) red[wave] = __popcll(m);
+    for (int base = 0; base < topk; base += R * kSpThreads) {
+        int j[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int s = base + r * kSpThreads + tid;
+            j[r] = s < topk ? src[s] : -1;
+        }
+        unsigned long long m[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            m[r] = __ballot(slot_valid(j[r], N));
+            if (lane == 0) red[2 * r + wave] = __popcll(m[r]);
+        }
         __syncthreads();
-        const int c0 = red[0], c1 = red[1];
-        if (ok) out[total + (wave ? c0 : 0) + before] = j;
-        total += c0 + c1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int c0 = red[2 * r], c1 = red[2 * r + 1];
+            if (slot_valid(j[r], N)) out[total + (wave ? c0 : 0) + __popcll(m[r] & ((1ull << lane) - 1ull))] = j[r];
+            total += c0 + c1;
+        }
         __syncthreads();
     }
     return total;
@@ -89,7 +102,7 @@ struct SpTile {
     static constexpr int TILE = kSpBK * D;                     // elements
     static constexpr int KV_BYTES = 4 * TILE * 2;             // 2 K slots + 2 V slots
     using Copy = CopyPlan<D, kSpBK, 2>;
-    static int lds_bytes(int topk) { return KV_BYTES + ((topk * 4 + 15) & ~15) + 16; }
+    static int lds_bytes(int topk) { return KV_BYTES + ((topk * 4 + 15) & ~15) + 64; }
 };
 
 // ---------------------------------------------------------------------------
@@ -284,7 +297,6 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
 
     const int n = compact_list(a.idx + ((size_t)b * a.S + i) * a.topk, a.topk, a.N, list, red);
     const bool precise = a.precise_all || n <= kSpPreciseSlots;
-    if (hb == 0 && hkv == 0 && tid == 0) a.ntok[(size_t)b * a.S + i] = n;  // for the next stage
 
     // Q and dO rows as B operands; delta = rowsum(dO * O) from the stored O.
     bf16x8 qf[DK], df[DK];
@@ -511,14 +523,18 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mu
     }
 }
 
-template <int D, bool PRECISE>
+// Every contribution takes the split (bf16 high part + remainder) P and dS: one
+// contribution sums up to 128 query heads, and rounding P to bf16 there alone moves
+// dV by up to 1e-2 at the 128-head cr4 shape. The products are cheap next to the
+// stores of this kernel.
+template <int D>
 __device__ __forceinline__ void part_both(const __bf16* Qt, const __bf16* Dt, const __bf16* Vt, const float* Ls,
                                           const float* Dl, const bf16x8 (&kf)[D / 16], bool valid, int wave,
                                           int lane, int Gp, const SparseArgs& a, size_t e0, int nslots) {
     f32x16 acc[D / 32];
-    part_product<D, PRECISE, false>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a.scale_log2, acc);
+    part_product<D, true, false>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a.scale_log2, acc);
     store_rows<D>(acc, 1.0f, a.inter_v + e0 * D, nslots, lane);
-    part_product<D, PRECISE, true>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a.scale_log2, acc);
+    part_product<D, true, true>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a.scale_log2, acc);
     store_rows<D>(acc, a.scale, a.inter_k + e0 * D, nslots, lane);
 }
 
@@ -550,9 +566,6 @@ __global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(Sp
     const int jraw = slot < a.topk ? lst[slot] : -1;
     const bool valid = slot_valid(jraw, a.N);
     const int j = valid ? jraw : 0;
-
-    // the token's number of non-empty slots (from the dQ stage) picks the exact path
-    const bool precise = a.precise_all || a.ntok[(size_t)b * a.S + i] <= kSpPreciseSlots;
 
     // Q / dO rows of the token's heads (rows past G repeat head G-1; their lse is
     // +inf, so they add exactly 0), and the V rows of this workgroup's slots.
@@ -590,10 +603,7 @@ __global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(Sp
 
     const int nslots = min(32, a.topk - slot0);  // rows of this wave inside the token's list
     const size_t e0 = (((size_t)b * a.Hkv + hkv) * a.S + i) * a.topk + slot0;
-    if (precise)
-        part_both<D, true>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a, e0, nslots);
-    else
-        part_both<D, false>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a, e0, nslots);
+    part_both<D>(Qt, Dt, Vt, Ls, Dl, kf, valid, wave, lane, Gp, a, e0, nslots);
 }
 
 // ---------------------------------------------------------------------------

@@ -60,7 +60,6 @@ struct SparseArgs {
     int* cnt;                // [B][nchunks][N]: per-chunk row counts, then chunk bases
     int* rowstart;           // [B][N+1]: start of each row's entries in `list`
     int* list;               // [B][S*topk]: entries i*topk + s grouped by row, token order
-    int* ntok;               // [B][S]: non-empty slots of each token's list (written by the dQ stage)
     int B, Hq, Hkv, S, N, G, topk, nchunks;
     float scale;             // signed scale (backward)
     float scale_log2;        // forward: max(|scale| * log2(e), 2^-100); backward: scale * log2(e)

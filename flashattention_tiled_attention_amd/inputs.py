@@ -95,4 +95,10 @@ CONFIGS = {
     # pool rows), one K/V head shared by all query heads, synthetic lists
     "csa_cr4_flash_s4096": dict(B=1, Hq=64, Hkv=1, S=4096, D=128, causal=False, sparse=True, window=128,
                                 ratio=4, pool_topk=512, bwd=True),
+    # the cr128 shape (window + every visible row of an S/128 pool) and the cr4 "Pro"
+    # shape (128 heads, window + top-1024 of S/4 pool rows), same recipe
+    "csa_cr128_flash_s4096": dict(B=1, Hq=64, Hkv=1, S=4096, D=128, causal=False, sparse=True, window=128,
+                                  ratio=128, pool_topk=32, bwd=True),
+    "csa_cr4_pro_s4096": dict(B=1, Hq=128, Hkv=1, S=4096, D=128, causal=False, sparse=True, window=128,
+                              ratio=4, pool_topk=1024, bwd=True),
 }

@@ -128,15 +128,18 @@ def test_deterministic():
         assert torch.equal(x, y)
 
 
-def test_full_size_csa_cr4_sampled():
-    """The cr4 "Flash" shape (64 query heads on one K/V head, S=4096, lists of a 128-token
-    window plus top-512 of 1024 pool rows): O/lse and dQ on sampled rows, dK/dV on
-    sampled window and pool rows, plus sum_j dV_j = sum of dO and sum_j dK_j = 0."""
-    c = CONFIGS["csa_cr4_flash_s4096"]
+@pytest.mark.parametrize("name", ["csa_cr4_flash_s4096", "csa_cr128_flash_s4096", "csa_cr4_pro_s4096"])
+def test_full_size_csa_sampled(name):
+    """The compressed-sparse-attention shapes at S=4096 (cr4 "Flash": 64 query heads on one
+    K/V head, a 128-token window plus top-512 of 1024 pool rows; cr128: the window plus
+    every visible row of a 32-row pool; cr4 "Pro": 128 heads, top-1024): O/lse and dQ on
+    sampled rows, dK/dV on sampled window and pool rows, plus sum_j dV_j = sum of dO and
+    sum_j dK_j = 0."""
+    c = CONFIGS[name]
     B, Hq, Hkv, S, D = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"]
     idx, N = csa_index_lists(B, S, c["window"], c["ratio"], c["pool_topk"], seed=0)
-    print("case full-size csa cr4 B=%d Hq=%d Hkv=%d S=%d N=%d D=%d topk=%d"
-          % (B, Hq, Hkv, S, N, D, idx.shape[2]), flush=True)
+    print("case full-size %s B=%d Hq=%d Hkv=%d S=%d N=%d D=%d topk=%d"
+          % (name, B, Hq, Hkv, S, N, D, idx.shape[2]), flush=True)
     q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, seed=0, with_dout=True)
     scale = 1.0 / math.sqrt(D)
     o, lse, dq, dk, dv = run(q, k, v, idx, do, scale)
@@ -154,9 +157,9 @@ def test_full_size_csa_cr4_sampled():
     assert_close(dv.reshape(-1, D)[kvrows], rv, "dV (%d sampled keys)" % kvrows.size)
     # Invariants over the whole output, a check for gross errors of the inverse map (a
     # misplaced chunk moves these sums by O(1) or more). Their rounding noise: each of
-    # the 262144 query rows carries P rounded to bf16, so sum_s P differs from 1 by
+    # the 262144 (524288) query rows carries P rounded to bf16, so sum_s P differs from 1 by
     # about 2^-9/sqrt(3) * sqrt(sum_s P^2), roughly 1e-4 for 100-200 keys; summed over
-    # the rows against unit-variance dO that is about 0.05 per element.
+    # the rows against unit-variance dO that is about 0.05 per element (0.1 with 128 heads).
     dof = bf16_to_f32(do).astype(np.float64)
     assert_close(dv.sum(axis=2), dof.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=(2, 3)), "sum_j dV_j",
                  tol_max=0.5, tol_mean=0.15)
