@@ -301,6 +301,7 @@ int attn_sparse_fwd(const void* q, const void* k, const void* v, const int* idx,
     a.scale_log2 = fmaxf(fabsf(scale) * 1.4426950408889634f, 7.888609052210118e-31f);
     a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
     a.precise_all = fabsf(scale) * sqrtf((float)D) > 2.0f ? 1 : 0;
+    a.max_slack = a.precise_all ? 0.0f : 8.0f;  // exact running maximum for peaked rows
     if (attn::launch_sparse_fwd(a, D, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
 }

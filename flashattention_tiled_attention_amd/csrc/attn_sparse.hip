@@ -211,14 +211,20 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
         float mx = fmaxf(sc[0], sc[1]);
 #pragma unroll
         for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-        const float mnew = fmaxf(m, halves_max(mx) * c);  // c > 0
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        l *= alpha;
+        const float mt = halves_max(mx) * c;  // c > 0
+        // As in the dense forward, the running maximum only moves when some row's
+        // grows by more than max_slack (log2 units): until then every probability is
+        // at most 2^slack, exact enough in fp32 and bf16, and O is not rescaled.
+        if (__any(mt > m + a.max_slack)) {
+            const float mnew = fmaxf(m, mt);
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            l *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
         bf16x8 pk[2], pl[2];
         float rs = 0.0f;
 #pragma unroll

@@ -65,6 +65,7 @@ struct SparseArgs {
     float scale_log2;        // forward: max(|scale| * log2(e), 2^-100); backward: scale * log2(e)
     uint32_t q_sign;         // forward: 0x80008000 when scale < 0, else 0
     int precise_all;         // every workgroup takes the exact (split P / dS) path
+    float max_slack;         // forward: log2 growth of a row maximum tolerated before rescaling O
 };
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
