@@ -45,7 +45,8 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSpBK = 32;            // list slots per gathered K/V tile
+constexpr int kSpBK = 32;            // list slots per gathered K/V tile (dQ)
+constexpr int kSpFwdBK = 32;         // list slots per gathered K/V tile (forward)
 constexpr int kSpRows = 64;          // query heads per forward / dQ workgroup
 constexpr int kSpThreads = 128;      // 2 waves x 32 heads
 constexpr int kSpPreciseSlots = 256; // tokens with at most this many keys take the exact path
@@ -97,11 +98,11 @@ __device__ __forceinline__ int compact_list(const int32_t* src, int topk, int N,
     return total;
 }
 
-template <int D>
+template <int D, int BK = kSpBK>
 struct SpTile {
-    static constexpr int TILE = kSpBK * D;                     // elements
+    static constexpr int TILE = BK * D;                        // elements
     static constexpr int KV_BYTES = 4 * TILE * 2;             // 2 K slots + 2 V slots
-    using Copy = CopyPlan<D, kSpBK, 2>;
+    using Copy = CopyPlan<D, BK, 2>;
     static int lds_bytes(int topk) { return KV_BYTES + ((topk * 4 + 15) & ~15) + 64; }
 };
 
@@ -110,7 +111,9 @@ struct SpTile {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a) {
-    using T = SpTile<D>;
+    constexpr int BK = kSpFwdBK;   // list slots per tile
+    constexpr int NB = BK / 32;    // 32-slot blocks per tile
+    using T = SpTile<D, BK>;
     using C = typename T::Copy;
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
@@ -168,7 +171,7 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
     auto copy_tile = [&](int slot, int t) {
 #pragma unroll
         for (int m = 0; m < C::N; ++m) {
-            const int j = list[min(t * kSpBK + crow[m], n - 1)];
+            const int j = list[min(t * BK + crow[m], n - 1)];
             const uint32_t off = (uint32_t)j * D + ccol[m];
             copy16_to_lds(Kp + off, Kring + slot * T::TILE + (wave * C::N + m) * 512);
             copy16_to_lds(Vp + off, Vring + slot * T::TILE + (wave * C::N + m) * 512);
@@ -189,7 +192,7 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
     for (int db = 0; db < DB; ++db) oacc[db] = zero16();
     float m = -1e30f, l = 0.0f;
 
-    const int nT = (n + kSpBK - 1) / kSpBK;
+    const int nT = (n + BK - 1) / BK;
     if (nT > 0) {
         copy_tile(0, 0);
         wait_copies();
@@ -199,18 +202,26 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
         if (t + 1 < nT) copy_tile((t + 1) & 1, t + 1);
         const __bf16* Ks = Kring + (t & 1) * T::TILE;
         const __bf16* Vs = Vring + (t & 1) * T::TILE;
-        f32x16 sc = zero16();
+        f32x16 sc[NB];
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) sc = mfma32(lds_read8(Ks + koff[dk]), qf[dk], sc);
-        if (t == nT - 1) {  // slot t*32 + 4h + off exists iff off < lim
-            const int lim = n - t * kSpBK - 4 * h;
+        for (int kb = 0; kb < NB; ++kb) sc[kb] = zero16();
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
+        for (int dk = 0; dk < DK; ++dk)
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb) sc[kb] = mfma32(lds_read8(Ks + koff[dk] + kb * 32 * D), qf[dk], sc[kb]);
+        if (t == nT - 1) {  // slot t*BK + 4h + off exists iff off < lim
+            const int lim = n - t * BK - 4 * h;
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sc[kb][r] = -INFINITY;
         }
-        float mx = fmaxf(sc[0], sc[1]);
+        float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
         const float mt = halves_max(mx) * c;  // c > 0
         // As in the dense forward, the running maximum only moves when some row's
         // grows by more than max_slack (log2 units): until then every probability is
@@ -225,14 +236,14 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
-        bf16x8 pk[2], pl[2];
+        bf16x8 pk[2 * NB], pl[2 * NB];
         float rs = 0.0f;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
+        for (int t2 = 0; t2 < 2 * NB; ++t2) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(fmaf(sc[8 * t2 + e], c, -m));
+                p[e] = fast_exp2(fmaf(sc[t2 >> 1][8 * (t2 & 1) + e], c, -m));
                 rs += p[e];
             }
             pk[t2] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -240,9 +251,9 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
                            bf_lo(p[6]), bf_lo(p[7]));
         }
         l += rs;
-        // O^T += V^T P^T over two 16-slot steps; V^T through transpose loads.
+        // O^T += V^T P^T over 16-slot steps; V^T through transpose loads.
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+        for (int t2 = 0; t2 < 2 * NB; ++t2)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const bf16x8 vt = concat(lds_read_tr(Vs + voff[0][db] + 16 * t2 * D),
@@ -772,7 +783,7 @@ template <int D>
 hipError_t launch_fwd_t(const SparseArgs& a, hipStream_t stream) {
     const int nHB = (a.G + kSpRows - 1) / kSpRows;
     const long long blocks = (long long)a.B * a.S * a.Hkv * nHB;
-    const int lds = SpTile<D>::lds_bytes(a.topk);
+    const int lds = SpTile<D, kSpFwdBK>::lds_bytes(a.topk);
     hipLaunchKernelGGL((sparse_fwd_kernel<D>), dim3((unsigned)blocks), dim3(kSpThreads), lds, stream, a);
     return hipGetLastError();
 }
