@@ -97,8 +97,11 @@ __device__ __forceinline__ void decode_item(int bid, int nQ, int qt_first, int B
     hq = (c % Hkv) * G + g;
 }
 
+// One workgroup's share: query rows q0 .. q_last of the kv head that hq reads;
+// this wave takes head hq, rows row0 .. row0+31.
 template <int D, int DV, bool CAUSAL, bool PRECISE>
-__device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, int hq, int qt) {
+__device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, int hq, int q0, int q_last,
+                                         int row0) {
     using T = FwdTile<D, DV>;
     using KC = typename T::KCopy;
     using VC = typename T::VCopy;
@@ -116,10 +119,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     const size_t qbase = qrows * D;
     const uint16_t* Kp = a.k + kvrows * D;
     const uint16_t* Vp = a.v + kvrows * DV;
-    const int q0 = qt * kFwdBQ;
-    // Rows interleave between the groups (group 0: 0-31, 64-95, ...; group 1:
-    // 32-63, 96-127, ...) so both see the same number of causal tiles.
-    const int row0 = q0 + 64 * (wave & 3) + 32 * grp;
     const int qrow = row0 + l32;
     const float c = a.scale_log2;
 
@@ -139,7 +138,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     }
 
     const int nK = (S + kFwdBK - 1) / kFwdBK;
-    const int jend = CAUSAL ? min(nK, (q0 + kFwdBQ - 1) / kFwdBK + 1) : nK;
+    const int jend = CAUSAL ? min(nK, q_last / kFwdBK + 1) : nK;
     int wjend = CAUSAL ? min(jend, (row0 + 31) / kFwdBK + 1) : jend;
     if (row0 >= S) wjend = 0;  // a wave with no live rows only helps load
     // Window: the workgroup's first tile holds the first row's first key, a wave's
@@ -371,30 +370,83 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     }
 }
 
-// Query tiles 0 .. a.precise_tiles-1 take the exact P V product.
+// One head, 256 query rows per workgroup. Query tiles 0 .. a.precise_tiles-1
+// take the exact P V product.
 template <int D, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(kFwdThreads, 1) fwd_kernel(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
     const int nQ = (a.S + kFwdBQ - 1) / kFwdBQ;
     int b, hq, qt;
     decode_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q0 = qt * kFwdBQ;
+    // Rows interleave between the ping-pong groups (group 0: 0-31, 64-95, ...;
+    // group 1: 32-63, 96-127, ...) so both see the same number of causal tiles.
+    const int row0 = q0 + 64 * (wave & 3) + 32 * (wave >> 2);
     if (qt < a.precise_tiles)
-        fwd_body<D, DV, CAUSAL, true>(a, smem, b, hq, qt);
+        fwd_body<D, DV, CAUSAL, true>(a, smem, b, hq, q0, q0 + kFwdBQ - 1, row0);
     else
-        fwd_body<D, DV, CAUSAL, false>(a, smem, b, hq, qt);
+        fwd_body<D, DV, CAUSAL, false>(a, smem, b, hq, q0, q0 + kFwdBQ - 1, row0);
+}
+
+// Heads of one kv head that a sliding-window workgroup takes together.
+__host__ __device__ inline int win_heads(int G) {
+    return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+}
+
+// Sliding window: a band of W keys gives 256 rows of one head about twice the key
+// tiles any one wave needs. Here the 8 waves take HW query heads of one kv head
+// (HW = 8, 4, 2 or 1, a divisor of G) and 8/HW blocks of 32 rows, so a workgroup
+// covers only 32*8/HW rows and every wave uses nearly all of its key tiles.
+// Workgroups whose rows see at most 128 keys (W <= 128, or the first 256 rows)
+// take the exact P V product.
+template <int D, int DV>
+__global__ void __launch_bounds__(kFwdThreads, 1) fwd_win_kernel(FwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+    const int HW = win_heads(a.G), BQ = 32 * (8 / HW);
+    const int nQ = (a.S + BQ - 1) / BQ;
+    const int groups = a.B * a.Hkv * (a.G / HW);   // (b, kv head, head block)
+    int qt, gid;
+    const int bid = blockIdx.x;
+    if ((groups & 7) == 0) {  // a head block stays on one XCD (workgroups are dealt round-robin)
+        const int x = bid & 7, st = bid >> 3, per = groups >> 3;
+        qt = st / per;
+        gid = (st - qt * per) * 8 + x;
+    } else {
+        qt = bid / groups;
+        gid = bid - qt * groups;
+    }
+    const int nblk = a.G / HW;
+    const int b = gid / (a.Hkv * nblk);
+    const int rem = gid - b * (a.Hkv * nblk);
+    const int hkv = rem / nblk, blk = rem - hkv * nblk;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hq = hkv * a.G + blk * HW + wave % HW;
+    const int q0 = qt * BQ;
+    const int row0 = q0 + 32 * (wave / HW);
+    if (a.window <= 128 || q0 < 256)
+        fwd_body<D, DV, true, true>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
+    else
+        fwd_body<D, DV, true, false>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
 }
 
 template <int D, int DV, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
-    // Rows that see at most 128 keys take the exact P V product: every tile of a
-    // window of <= 128 keys, else tile 0 of a causal problem (rows 0..255 see at
-    // most 256 keys; the first 128 of them, the ones that need it, are there) or
-    // the single tile of S <= 128.
+    // Rows that see at most 128 keys take the exact P V product: tile 0 of a
+    // causal problem (rows 0..255 see at most 256 keys; the first 128 of them, the
+    // ones that need it, are there) or the single tile of S <= 128 (windowed
+    // problems: fwd_win_kernel).
     const int nQ = (args.S + kFwdBQ - 1) / kFwdBQ;
     FwdArgs a = args;
-    a.precise_tiles = (CAUSAL && a.window > 0 && a.window <= 128) ? nQ : (CAUSAL || a.S <= 128) ? 1 : 0;
-    const long long blocks = (long long)a.B * a.Hq * nQ;
     constexpr int lds = FwdTile<D, DV>::LDS_BYTES;
+    if (CAUSAL && a.window > 0) {
+        const int HW = win_heads(a.G), BQ = 32 * (8 / HW);
+        const long long wblocks = (long long)((a.S + BQ - 1) / BQ) * a.B * a.Hkv * (a.G / HW);
+        hipLaunchKernelGGL((fwd_win_kernel<D, DV>), dim3((unsigned)wblocks), dim3(kFwdThreads), lds, stream, a);
+        return hipGetLastError();
+    }
+    a.precise_tiles = (CAUSAL || a.S <= 128) ? 1 : 0;
+    const long long blocks = (long long)a.B * a.Hq * nQ;
     hipLaunchKernelGGL((fwd_kernel<D, DV, CAUSAL>), dim3((unsigned)blocks), dim3(kFwdThreads), lds, stream, a);
     return hipGetLastError();
 }
@@ -407,7 +459,8 @@ hipError_t set_lds(K kernel, int bytes) {
 template <int D, int DV>
 hipError_t setup_pair() {
     hipError_t e = set_lds(fwd_kernel<D, DV, false>, FwdTile<D, DV>::LDS_BYTES);
-    return e ? e : set_lds(fwd_kernel<D, DV, true>, FwdTile<D, DV>::LDS_BYTES);
+    if (!e) e = set_lds(fwd_kernel<D, DV, true>, FwdTile<D, DV>::LDS_BYTES);
+    return e ? e : set_lds(fwd_win_kernel<D, DV>, FwdTile<D, DV>::LDS_BYTES);
 }
 
 template <int D, int DV>

@@ -25,7 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # benchmarked workloads launch
 HOT = {
     "attn_fwd.hip": ["fwd_kernelILi128ELi128ELb1E", "fwd_kernelILi64ELi64ELb0E", "fwd_kernelILi64ELi64ELb1E",
-                     "fwd_kernelILi128ELi64ELb1E"],
+                     "fwd_kernelILi128ELi64ELb1E", "fwd_win_kernelILi128ELi128E"],
     "attn_bwd.hip": ["dq_kernelILi128ELi128ELb1E", "dq_kernelILi128ELi128ELb0E", "dkv_kernelILi128ELi128ELb1E",
                      "dkv_kernelILi128ELi128ELb0E", "dq_kernelILi64ELi64ELb0E", "dkv_kernelILi64ELi64ELb0E",
                      "dq_kernelILi128ELi64ELb1E", "dkv_kernelILi128ELi64ELb1E"],
