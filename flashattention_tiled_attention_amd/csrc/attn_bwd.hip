@@ -95,8 +95,11 @@ __device__ __forceinline__ void decode_q_item(int bid, int nQ, int qt_first, int
 
 // The PRECISE body runs the tiles whose rows need the exact path (below); the
 // plain body never touches its registers.
+// One workgroup's share: query rows q0 .. q_last of the kv head that hq reads;
+// this wave takes head hq, rows row0 .. row0+31.
 template <int D, int DV, bool CAUSAL, bool PRECISE>
-__device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, int hq, int qt) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, int hq, int q0, int q_last,
+                                        int row0) {
     using T = DqTile<D, DV>;
     using KC = typename T::KCopy;
     using VC = typename T::VCopy;
@@ -114,8 +117,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
     const size_t kvrows = ((size_t)b * a.Hkv + hkv) * (size_t)S;
     const uint16_t* Kp = a.k + kvrows * D;
     const uint16_t* Vp = a.v + kvrows * DV;
-    const int q0 = qt * kDqBQ;
-    const int qrow = q0 + 32 * wave + l32;
+    const int qrow = row0 + l32;
     const bool live = qrow < S;
     const float c = a.scale_log2;
     constexpr bool precise = PRECISE;
@@ -147,8 +149,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
     const float lse2 = live ? a.lse[rowbase + qrow] * kLog2e : INFINITY;
 
     const int nK = (S + kDqBK - 1) / kDqBK;
-    const int jend = CAUSAL ? min(nK, (q0 + kDqBQ - 1) / kDqBK + 1) : nK;
-    const int row0 = q0 + 32 * wave;
+    const int jend = CAUSAL ? min(nK, q_last / kDqBK + 1) : nK;
     int wjend = CAUSAL ? min(jend, (row0 + 31) / kDqBK + 1) : jend;
     if (row0 >= S) wjend = 0;
     const int W = CAUSAL ? a.window : 0;
@@ -299,10 +300,48 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
     const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
     int b, hq, qt;
     decode_q_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q0 = qt * kDqBQ;
     if (qt < a.precise_tiles)
-        dq_body<D, DV, CAUSAL, true>(a, smem, b, hq, qt);
+        dq_body<D, DV, CAUSAL, true>(a, smem, b, hq, q0, q0 + kDqBQ - 1, q0 + 32 * wave);
     else
-        dq_body<D, DV, CAUSAL, false>(a, smem, b, hq, qt);
+        dq_body<D, DV, CAUSAL, false>(a, smem, b, hq, q0, q0 + kDqBQ - 1, q0 + 32 * wave);
+}
+
+// Heads of one kv head that a sliding-window dQ workgroup takes together.
+__host__ __device__ inline int dq_win_heads(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+
+// Sliding window (as fwd_win_kernel does for the forward): the 4 waves take HW
+// query heads of one kv head and 4/HW blocks of 32 rows, so every wave uses nearly
+// all of the workgroup's key tiles. Workgroups with rows below 128 take the exact
+// path, as do all of them when the window is at most 128 keys (precise_all).
+template <int D, int DV>
+__global__ void __launch_bounds__(kDqThreads, 2) dq_win_kernel(BwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+    const int HW = dq_win_heads(a.G), BQ = 32 * (4 / HW);
+    const int nblk = a.G / HW;
+    const int groups = a.B * a.Hkv * nblk;   // (b, kv head, head block)
+    int qt, gid;
+    const int bid = blockIdx.x;
+    if ((groups & 7) == 0) {  // a head block stays on one XCD
+        const int x = bid & 7, st = bid >> 3, per = groups >> 3;
+        qt = st / per;
+        gid = (st - qt * per) * 8 + x;
+    } else {
+        qt = bid / groups;
+        gid = bid - qt * groups;
+    }
+    const int b = gid / (a.Hkv * nblk);
+    const int rem = gid - b * (a.Hkv * nblk);
+    const int hkv = rem / nblk, blk = rem - hkv * nblk;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hq = hkv * a.G + blk * HW + wave % HW;
+    const int q0 = qt * BQ;
+    const int row0 = q0 + 32 * (wave / HW);
+    if (a.precise_all || q0 < kPreciseRows)
+        dq_body<D, DV, true, true>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
+    else
+        dq_body<D, DV, true, false>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
 }
 
 // ---------------------------------------------------------------------------
@@ -663,9 +702,15 @@ hipError_t launch_bwd_t(const BwdArgs& args, int stages, hipStream_t stream) {
         // else tile 0 of a causal problem or the single tile of S <= 128.
         const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
         a.precise_tiles = a.precise_all ? nQ : (CAUSAL || a.S <= kPreciseRows) ? 1 : 0;
-        const long long blocks = (long long)a.B * a.Hq * nQ;
         constexpr int lds = DqTile<D, DV>::LDS_BYTES;
-        hipLaunchKernelGGL((dq_kernel<D, DV, CAUSAL>), dim3((unsigned)blocks), dim3(kDqThreads), lds, stream, a);
+        if (CAUSAL && a.window > 0) {
+            const int HW = dq_win_heads(a.G), BQ = 32 * (4 / HW);
+            const long long wblocks = (long long)((a.S + BQ - 1) / BQ) * a.B * a.Hkv * (a.G / HW);
+            hipLaunchKernelGGL((dq_win_kernel<D, DV>), dim3((unsigned)wblocks), dim3(kDqThreads), lds, stream, a);
+        } else {
+            const long long blocks = (long long)a.B * a.Hq * nQ;
+            hipLaunchKernelGGL((dq_kernel<D, DV, CAUSAL>), dim3((unsigned)blocks), dim3(kDqThreads), lds, stream, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -689,6 +734,7 @@ hipError_t setup_pair() {
     hipError_t e;
     if ((e = set_lds(dq_kernel<D, DV, false>, DqTile<D, DV>::LDS_BYTES))) return e;
     if ((e = set_lds(dq_kernel<D, DV, true>, DqTile<D, DV>::LDS_BYTES))) return e;
+    if ((e = set_lds(dq_win_kernel<D, DV>, DqTile<D, DV>::LDS_BYTES))) return e;
     if ((e = set_lds(dkv_kernel<D, DV, false>, KvTile<D, DV>::LDS_BYTES))) return e;
     return set_lds(dkv_kernel<D, DV, true>, KvTile<D, DV>::LDS_BYTES);
 }

@@ -28,7 +28,7 @@ HOT = {
                      "fwd_kernelILi128ELi64ELb1E", "fwd_win_kernelILi128ELi128E"],
     "attn_bwd.hip": ["dq_kernelILi128ELi128ELb1E", "dq_kernelILi128ELi128ELb0E", "dkv_kernelILi128ELi128ELb1E",
                      "dkv_kernelILi128ELi128ELb0E", "dq_kernelILi64ELi64ELb0E", "dkv_kernelILi64ELi64ELb0E",
-                     "dq_kernelILi128ELi64ELb1E", "dkv_kernelILi128ELi64ELb1E"],
+                     "dq_kernelILi128ELi64ELb1E", "dkv_kernelILi128ELi64ELb1E", "dq_win_kernelILi128ELi128E"],
     "attn_sparse.hip": ["sparse_fwd_kernelILi128E", "sparse_dq_kernelILi128E"],
 }
 
