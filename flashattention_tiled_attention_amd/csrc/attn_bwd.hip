@@ -14,7 +14,10 @@
 //   dq_kernel   one workgroup per (b, hq, 128-row query tile); K/V tiles stream
 //               from HBM straight into double-buffered, swizzled LDS tiles
 //               (global_load_lds). It also computes delta for its rows and stores
-//               it in the workspace.
+//               it in the workspace. With a sliding window, dq_win_kernel runs the
+//               same body with the query heads of one kv head side by side in a
+//               workgroup (fewer rows per head, so every wave uses nearly all of
+//               the workgroup's key tiles).
 //   dkv_kernel  one workgroup of 8 waves per (b, kv head, 64-key tile). K stays
 //               in registers and V in LDS; 32-row Q/dO tiles of every query head of
 //               the group stream from HBM into double-buffered LDS. Four wave pairs

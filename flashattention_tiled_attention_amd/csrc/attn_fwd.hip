@@ -9,7 +9,9 @@
 // never leaves the chip (the same result as the algorithm's printed order).
 //
 // One workgroup = 8 waves = one tile of 256 query rows of one (batch, head);
-// each wave owns 32 rows. Per 64-key tile j, a wave does
+// each wave owns 32 rows (with a sliding window, fwd_win_kernel gives the 8
+// waves several query heads of one kv head instead, see there). Per 64-key tile
+// j, a wave does
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in registers (B)
 //                      -> every lane holds one query column and 32 of its keys,
 //                         so the row max/sum are lane-local plus one permlane32 swap
