@@ -317,7 +317,7 @@ __host__ __device__ inline int dq_win_heads(int G) { return (G % 4 == 0) ? 4 : (
 // Sliding window (as fwd_win_kernel does for the forward): the 4 waves take HW
 // query heads of one kv head and 4/HW blocks of 32 rows, so every wave uses nearly
 // all of the workgroup's key tiles. Workgroups with rows below 128 take the exact
-// path, as do all of them when the window is at most 128 keys (precise_all).
+// path, as do all of them when the window is under 128 keys (precise_all).
 template <int D, int DV>
 __global__ void __launch_bounds__(kDqThreads, 2) dq_win_kernel(BwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];

@@ -35,8 +35,8 @@
 //
 // Rows that see few keys carry large probabilities, where rounding P to bf16 for
 // the P V product would cost up to about 2^-9 of |V| in O. For those rows (a
-// window of at most 128 keys, the first query tile of a causal problem, a
-// single tile of S <= 128) the workgroup takes a PRECISE body that splits P into
+// window of fewer than 128 keys, the first query tile of a causal or windowed
+// problem, a single tile of S <= 128) the workgroup takes a PRECISE body that splits P into
 // a bf16 high part and a bf16 remainder and runs the P V product on both. Both
 // bodies live in one launch, so the few exact-path workgroups run in the tail
 // of the longest-first schedule instead of in a launch of their own.
@@ -400,8 +400,8 @@ __host__ __device__ inline int win_heads(int G) {
 // tiles any one wave needs. Here the 8 waves take HW query heads of one kv head
 // (HW = 8, 4, 2 or 1, a divisor of G) and 8/HW blocks of 32 rows, so a workgroup
 // covers only 32*8/HW rows and every wave uses nearly all of its key tiles.
-// Workgroups whose rows see at most 128 keys (W <= 128, or the first 256 rows)
-// take the exact P V product.
+// Workgroups whose rows may see fewer than 128 keys (W < 128, or the first 256
+// rows) take the exact P V product.
 template <int D, int DV>
 __global__ void __launch_bounds__(kFwdThreads, 1) fwd_win_kernel(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
@@ -426,7 +426,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_win_kernel(FwdArgs a) {
     const int hq = hkv * a.G + blk * HW + wave % HW;
     const int q0 = qt * BQ;
     const int row0 = q0 + 32 * (wave / HW);
-    if (a.window <= 128 || q0 < 256)
+    if (a.window < 128 || q0 < 256)
         fwd_body<D, DV, true, true>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
     else
         fwd_body<D, DV, true, false>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
