@@ -109,38 +109,45 @@ struct SpTile {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a) {
+// Work item of a forward / dQ workgroup: (b, token i, kv head, block hb of 64
+// query heads).
+struct SpItem {
+    int b, i, hkv, hb;
+};
+__device__ __forceinline__ SpItem sp_item(const SparseArgs& a) {
+    const int nHB = (a.G + kSpRows - 1) / kSpRows;
+    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nHB);
+    SpItem it;
+    it.hb = w % nHB; w /= nHB;
+    it.hkv = w % a.Hkv; w /= a.Hkv;
+    it.i = w % a.S;
+    it.b = w / a.S;
+    return it;
+}
+
+// The body after the list is compacted into LDS (n entries). PRECISE is the exact
+// path, chosen once per workgroup, so the loop is straight-line code either way.
+template <int D, bool PRECISE>
+__device__ __forceinline__ void sparse_fwd_body(const SparseArgs& a, unsigned char* lds_raw, const SpItem& it,
+                                                const int* list, int n) {
     constexpr int BK = kSpFwdBK;   // list slots per tile
     constexpr int NB = BK / 32;    // 32-slot blocks per tile
     using T = SpTile<D, BK>;
     using C = typename T::Copy;
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     __bf16* const Kring = (__bf16*)lds_raw;
     __bf16* const Vring = Kring + 2 * T::TILE;
-    int* const list = (int*)(lds_raw + T::KV_BYTES);
-    int* const red = list + ((a.topk + 3) & ~3);
-
-    const int nHB = (a.G + kSpRows - 1) / kSpRows;
-    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nHB);
-    const int hb = w % nHB; w /= nHB;
-    const int hkv = w % a.Hkv; w /= a.Hkv;
-    const int i = w % a.S;
-    const int b = w / a.S;
+    const int b = it.b, i = it.i, hkv = it.hkv;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
-    const int head = hb * kSpRows + 32 * wave + l32;
+    const int head = it.hb * kSpRows + 32 * wave + l32;
     const bool live = head < a.G;
     const int hq = hkv * a.G + head;
     const size_t row = ((size_t)b * a.Hq + hq) * a.S + i;   // flat query row (when live)
     const float c = a.scale_log2;
-
-    const int n = compact_list(a.idx + ((size_t)b * a.S + i) * a.topk, a.topk, a.N, list, red);
-    const bool precise = a.precise_all || n <= kSpPreciseSlots;
 
     bf16x8 qf[DK];
     if (live) {
@@ -247,8 +254,9 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
                 rs += p[e];
             }
             pk[t2] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            pl[t2] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
-                           bf_lo(p[6]), bf_lo(p[7]));
+            if (PRECISE)
+                pl[t2] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
+                               bf_lo(p[6]), bf_lo(p[7]));
         }
         l += rs;
         // O^T += V^T P^T over 16-slot steps; V^T through transpose loads.
@@ -259,7 +267,7 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
                 const bf16x8 vt = concat(lds_read_tr(Vs + voff[0][db] + 16 * t2 * D),
                                          lds_read_tr(Vs + voff[1][db] + 16 * t2 * D));
                 oacc[db] = mfma32(vt, pk[t2], oacc[db]);
-                if (precise) oacc[db] = mfma32(vt, pl[t2], oacc[db]);
+                if (PRECISE) oacc[db] = mfma32(vt, pl[t2], oacc[db]);
             }
         wait_copies();
         __syncthreads();
@@ -281,39 +289,42 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
     }
 }
 
+template <int D>
+__global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a) {
+    using T = SpTile<D, kSpFwdBK>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    int* const list = (int*)(lds_raw + T::KV_BYTES);
+    int* const red = list + ((a.topk + 3) & ~3);
+    const SpItem it = sp_item(a);
+    const int n = compact_list(a.idx + ((size_t)it.b * a.S + it.i) * a.topk, a.topk, a.N, list, red);
+    if (a.precise_all || n <= kSpPreciseSlots)
+        sparse_fwd_body<D, true>(a, lds_raw, it, list, n);
+    else
+        sparse_fwd_body<D, false>(a, lds_raw, it, list, n);
+}
+
 // ---------------------------------------------------------------------------
 // dQ (+ delta)
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) {
+template <int D, bool PRECISE>
+__device__ __forceinline__ void sparse_dq_body(const SparseArgs& a, unsigned char* lds_raw, const SpItem& it,
+                                               const int* list, int n) {
     using T = SpTile<D>;
     using C = typename T::Copy;
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     __bf16* const Kring = (__bf16*)lds_raw;
     __bf16* const Vring = Kring + 2 * T::TILE;
-    int* const list = (int*)(lds_raw + T::KV_BYTES);
-    int* const red = list + ((a.topk + 3) & ~3);
-
-    const int nHB = (a.G + kSpRows - 1) / kSpRows;
-    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nHB);
-    const int hb = w % nHB; w /= nHB;
-    const int hkv = w % a.Hkv; w /= a.Hkv;
-    const int i = w % a.S;
-    const int b = w / a.S;
+    const int b = it.b, i = it.i, hkv = it.hkv;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
-    const int head = hb * kSpRows + 32 * wave + l32;
+    const int head = it.hb * kSpRows + 32 * wave + l32;
     const bool live = head < a.G;
     const int hq = hkv * a.G + head;
     const size_t row = ((size_t)b * a.Hq + hq) * a.S + i;
     const float c = a.scale_log2;  // signed
-
-    const int n = compact_list(a.idx + ((size_t)b * a.S + i) * a.topk, a.topk, a.N, list, red);
-    const bool precise = a.precise_all || n <= kSpPreciseSlots;
 
     // Q and dO rows as B operands; delta = rowsum(dO * O) from the stored O.
     bf16x8 qf[DK], df[DK];
@@ -375,7 +386,7 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
     // Pass 0 (exact path only) accumulates delta = sum_s P dP; the last pass forms
     // dS and accumulates dQ^T += K^T dS^T.
     const int nT = (n + kSpBK - 1) / kSpBK;
-    for (int pass = precise ? 0 : 1; pass < 2; ++pass) {
+    for (int pass = PRECISE ? 0 : 1; pass < 2; ++pass) {
         float dacc = 0.0f;
         if (nT > 0) {
             copy_tile(0, 0);
@@ -401,7 +412,7 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                if (precise) dacc += s[r] * dp[r];  // used by pass 0 only
+                if (PRECISE) dacc += s[r] * dp[r];  // used by pass 0 only
                 s[r] = s[r] * (dp[r] - delta);
             }
             if (pass == 1) {
@@ -410,15 +421,16 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
                     const int r0 = 8 * t2;
                     const bf16x8 hi = pack8(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5],
                                             s[r0 + 6], s[r0 + 7]);
-                    const bf16x8 lo = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
-                                            bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]),
-                                            bf_lo(s[r0 + 7]));
+                    bf16x8 lo;
+                    if (PRECISE)
+                        lo = pack8(bf_lo(s[r0]), bf_lo(s[r0 + 1]), bf_lo(s[r0 + 2]), bf_lo(s[r0 + 3]),
+                                   bf_lo(s[r0 + 4]), bf_lo(s[r0 + 5]), bf_lo(s[r0 + 6]), bf_lo(s[r0 + 7]));
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const bf16x8 kt = concat(lds_read_tr(Ks + toff[0][db] + 16 * t2 * D),
                                                  lds_read_tr(Ks + toff[1][db] + 16 * t2 * D));
                         dq[db] = mfma32(kt, hi, dq[db]);
-                        if (precise) dq[db] = mfma32(kt, lo, dq[db]);
+                        if (PRECISE) dq[db] = mfma32(kt, lo, dq[db]);
                     }
                 }
             }
@@ -441,6 +453,20 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
                 *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * h) = v;
             }
     }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) {
+    using T = SpTile<D>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    int* const list = (int*)(lds_raw + T::KV_BYTES);
+    int* const red = list + ((a.topk + 3) & ~3);
+    const SpItem it = sp_item(a);
+    const int n = compact_list(a.idx + ((size_t)it.b * a.S + it.i) * a.topk, a.topk, a.N, list, red);
+    if (a.precise_all || n <= kSpPreciseSlots)
+        sparse_dq_body<D, true>(a, lds_raw, it, list, n);
+    else
+        sparse_dq_body<D, false>(a, lds_raw, it, list, n);
 }
 
 // ---------------------------------------------------------------------------
