@@ -54,14 +54,26 @@ constexpr int kSpSlotsPerWG = 128;   // partial kernel: list slots per workgroup
 constexpr int kSpPartThreads = 256;
 constexpr int kSpMaxG = 128;         // query heads per kv head
 constexpr int kSpChunk = 16;         // tokens per inverse-map chunk
+constexpr int kSpXcdTokens = 64;     // tokens per XCD chunk (forward, dQ, partial)
 
 __device__ __forceinline__ bool slot_valid(int j, int N) { return j >= 0 && j < N; }
 
 // Work item of workgroup `bid` among `total` items ordered (b, token, kv head,
-// block): when total divides by 8, each XCD takes a contiguous range of items,
-// so neighbouring tokens (whose windows overlap) share one L2.
-__device__ __forceinline__ int xcd_item(int bid, int total) {
-    if ((total & 7) == 0) return (bid & 7) * (total >> 3) + (bid >> 3);
+// block), `per` items per token. Workgroup bid runs on XCD bid % 8. Tokens go to
+// the XCDs in chunks of kSpXcdTokens, so neighbouring tokens (whose windows
+// overlap) share one L2, dealt round robin from the last chunk down: every XCD
+// gets the same mix of short and long lists (later tokens list more pool rows),
+// and the longest start first. When the items do not split into whole rounds of
+// chunks, each XCD takes a contiguous range (total divisible by 8), else launch
+// order.
+__device__ __forceinline__ int xcd_item(int bid, int total, int per) {
+    const int chunk = kSpXcdTokens * per;
+    const int x = bid & 7, r = bid >> 3;
+    if (total % (8 * chunk) == 0) {
+        const int rounds = total / (8 * chunk);
+        return ((rounds - 1 - r / chunk) * 8 + x) * chunk + r % chunk;
+    }
+    if ((total & 7) == 0) return x * (total >> 3) + r;
     return bid;
 }
 
@@ -116,7 +128,7 @@ struct SpItem {
 };
 __device__ __forceinline__ SpItem sp_item(const SparseArgs& a) {
     const int nHB = (a.G + kSpRows - 1) / kSpRows;
-    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nHB);
+    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nHB, a.Hkv * nHB);
     SpItem it;
     it.hb = w % nHB; w /= nHB;
     it.hkv = w % a.Hkv; w /= a.Hkv;
@@ -594,7 +606,7 @@ __global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(Sp
     float* const Dl = Ls + Gp;
 
     const int nSB = (a.topk + kSpSlotsPerWG - 1) / kSpSlotsPerWG;
-    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nSB);
+    int w = xcd_item(blockIdx.x, a.B * a.S * a.Hkv * nSB, a.Hkv * nSB);
     const int sb = w % nSB; w /= nSB;
     const int hkv = w % a.Hkv; w /= a.Hkv;
     const int i = w % a.S;
