@@ -564,6 +564,8 @@ __device__ __forceinline__ void part_product(const __bf16* Qt, const __bf16* Dt,
 
 // Store a [slot][d] accumulator (lane = column) times `mul` into rows
 // dst[slot][0..D) for slots < nslots: each store writes two 128-byte row pieces.
+// The contributions are read once, by the reduction, long after: the stores are
+// non-temporal, so they stream to memory instead of filling the L2.
 template <int D>
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mul, float* dst, int nslots,
                                            int lane) {
@@ -573,7 +575,8 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mu
         const int slot = 8 * (r >> 2) + 4 * h + (r & 3);
         if (slot < nslots) {
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) dst[(size_t)slot * D + db * 32 + l32] = acc[db][r] * mul;
+            for (int db = 0; db < D / 32; ++db)
+                __builtin_nontemporal_store(acc[db][r] * mul, dst + (size_t)slot * D + db * 32 + l32);
         }
     }
 }
@@ -754,8 +757,8 @@ __global__ void __launch_bounds__(256) sp_scatter(SparseArgs a) {
 // The row's entries are split into four contiguous quarters, one per wave; a wave
 // reads 64 entry numbers at once (one per lane) and then walks them eight at a
 // time, the entry number broadcast from a scalar register, so sixteen row loads
-// are in flight. The four partial sums are added in wave order. Lane l holds
-// columns 2l, 2l+1.
+// are in flight; each contribution is read once, so the loads are non-temporal.
+// The four partial sums are added in wave order. Lane l holds columns 2l, 2l+1.
 template <int D>
 __global__ void __launch_bounds__(256) sp_reduce(SparseArgs a) {
     typedef float fv __attribute__((ext_vector_type(2)));
@@ -784,8 +787,8 @@ __global__ void __launch_bounds__(256) sp_reduce(SparseArgs a) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const size_t x = (size_t)__builtin_amdgcn_readlane(mine, u + t) * D;
-                k8[t] = *(const fv*)(ik + x);
-                v8[t] = *(const fv*)(iv + x);
+                k8[t] = __builtin_nontemporal_load((const fv*)(ik + x));
+                v8[t] = __builtin_nontemporal_load((const fv*)(iv + x));
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -795,8 +798,8 @@ __global__ void __launch_bounds__(256) sp_reduce(SparseArgs a) {
         }
         for (; u < cntb; ++u) {
             const size_t x = (size_t)__builtin_amdgcn_readlane(mine, u) * D;
-            sk += *(const fv*)(ik + x);
-            sv += *(const fv*)(iv + x);
+            sk += __builtin_nontemporal_load((const fv*)(ik + x));
+            sv += __builtin_nontemporal_load((const fv*)(iv + x));
         }
     }
     part[0][wave][lane] = sk;

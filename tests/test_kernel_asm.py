@@ -58,19 +58,55 @@ def functions(lines):
 
 
 def loops_of(body):
-    """Line ranges of every loop (a backward branch to a label above it)."""
+    """Line ranges of every loop: a backward branch to a label above it whose
+    target block reaches the branch again. (The compiler also places one-way
+    blocks below the code they jump back into; those close no cycle.)"""
     labels = {}
+    starts = [0]
     for k, l in enumerate(body):
         m = re.match(r"^(\.LBB\d+_\d+):", l)
         if m:
             labels[m.group(1)] = k
+        if m or re.match(r"^; %bb\.\d+:", l):
+            starts.append(k)
+    starts = sorted(set(starts))
+    block_of = {}
+    for n, s in enumerate(starts):
+        end = starts[n + 1] if n + 1 < len(starts) else len(body)
+        for k in range(s, end):
+            block_of[k] = n
+    succ = {n: set() for n in range(len(starts))}
+    branches = []
+    for n, s in enumerate(starts):
+        end = starts[n + 1] if n + 1 < len(starts) else len(body)
+        falls = True
+        for k in range(s, end):
+            m = re.search(r"(s_cbranch_\w+|s_branch)\s+(\.LBB\d+_\d+)", body[k])
+            if m and m.group(2) in labels:
+                succ[n].add(block_of[labels[m.group(2)]])
+                branches.append((k, m.group(2)))
+                if m.group(1) == "s_branch":
+                    falls = False
+            if re.search(r"\bs_endpgm\b|\bs_setpc_b64\b", body[k]):
+                falls = False
+        if falls and n + 1 < len(starts):
+            succ[n].add(n + 1)
+
+    def reaches(a, b):
+        seen, todo = set(), [a]
+        while todo:
+            x = todo.pop()
+            if x == b:
+                return True
+            if x not in seen:
+                seen.add(x)
+                todo.extend(succ[x])
+        return False
+
     loops = set()
-    for k, l in enumerate(body):
-        m = re.search(r"s_cbranch_\w+\s+(\.LBB\d+_\d+)|s_branch\s+(\.LBB\d+_\d+)", l)
-        if m:
-            t = m.group(1) or m.group(2)
-            if t in labels and labels[t] < k:
-                loops.add((labels[t], k))
+    for k, t in branches:
+        if labels[t] < k and reaches(block_of[labels[t]], block_of[k]):
+            loops.add((labels[t], k))
     return sorted(loops)
 
 
