@@ -24,7 +24,7 @@
 //                         the token's query heads are the rows of one Q and one
 //                         dO tile in LDS, each lane owns one slot; it writes
 //                         scale dS^T Q and P^T dO for every non-empty slot.
-//   sp_count, sp_scan_chunks, sp_scan_rows, sp_scatter
+//   sp_count, sp_scan_chunks, sp_scan_rows, sp_offset_chunks, sp_scatter
 //                         the inverse of the index map: for every key/value row,
 //                         the (token, slot) entries that name it, in token order
 //                         (deterministic: counts are order-free, and positions
@@ -55,6 +55,7 @@ constexpr int kSpPartThreads = 256;
 constexpr int kSpMaxG = 128;         // query heads per kv head
 constexpr int kSpChunk = 16;         // tokens per inverse-map chunk
 constexpr int kSpXcdTokens = 64;     // tokens per XCD chunk (forward, dQ, partial)
+constexpr int kSpLdsRows = 16384;    // inverse map: per-chunk row counters in LDS up to this N
 
 __device__ __forceinline__ bool slot_valid(int j, int N) { return j >= 0 && j < N; }
 
@@ -67,11 +68,11 @@ __device__ __forceinline__ bool slot_valid(int j, int N) { return j >= 0 && j < 
 // chunks, each XCD takes a contiguous range (total divisible by 8), else launch
 // order.
 __device__ __forceinline__ int xcd_item(int bid, int total, int per) {
-    const int chunk = kSpXcdTokens * per;
+    const long long chunk = (long long)kSpXcdTokens * per;  // 64-bit: per can be large
     const int x = bid & 7, r = bid >> 3;
-    if (total % (8 * chunk) == 0) {
-        const int rounds = total / (8 * chunk);
-        return ((rounds - 1 - r / chunk) * 8 + x) * chunk + r % chunk;
+    if (total % (8 * chunk) == 0) {  // then 8 * chunk <= total < 2^31
+        const long long rounds = total / (8 * chunk);
+        return (int)(((rounds - 1 - r / chunk) * 8 + x) * chunk + r % chunk);
     }
     if ((total & 7) == 0) return x * (total >> 3) + r;
     return bid;
@@ -672,16 +673,40 @@ __global__ void __launch_bounds__(256) sp_fill_zero(int* p, size_t n) {
 }
 
 // cnt[b][c][j] = number of entries of chunk c (tokens 16c .. 16c+15) naming row j.
+// Counts do not depend on order, so the workgroup walks the chunk's lists as one
+// contiguous range, eight loads in flight per thread. With LDS_ROWS the chunk's N
+// counters live in LDS (N <= kSpLdsRows): a window row is named by up to 16 tokens
+// of a chunk, and LDS atomics take that contention far faster than the L2's; the
+// counters, zeros included, then go out in one coalesced pass. Otherwise the
+// atomics go to the zero-filled global counters.
+template <bool LDS_ROWS>
 __global__ void __launch_bounds__(256) sp_count(SparseArgs a) {
+    constexpr int U = 8;
+    extern __shared__ int lds_cnt[];
     const int b = blockIdx.x / a.nchunks, ch = blockIdx.x % a.nchunks;
     int* cnt = a.cnt + ((size_t)b * a.nchunks + ch) * a.N;
-    const int i1 = min(a.S, (ch + 1) * kSpChunk);
-    for (int i = ch * kSpChunk; i < i1; ++i) {
-        const int32_t* lst = a.idx + ((size_t)b * a.S + i) * a.topk;
-        for (int s = threadIdx.x; s < a.topk; s += 256) {
-            const int j = lst[s];
-            if (slot_valid(j, a.N)) atomicAdd(cnt + j, 1);
+    int* ctr = LDS_ROWS ? lds_cnt : cnt;
+    if (LDS_ROWS) {
+        for (int j = threadIdx.x; j < a.N; j += 256) lds_cnt[j] = 0;
+        __syncthreads();
+    }
+    const int i0 = ch * kSpChunk, i1 = min(a.S, i0 + kSpChunk);
+    const int32_t* lst = a.idx + ((size_t)b * a.S + i0) * a.topk;
+    const int n = (i1 - i0) * a.topk;
+    for (int base = 0; base < n; base += 256 * U) {
+        int j[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + u * 256 + (int)threadIdx.x;
+            j[u] = e < n ? lst[e] : -1;
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (slot_valid(j[u], a.N)) atomicAdd(ctr + j[u], 1);
+    }
+    if (LDS_ROWS) {
+        __syncthreads();
+        for (int j = threadIdx.x; j < a.N; j += 256) cnt[j] = lds_cnt[j];
     }
 }
 
@@ -734,22 +759,52 @@ __global__ void __launch_bounds__(1024) sp_scan_rows(SparseArgs a) {
     if (threadIdx.x == 0) rs[a.N] = base;
 }
 
+// cnt[b][c][j] += rowstart[b][j]: each chunk's base for row j becomes the place,
+// in the entry list, of that chunk's first entry naming j.
+__global__ void __launch_bounds__(256) sp_offset_chunks(SparseArgs a) {
+    const size_t per_b = (size_t)a.nchunks * a.N, n = (size_t)a.B * per_b;
+    for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
+        const int b = (int)(x / per_b), j = (int)(x % a.N);
+        a.cnt[x] += a.rowstart[(size_t)b * (a.N + 1) + j];
+    }
+}
+
 // list[b][rowstart[j] + k] = the k-th entry (i*topk + s, in token order) naming
 // row j. A workgroup walks its chunk's tokens in order; a returning atomic on the
-// chunk base of row j gives each entry its place.
+// chunk's place for row j gives each entry its place (in LDS with LDS_ROWS, as in
+// sp_count). Slot s of a token is thread s % 256's entry s / 256 (PER = entries
+// per thread, a power of two covering topk); the next token's entries load while
+// this token's atomics run.
+template <int PER, bool LDS_ROWS>
 __global__ void __launch_bounds__(256) sp_scatter(SparseArgs a) {
+    extern __shared__ int lds_cur[];
     const int b = blockIdx.x / a.nchunks, ch = blockIdx.x % a.nchunks;
     int* cur = a.cnt + ((size_t)b * a.nchunks + ch) * a.N;
-    const int* rs = a.rowstart + (size_t)b * (a.N + 1);
+    if (LDS_ROWS) {
+        for (int j = threadIdx.x; j < a.N; j += 256) lds_cur[j] = cur[j];
+        __syncthreads();
+        cur = lds_cur;
+    }
     int* out = a.list + (size_t)b * a.S * a.topk;
-    const int i1 = min(a.S, (ch + 1) * kSpChunk);
-    for (int i = ch * kSpChunk; i < i1; ++i) {
+    const int i0 = ch * kSpChunk, i1 = min(a.S, i0 + kSpChunk);
+    auto load = [&](int i, int (&j)[PER]) {
         const int32_t* lst = a.idx + ((size_t)b * a.S + i) * a.topk;
-        for (int s = threadIdx.x; s < a.topk; s += 256) {
-            const int j = lst[s];
-            if (slot_valid(j, a.N)) out[rs[j] + atomicAdd(cur + j, 1)] = i * a.topk + s;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int s = u * 256 + (int)threadIdx.x;
+            j[u] = s < a.topk ? lst[s] : -1;
         }
+    };
+    int jc[PER], jn[PER];
+    load(i0, jc);
+    for (int i = i0; i < i1; ++i) {
+        if (i + 1 < i1) load(i + 1, jn);
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            if (slot_valid(jc[u], a.N)) out[atomicAdd(cur + jc[u], 1)] = i * a.topk + u * 256 + (int)threadIdx.x;
         __syncthreads();  // token i's places are taken before token i+1's
+#pragma unroll
+        for (int u = 0; u < PER; ++u) jc[u] = jn[u];
     }
 }
 
@@ -829,12 +884,28 @@ hipError_t launch_fwd_t(const SparseArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <bool LDS_ROWS>
+void launch_scatter(const SparseArgs& a, dim3 grid, int lds, hipStream_t stream) {
+    if (a.topk <= 256)
+        hipLaunchKernelGGL((sp_scatter<1, LDS_ROWS>), grid, dim3(256), lds, stream, a);
+    else if (a.topk <= 512)
+        hipLaunchKernelGGL((sp_scatter<2, LDS_ROWS>), grid, dim3(256), lds, stream, a);
+    else if (a.topk <= 1024)
+        hipLaunchKernelGGL((sp_scatter<4, LDS_ROWS>), grid, dim3(256), lds, stream, a);
+    else if (a.topk <= 2048)
+        hipLaunchKernelGGL((sp_scatter<8, LDS_ROWS>), grid, dim3(256), lds, stream, a);
+    else
+        hipLaunchKernelGGL((sp_scatter<16, LDS_ROWS>), grid, dim3(256), lds, stream, a);
+}
+
 template <int D>
 hipError_t launch_bwd_t(const SparseArgs& a, hipStream_t stream) {
     hipError_t e;
     const size_t ncnt = (size_t)a.B * a.nchunks * a.N;
-    hipLaunchKernelGGL(sp_fill_zero, dim3((unsigned)min((size_t)4096, (ncnt + 255) / 256)), dim3(256), 0, stream,
-                       a.cnt, ncnt);
+    const bool lds_rows = a.N <= kSpLdsRows;
+    if (!lds_rows)
+        hipLaunchKernelGGL(sp_fill_zero, dim3((unsigned)min((size_t)4096, (ncnt + 255) / 256)), dim3(256), 0, stream,
+                           a.cnt, ncnt);
     const int nHB = (a.G + kSpRows - 1) / kSpRows;
     const long long qblocks = (long long)a.B * a.S * a.Hkv * nHB;
     const int qlds = SpTile<D>::lds_bytes(a.topk);
@@ -844,10 +915,20 @@ hipError_t launch_bwd_t(const SparseArgs& a, hipStream_t stream) {
     const int plds = PartTile<D>::lds_bytes((a.G + 31) & ~31);
     hipLaunchKernelGGL((sparse_kv_partial_kernel<D>), dim3((unsigned)pblocks), dim3(kSpPartThreads), plds, stream,
                        a);
-    hipLaunchKernelGGL(sp_count, dim3((unsigned)(a.B * a.nchunks)), dim3(256), 0, stream, a);
+    const dim3 cgrid((unsigned)(a.B * a.nchunks));
+    const int rows_lds = lds_rows ? a.N * 4 : 0;
+    if (lds_rows)
+        hipLaunchKernelGGL(sp_count<true>, cgrid, dim3(256), rows_lds, stream, a);
+    else
+        hipLaunchKernelGGL(sp_count<false>, cgrid, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(sp_scan_chunks, dim3((unsigned)(((size_t)a.B * a.N + 255) / 256)), dim3(256), 0, stream, a);
     hipLaunchKernelGGL(sp_scan_rows, dim3((unsigned)a.B), dim3(1024), 0, stream, a);
-    hipLaunchKernelGGL(sp_scatter, dim3((unsigned)(a.B * a.nchunks)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sp_offset_chunks, dim3((unsigned)min((size_t)65536, (ncnt + 255) / 256)), dim3(256), 0,
+                       stream, a);
+    if (lds_rows)
+        launch_scatter<true>(a, cgrid, rows_lds, stream);
+    else
+        launch_scatter<false>(a, cgrid, 0, stream);
     hipLaunchKernelGGL((sp_reduce<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.N)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return hipSuccess;

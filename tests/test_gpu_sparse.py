@@ -71,12 +71,25 @@ def test_random_lists(D, Hq, Hkv):
     check(q, k, v, idx, do, 1.0 / math.sqrt(D), "random G=%d D=%d" % (Hq // Hkv, D))
 
 
-@pytest.mark.parametrize("topk", [1, 2, 31, 32, 33, 64, 129, 300])
+# 1..300, then one length in each range of the inverse map's per-thread entry counts
+# (up to 512, 1024, 2048 and the 4096 maximum; rows repeat within a list once topk > N)
+@pytest.mark.parametrize("topk", [1, 2, 31, 32, 33, 64, 129, 300, 600, 1100, 2100, 4096])
 def test_list_lengths(topk):
     B, Hq, Hkv, S, N, D = 1, 8, 2, 30, 400, 128
     q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, seed=topk, with_dout=True)
     idx = random_lists(B, S, N, topk, seed=topk + 1, empty_frac=0.1, empty_tokens=(3,))
     check(q, k, v, idx, do, 1.0 / math.sqrt(D), "topk=%d" % topk)
+
+
+# The inverse map keeps a chunk's per-row counters in LDS up to N = 16384 rows and
+# in global memory beyond: both sides of that boundary.
+@pytest.mark.parametrize("N", [16384, 16385, 20000])
+def test_many_rows(N):
+    B, Hq, Hkv, S, D, topk = 1, 4, 1, 40, 128, 200
+    q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, seed=N % 1000, with_dout=True)
+    idx = random_lists(B, S, N, topk, seed=N % 997, empty_frac=0.1)
+    idx[0, :8, :64] = np.arange(64, dtype=np.int32)  # shared rows: several tokens per row
+    check(q, k, v, idx, do, 1.0 / math.sqrt(D), "N=%d" % N)
 
 
 def test_all_empty_and_single_slot():
