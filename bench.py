@@ -325,9 +325,11 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # Per-entry-point durations with HIP events recorded on the stream the kernels run
-    # on: attn_fwd (its main launch plus the small exact-path launch of the first
-    # causal query tile), attn_bwd_dq (likewise two launches) and attn_bwd_dkdv (one
-    # launch); a windowed workload times attn_fwd_window and attn_bwd_window.
+    # on: attn_fwd, attn_bwd_dq and attn_bwd_dkdv are one launch each (the exact-path
+    # tiles run inside the same launch); a windowed, d_v or sparse workload times its
+    # forward and its whole backward entry point. The mean is over n back-to-back
+    # calls; then an event between consecutive calls gives each call's own duration,
+    # for the median and the minimum.
     def time_calls(fn, n):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -336,10 +338,19 @@ def main():
             fn()
         e1.record(stream)
         e1.synchronize()
-        return e0.elapsed_time(e1) / n
+        mean = e0.elapsed_time(e1) / n
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record(stream)
+        for i in range(n):
+            fn()
+            evs[i + 1].record(stream)
+        evs[-1].synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+        return mean, per[n // 2], per[0]
 
     n_rep = max(args.steps, 10)
-    kernel_ms = {name: time_calls(fn, n_rep) for name, fn in calls.items()}
+    kernel_stats = {name: time_calls(fn, n_rep) for name, fn in calls.items()}
+    kernel_ms = {name: st[0] for name, st in kernel_stats.items()}
 
     # FLOP convention (pair_flops): each launch's products over the visible pairs; the
     # step's algorithmic work is the forward plus the backward's five products.
@@ -362,7 +373,8 @@ def main():
         fl = pf[kname] * pairs
         kernels[kname] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                          "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "hbm_bytes": hbm_traffic(kname) if headline else None}
+                         "ms_median": round(kernel_stats[kname][1], 4), "ms_min": round(kernel_stats[kname][2], 4),
+                         "calls": n_rep, "hbm_bytes": hbm_traffic(kname) if headline else None}
 
     result = {
         "metric": "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak on 1 MI355X",

@@ -92,6 +92,16 @@ def test_many_rows(N):
     check(q, k, v, idx, do, 1.0 / math.sqrt(D), "N=%d" % N)
 
 
+def test_chunked_work_order_batches_and_kv_heads():
+    """2 batches x 2 kv heads x 512 tokens: the item count divides into whole rounds of
+    64-token chunks over the 8 XCDs, so the forward, dQ and partial kernels take the
+    chunked order with more than one item per token."""
+    B, Hq, Hkv, S, N, D, topk = 2, 8, 2, 512, 640, 128, 96
+    q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, seed=21, with_dout=True)
+    idx = random_lists(B, S, N, topk, seed=22, empty_frac=0.15, empty_tokens=(5, 300))
+    check(q, k, v, idx, do, 1.0 / math.sqrt(D), "chunked order B=2 Hkv=2 S=512")
+
+
 def test_all_empty_and_single_slot():
     B, Hq, Hkv, S, N, D = 1, 64, 1, 12, 50, 128
     q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, seed=7, with_dout=True)
