@@ -33,8 +33,8 @@
 // part plus a bf16 remainder (two MFMAs each). When |scale| * sqrt(D) > 2 the
 // scores of unit-variance inputs spread wide enough for any row to concentrate
 // on a few keys, and the host asks for this treatment on every tile; so it does
-// for a sliding window of at most 128 keys, where no row sees more keys than the
-// first causal rows do.
+// for a sliding window of fewer than 128 keys, where every row sees fewer keys
+// than the first causal rows do.
 //
 // Queries and keys have D columns and values DV (the d and d_v of Eq. (1)); each
 // is 64 or 128, in any combination: Q, K, dQ and dK are D wide, V, O, dO and dV

@@ -436,8 +436,8 @@ template <int D, int DV, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
     // Rows that see at most 128 keys take the exact P V product: tile 0 of a
     // causal problem (rows 0..255 see at most 256 keys; the first 128 of them, the
-    // ones that need it, are there) or the single tile of S <= 128 (windowed
-    // problems: fwd_win_kernel).
+    // ones that need it, are there) or the single tile of S <= 128. Windowed
+    // problems go to fwd_win_kernel, which makes that choice per workgroup.
     const int nQ = (args.S + kFwdBQ - 1) / kFwdBQ;
     FwdArgs a = args;
     constexpr int lds = FwdTile<D, DV>::LDS_BYTES;
