@@ -374,8 +374,29 @@ struct KvTile {
     using VCopy = CopyPlan<DV, kKvBK, 2 * kKvSplits>;                // per wave
 };
 
-template <int D, int DV, bool CAUSAL>
-__global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
+// Work item of a dK/dV workgroup: (b, hkv, key tile); causal tiles issued longest
+// (lowest) first, groups dealt to XCDs as in the forward.
+__device__ __forceinline__ void dkv_item(const BwdArgs& a, int& b, int& hkv, int& kt) {
+    const int C = a.B * a.Hkv, bid = blockIdx.x;
+    int rank, cgrp;
+    if ((C & 7) == 0) {
+        const int x = bid & 7, st = bid >> 3, per = C >> 3;
+        rank = st / per;
+        cgrp = (st - rank * per) * 8 + x;
+    } else {
+        rank = bid / C;
+        cgrp = bid - rank * C;
+    }
+    kt = rank;  // ascending key tile = most query tiles first when causal
+    b = cgrp / a.Hkv;
+    hkv = cgrp % a.Hkv;
+}
+
+// MAYBE_PRECISE: whether any iteration of this workgroup can take the exact path.
+// Without it the per-iteration test is compiled out and the dV/dK product loop is
+// straight-line code.
+template <int D, int DV, bool CAUSAL, bool MAYBE_PRECISE>
+__device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_raw, int b, int hkv, int kt) {
     using T = KvTile<D, DV>;
     using QC = typename T::QCopy;
     using DC = typename T::DCopy;
@@ -386,7 +407,6 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     constexpr int DBK = D / 32;    // 32-row blocks of dK^T
     constexpr int DBV = DV / 32;   // 32-row blocks of dV^T
     constexpr int DBM = DBK > DBV ? DBK : DBV;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -395,24 +415,6 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     const int S = a.S, G = a.G;
     const int nQB = (S + kKvBQ - 1) / kKvBQ;
 
-    // work item: (b, hkv, key tile); causal tiles issued longest (lowest) first,
-    // groups dealt to XCDs as in the forward.
-    int b, hkv, kt;
-    {
-        const int C = a.B * a.Hkv, bid = blockIdx.x;
-        int rank, cgrp;
-        if ((C & 7) == 0) {
-            const int x = bid & 7, st = bid >> 3, per = C >> 3;
-            rank = st / per;
-            cgrp = (st - rank * per) * 8 + x;
-        } else {
-            rank = bid / C;
-            cgrp = bid - rank * C;
-        }
-        kt = rank;  // ascending key tile = most query tiles first when causal
-        b = cgrp / a.Hkv;
-        hkv = cgrp % a.Hkv;
-    }
     const int kv0 = kt * kKvBK;
     const int kw0 = kv0 + 32 * w2;  // this wave's first key
     const int key = kw0 + l32;      // this lane's key (column of S, dP)
@@ -558,7 +560,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
             const float* Ls = stage_lse(st);
             const float* Dl = stage_dl(st);
             const int qs0 = (qi_first + it % per_g) * kKvBQ;
-            const bool precise = a.precise_all || (precise_problem && qs0 < kPreciseRows);
+            const bool precise = MAYBE_PRECISE && (a.precise_all || (precise_problem && qs0 < kPreciseRows));
             // skip when every query precedes every key of the wave, or (window)
             // every query lies past the band of the wave's last key
             const bool skip = (CAUSAL && qs0 + 31 < kw0) || qs0 >= S || (W > 0 && qs0 > kw0 + 31 + W - 1);
@@ -695,6 +697,20 @@ __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
                 *(f32x4*)(out + db * 32 + 8 * g4 + 4 * h) = v;
             }
     }
+}
+
+template <int D, int DV, bool CAUSAL>
+__global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    int b, hkv, kt;
+    dkv_item(a, b, hkv, kt);
+    // Exact-path iterations have query rows below kPreciseRows; a causal (or
+    // windowed) key tile only sees queries at or past its first key.
+    const bool precise_problem = CAUSAL || a.S <= kPreciseRows;
+    if (a.precise_all || (precise_problem && kt * kKvBK < kPreciseRows))
+        dkv_body<D, DV, CAUSAL, true>(a, lds_raw, b, hkv, kt);
+    else
+        dkv_body<D, DV, CAUSAL, false>(a, lds_raw, b, hkv, kt);
 }
 
 template <int D, int DV, bool CAUSAL>
