@@ -211,8 +211,8 @@ def main():
                     help="run only the LDS-to-register transpose microbenchmark (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path; use --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
