@@ -625,6 +625,9 @@ __global__ void __launch_bounds__(kSpPartThreads, 2) sparse_kv_partial_kernel(Sp
     const int jraw = slot < a.topk ? lst[slot] : -1;
     const bool valid = slot_valid(jraw, a.N);
     const int j = valid ? jraw : 0;
+    // A block of empty slots (the unused tail of a short list) has nothing to write:
+    // the whole workgroup leaves before loading anything.
+    if (!__syncthreads_or(valid)) return;
 
     // Q / dO rows of the token's heads (rows past G repeat head G-1; their lse is
     // +inf, so they add exactly 0), and the V rows of this workgroup's slots.
