@@ -62,6 +62,8 @@ int check_sizes(int B, int Hq, int Hkv, int S, int D, int Dv) {
     if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || Dv < 1) return ATTN_ERR_SHAPE;
     const double elems = (double)B * Hq * S * (D > Dv ? D : Dv);
     if (elems >= 1099511627776.0) return ATTN_ERR_SHAPE;  // 2^40
+    // row offsets within one head are 32-bit in the kernels' tile copies
+    if ((double)S * (D > Dv ? D : Dv) >= 2147483648.0) return ATTN_ERR_SHAPE;  // 2^31
     // grid size: B * Hq * ceil(S / 128) work groups must fit a 32-bit grid
     if ((double)B * Hq * ((S + 127) / 128) >= 2147483647.0) return ATTN_ERR_SHAPE;
     if (Hq % Hkv != 0) return ATTN_ERR_GQA;

@@ -20,7 +20,8 @@
  *  - causal != 0: query row i sees key rows j <= i (query and key lengths are
  *    both S). causal == 0: every row sees all S keys.
  *  - scale: any finite float; the usual value is 1/sqrt(D).
- *  - D must be 64 or 128. S, B, Hq, Hkv >= 1, and B*Hq*S*D < 2^40.
+ *  - D must be 64 or 128. S, B, Hq, Hkv >= 1, B*Hq*S*D < 2^40 and S*D < 2^31
+ *    (the kernels address rows within one head with 32-bit offsets).
  *  - stream: a hipStream_t passed as void*; NULL means the null stream.
  *    Calls are asynchronous: ATTN_OK means the kernels were enqueued. A device
  *    fault surfaces at the caller's next synchronisation.
@@ -44,7 +45,8 @@ extern "C" {
 enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,          /* a required pointer is NULL */
-    ATTN_ERR_SHAPE = 2,         /* B, Hq, Hkv, S, D or Dv < 1, or B*Hq*S*max(D, Dv) >= 2^40 */
+    ATTN_ERR_SHAPE = 2,         /* B, Hq, Hkv, S, D or Dv < 1, B*Hq*S*max(D, Dv) >= 2^40,
+                                   or S*max(D, Dv) >= 2^31 */
     ATTN_ERR_GQA = 3,           /* Hq is not a multiple of Hkv */
     ATTN_ERR_UNSUPPORTED_D = 4, /* D (or Dv) is neither 64 nor 128 */
     ATTN_ERR_ALIGN = 5,         /* a tensor or workspace pointer is not 16-byte aligned */
@@ -154,7 +156,7 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
  * needs o and lse from attn_fwd_vdim with the same arguments. With Dv == D these
  * are attn_fwd / attn_bwd (window = 0) and attn_fwd_window / attn_bwd_window.
  * Every other rule, layout and error is that of attn_fwd and attn_bwd, with
- * B*Hq*S*max(D, Dv) < 2^40.
+ * B*Hq*S*max(D, Dv) < 2^40 and S*max(D, Dv) < 2^31.
  */
 int attn_fwd_vdim(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int S, int D, int Dv, int causal, int window,

@@ -80,6 +80,9 @@ def test_fwd_null(name):
     (dict(B=0), fa.ATTN_ERR_SHAPE), (dict(Hq=0), fa.ATTN_ERR_SHAPE), (dict(Hkv=0), fa.ATTN_ERR_SHAPE),
     (dict(S=0), fa.ATTN_ERR_SHAPE), (dict(S=-5), fa.ATTN_ERR_SHAPE), (dict(D=0), fa.ATTN_ERR_SHAPE),
     (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, S=1 << 12, D=128), fa.ATTN_ERR_SHAPE),
+    # one head's rows must be addressable with 32-bit offsets: S * D < 2^31
+    (dict(B=1, Hq=1, Hkv=1, S=1 << 24, D=128), fa.ATTN_ERR_SHAPE),
+    (dict(B=1, Hq=1, Hkv=1, S=(1 << 25) + 1, D=64), fa.ATTN_ERR_SHAPE),
     (dict(Hq=6, Hkv=4), fa.ATTN_ERR_GQA), (dict(D=96), fa.ATTN_ERR_UNSUPPORTED_D),
     (dict(D=256), fa.ATTN_ERR_UNSUPPORTED_D), (dict(scale=math.nan), fa.ATTN_ERR_SCALE),
     (dict(scale=math.inf), fa.ATTN_ERR_SCALE), (dict(q=MIS), fa.ATTN_ERR_ALIGN),
@@ -161,6 +164,7 @@ def bwd_vdim(*, window=0, causal=1, dv=P, B=1, Hq=4, Hkv=2, S=128, D=128, Dv=64,
     (dict(Hq=6, Hkv=4), fa.ATTN_ERR_GQA), (dict(scale=math.nan), fa.ATTN_ERR_SCALE),
     # the size limit counts the wider of the two head dimensions
     (dict(B=1 << 19, Hq=1 << 10, Hkv=1 << 10, S=1 << 12, D=64, Dv=128), fa.ATTN_ERR_SHAPE),
+    (dict(B=1, Hq=1, Hkv=1, S=1 << 24, D=64, Dv=128), fa.ATTN_ERR_SHAPE),
 ])
 def test_vdim_rejects(kw, code):
     assert fwd_vdim(**kw) == code
