@@ -257,6 +257,30 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
         __builtin_amdgcn_s_setprio(0);
     };
 
+    // Probabilities exp2(s c - m) of the tile as bf16 B operands (and their bf16
+    // remainders on the exact path); returns this lane's sum of the 32.
+    auto probs = [&]() {
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(fmaf(sc[t >> 1][8 * (t & 1) + e], c, -m));
+                rs[e & 3] += p[e];
+            }
+            pk[t] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            if (PRECISE)
+                pl[t] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
+                              bf_lo(p[6]), bf_lo(p[7]));
+        }
+        return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    };
+    // The maximum can be skipped only where the running maximum may lag
+    // (slack > 0); with slack 0 it is tracked exactly.
+    const bool fast_max = a.max_slack >= 1.0f;
+    const float max_bound = exp2f(a.max_slack - 1.0f);
+
     // Softmax phase of tile j: mask (last tile only), row maxima, lazy move of
     // the running maximum, probabilities as bf16 B operands, row sums.
     auto softmax_phase = [&](int j) {
@@ -274,42 +298,46 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
                     if (off > lim || off < lo) sc[kb][r] = -INFINITY;
                 }
         }
-        float mx0 = fmaxf(sc[0][0], sc[0][1]), mx1 = fmaxf(sc[1][0], sc[1][1]);
-#pragma unroll
-        for (int r = 2; r < 16; ++r) {
-            mx0 = fmaxf(mx0, sc[0][r]);
-            mx1 = fmaxf(mx1, sc[1][r]);
+        // Past a wave's first tile the maximum is usually not needed: if every
+        // lane's 32 probabilities against the current m sum to at most
+        // 2^(slack-1), each of them is at most that, so the tile maximum is
+        // within slack-1 of m (one unit of margin covers the rounding of the two
+        // forms) and the rule below would leave m alone. The probabilities and
+        // sums are then exactly those of the full step; otherwise (a new
+        // maximum, an overflow, a NaN) the full step runs on the unchanged
+        // scores.
+        bool need_max = PRECISE || !fast_max || j <= wjstart;
+        float tot = 0.0f;
+        if (!need_max) {
+            tot = probs();
+            need_max = __any(!(tot <= max_bound));
         }
-        const float mt = halves_max(fmaxf(mx0, mx1)) * c;  // c > 0
-        // The running maximum only moves when some row's grows by more than
-        // max_slack (log2 units; 8 for ordinary score spreads): until then every
-        // exp2(t - m) <= 2^slack, carried by fp32 and bf16 without loss, and the
-        // O rescale is skipped. A row's first visible key always moves it.
-        if (__any(mt > m + a.max_slack)) {
-            const float mnew = fmaxf(m, mt);
-            const float alpha = fast_exp2(m - mnew);
-            m = mnew;
-            l *= alpha;
+        if (need_max) {
+            float mx0 = fmaxf(sc[0][0], sc[0][1]), mx1 = fmaxf(sc[1][0], sc[1][1]);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
-        float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(fmaf(sc[t >> 1][8 * (t & 1) + e], c, -m));
-                rs[e & 3] += p[e];
+            for (int r = 2; r < 16; ++r) {
+                mx0 = fmaxf(mx0, sc[0][r]);
+                mx1 = fmaxf(mx1, sc[1][r]);
             }
-            pk[t] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            if (PRECISE)
-                pl[t] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
-                              bf_lo(p[6]), bf_lo(p[7]));
+            const float mt = halves_max(fmaxf(mx0, mx1)) * c;  // c > 0
+            // The running maximum only moves when some row's grows by more than
+            // max_slack (log2 units; 8 for ordinary score spreads): until then
+            // every exp2(t - m) <= 2^slack, carried by fp32 and bf16 without
+            // loss, and the O rescale is skipped. A row's first visible key
+            // always moves it.
+            if (__any(mt > m + a.max_slack)) {
+                const float mnew = fmaxf(m, mt);
+                const float alpha = fast_exp2(m - mnew);
+                m = mnew;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            tot = probs();
         }
-        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        l += tot;
     };
 
     // Prologue: tile j sits in slot j & 1 of its ring; the first two K tiles and
