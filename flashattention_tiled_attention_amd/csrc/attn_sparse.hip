@@ -211,6 +211,8 @@ __device__ __forceinline__ void sparse_fwd_body(const SparseArgs& a, unsigned ch
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = zero16();
     float m = -1e30f, l = 0.0f;
+    const bool fast_max = a.max_slack >= 1.0f;
+    const float max_bound = exp2f(a.max_slack - 1.0f);
 
     const int nT = (n + BK - 1) / BK;
     if (nT > 0) {
@@ -237,41 +239,58 @@ __device__ __forceinline__ void sparse_fwd_body(const SparseArgs& a, unsigned ch
                 for (int r = 0; r < 16; ++r)
                     if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sc[kb][r] = -INFINITY;
         }
-        float mx = fmaxf(sc[0][0], sc[0][1]);
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        const float mt = halves_max(mx) * c;  // c > 0
-        // As in the dense forward, the running maximum only moves when some row's
-        // grows by more than max_slack (log2 units): until then every probability is
-        // at most 2^slack, exact enough in fp32 and bf16, and O is not rescaled.
-        if (__any(mt > m + a.max_slack)) {
-            const float mnew = fmaxf(m, mt);
-            const float alpha = fast_exp2(m - mnew);
-            m = mnew;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
         bf16x8 pk[2 * NB], pl[2 * NB];
-        float rs = 0.0f;
+        auto probs = [&]() {  // exp2(s c - m) as bf16 operands; this lane's sum
+            float rs = 0.0f;
 #pragma unroll
-        for (int t2 = 0; t2 < 2 * NB; ++t2) {
-            float p[8];
+            for (int t2 = 0; t2 < 2 * NB; ++t2) {
+                float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(fmaf(sc[t2 >> 1][8 * (t2 & 1) + e], c, -m));
-                rs += p[e];
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = fast_exp2(fmaf(sc[t2 >> 1][8 * (t2 & 1) + e], c, -m));
+                    rs += p[e];
+                }
+                pk[t2] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+                if (PRECISE)
+                    pl[t2] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]),
+                                   bf_lo(p[5]), bf_lo(p[6]), bf_lo(p[7]));
             }
-            pk[t2] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            if (PRECISE)
-                pl[t2] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
-                               bf_lo(p[6]), bf_lo(p[7]));
+            return rs;
+        };
+        // As in the dense forward, past the first tile the maximum is taken only
+        // when some lane's probabilities against the current m sum past
+        // 2^(slack-1); below that the rule that follows would leave m alone, so
+        // the result is the same.
+        bool need_max = PRECISE || !fast_max || t == 0;
+        float tot = 0.0f;
+        if (!need_max) {
+            tot = probs();
+            need_max = __any(!(tot <= max_bound));
         }
-        l += rs;
+        if (need_max) {
+            float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+            const float mt = halves_max(mx) * c;  // c > 0
+            // As in the dense forward, the running maximum only moves when some
+            // row's grows by more than max_slack (log2 units): until then every
+            // probability is at most 2^slack, exact enough in fp32 and bf16, and O
+            // is not rescaled.
+            if (__any(mt > m + a.max_slack)) {
+                const float mnew = fmaxf(m, mt);
+                const float alpha = fast_exp2(m - mnew);
+                m = mnew;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            tot = probs();
+        }
+        l += tot;
         // O^T += V^T P^T over 16-slot steps; V^T through transpose loads.
 #pragma unroll
         for (int t2 = 0; t2 < 2 * NB; ++t2)
