@@ -85,12 +85,19 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
     flops, secs = row_flops(rows), t_f
     sample = "forward: %d of %d query rows (uniform without replacement)" % (n, B * Hq * S)
     if with_bwd:
-        # one group's key rows: the group's per-row statistics plus dK/dV of sampled keys
+        # one group's key rows: the group's per-row statistics plus dK/dV of sampled keys;
+        # a first call on 64 keys sizes the timed one to the rest of the budget
+        def bwd_sample(nk):
+            keys = np.sort(rng.choice(S, size=nk, replace=False)).astype(np.int64)
+            t = time.perf_counter()
+            oracle.bwd_rows(q, k, v, dout, np.zeros(0, np.int64), keys, causal, scale, W)
+            return keys, time.perf_counter() - t
         nk = 64
-        keys = np.sort(rng.choice(S, size=nk, replace=False)).astype(np.int64)
-        t = time.perf_counter()
-        oracle.bwd_rows(q, k, v, dout, np.zeros(0, np.int64), keys, causal, scale, W)
-        t_b = time.perf_counter() - t
+        keys, t_b = bwd_sample(nk)
+        rest = max(target_s - t_f - t_b, 0.0)
+        if rest > t_b:
+            nk = int(min(S, nk * rest / t_b))
+            keys, t_b = bwd_sample(nk)
         G = Hq // Hkv
         stat_flops = G * row_flops(np.arange(S, dtype=np.int64))           # S, P and dP rows of the group
         seen_by = (S - keys) if causal else np.full_like(keys, S)         # query rows that see each key
