@@ -463,18 +463,19 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
     const int steps = (total + kKvSplits - 1) / kKvSplits;
 
     // Q / dO copies of a pair: copy n of wave w2 fills tile rows (w2*N + n) *
-    // ROWS_PER_COPY + lane / CH. Rows past S repeat row S-1; their lse is +inf,
-    // so their probabilities, and every term they touch, are exactly 0.
-    int qcrow[QC::N], qccol[QC::N], dcrow[DC::N], dccol[DC::N];
+    // ROWS_PER_COPY + lane / CH, kept as this lane's byte offset within a tile of
+    // whole rows. Rows past S repeat row S-1; their lse is +inf, so their
+    // probabilities, and every term they touch, are exactly 0.
+    uint32_t qcoff[QC::N], dcoff[DC::N];
 #pragma unroll
     for (int n = 0; n < QC::N; ++n) {
-        qcrow[n] = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
-        qccol[n] = (((lane % QC::CH) ^ swz_f<D>(qcrow[n]))) * 8;
+        const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+        qcoff[n] = (uint32_t)(row * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8) * 2u;
     }
 #pragma unroll
-    for (int n = 0; n < DC::N; ++n) {
-        dcrow[n] = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
-        dccol[n] = (((lane % DC::CH) ^ swz_f<DV>(dcrow[n]))) * 8;
+    for (int n = 0; n < DC::N; ++n) {  // the same as qcoff when D == DV
+        const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
+        dcoff[n] = D == DV ? 0u : (uint32_t)(row * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8) * 2u;
     }
     float lst = 0.f, dlst = 0.f;
     auto fetch = [&](int step) {  // async copies of Q/dO + lse/delta into registers
@@ -484,22 +485,37 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
         const int g = it / per_g, qi = qi_first + it % per_g;
         const size_t rb = ((size_t)b * a.Hq + hkv * G + g) * (size_t)S;
         const int qr0 = qi * kKvBQ;
-        if (D == DV) {  // one address for both tensors
+        // A whole tile inside S: its first row's address (scalar) plus lane offsets.
+        // The body with the exact path keeps per-lane addresses: it has no
+        // registers to spare for the scalar form's.
+        if (!MAYBE_PRECISE && qr0 + kKvBQ <= S) {
+            const uint16_t* qb = a.q + (rb + qr0) * D;
+            const uint16_t* db = a.dout + (rb + qr0) * DV;
+#pragma unroll
+            for (int n = 0; n < QC::N; ++n)
+                copy16_to_lds_s(qb, qcoff[n], stage_q(st) + (w2 * QC::N + n) * 512);
+#pragma unroll
+            for (int n = 0; n < DC::N; ++n)
+                copy16_to_lds_s(db, D == DV ? qcoff[n] : dcoff[n], stage_do(st) + (w2 * DC::N + n) * 512);
+        } else if (D == DV) {  // one address for both tensors
 #pragma unroll
             for (int n = 0; n < QC::N; ++n) {
-                const size_t off = (rb + min(qr0 + qcrow[n], S - 1)) * D + qccol[n];
+                const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+                const size_t off = (rb + min(qr0 + row, S - 1)) * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8;
                 copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
                 copy16_to_lds(a.dout + off, stage_do(st) + (w2 * QC::N + n) * 512);
             }
         } else {
 #pragma unroll
             for (int n = 0; n < QC::N; ++n) {
-                const size_t off = (rb + min(qr0 + qcrow[n], S - 1)) * D + qccol[n];
+                const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+                const size_t off = (rb + min(qr0 + row, S - 1)) * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8;
                 copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
             }
 #pragma unroll
             for (int n = 0; n < DC::N; ++n) {
-                const size_t off = (rb + min(qr0 + dcrow[n], S - 1)) * DV + dccol[n];
+                const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
+                const size_t off = (rb + min(qr0 + row, S - 1)) * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8;
                 copy16_to_lds(a.dout + off, stage_do(st) + (w2 * DC::N + n) * 512);
             }
         }

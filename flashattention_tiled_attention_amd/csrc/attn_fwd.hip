@@ -156,31 +156,45 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     // ROWS_PER_COPY + lane / CH, physical chunk lane % CH, which holds logical
     // chunk (lane % CH) ^ swz_f(row). Rows past the end repeat row S-1: their
     // scores are masked and their probabilities are exactly 0.
-    int kcrow[KC::N], kccol[KC::N], vcrow[VC::N], vccol[VC::N];
+    // This lane's copy n as a byte offset within a tile of whole rows: a tile that
+    // lies inside S is copied from its first row's address (scalar) plus these.
+    uint32_t kcoff[KC::N], vcoff[VC::N];
 #pragma unroll
     for (int n = 0; n < KC::N; ++n) {
-        kcrow[n] = (wave * KC::N + n) * KC::ROWS_PER_COPY + lane / KC::CH;
-        kccol[n] = (((lane % KC::CH) ^ swz_f<D>(kcrow[n]))) * 8;
+        const int row = (wave * KC::N + n) * KC::ROWS_PER_COPY + lane / KC::CH;
+        kcoff[n] = (uint32_t)(row * D + ((lane % KC::CH) ^ swz_f<D>(row)) * 8) * 2u;
     }
 #pragma unroll
     for (int n = 0; n < VC::N; ++n) {
-        vcrow[n] = (wave * VC::N + n) * VC::ROWS_PER_COPY + lane / VC::CH;
-        vccol[n] = (((lane % VC::CH) ^ swz_f<DV>(vcrow[n]))) * 8;
+        const int row = (wave * VC::N + n) * VC::ROWS_PER_COPY + lane / VC::CH;
+        vcoff[n] = (uint32_t)(row * DV + ((lane % VC::CH) ^ swz_f<DV>(row)) * 8) * 2u;
     }
     auto copy_k = [&](__bf16* dst, int j) {
         const int k0 = j * kFwdBK;
+        if (k0 + kFwdBK <= S) {
+            const uint16_t* base = Kp + (size_t)k0 * D;
 #pragma unroll
-        for (int n = 0; n < KC::N; ++n) {
-            const int key = min(k0 + kcrow[n], S - 1);
-            copy16_to_lds(Kp + (uint32_t)(key * D + kccol[n]), dst + (wave * KC::N + n) * 512);
+            for (int n = 0; n < KC::N; ++n) copy16_to_lds_s(base, kcoff[n], dst + (wave * KC::N + n) * 512);
+            return;
+        }
+#pragma unroll
+        for (int n = 0; n < KC::N; ++n) {  // the last tile: rows past S repeat row S-1
+            const int e = kcoff[n] >> 1, key = min(k0 + e / D, S - 1);
+            copy16_to_lds(Kp + (uint32_t)(key * D + e % D), dst + (wave * KC::N + n) * 512);
         }
     };
     auto copy_v = [&](__bf16* dst, int j) {
         const int k0 = j * kFwdBK;
+        if (k0 + kFwdBK <= S) {
+            const uint16_t* base = Vp + (size_t)k0 * DV;
+#pragma unroll
+            for (int n = 0; n < VC::N; ++n) copy16_to_lds_s(base, vcoff[n], dst + (wave * VC::N + n) * 512);
+            return;
+        }
 #pragma unroll
         for (int n = 0; n < VC::N; ++n) {
-            const int key = min(k0 + vcrow[n], S - 1);
-            copy16_to_lds(Vp + (uint32_t)(key * DV + vccol[n]), dst + (wave * VC::N + n) * 512);
+            const int e = vcoff[n] >> 1, key = min(k0 + e / DV, S - 1);
+            copy16_to_lds(Vp + (uint32_t)(key * DV + e % DV), dst + (wave * VC::N + n) * 512);
         }
     };
     // Per-lane read offsets (elements) into a slot: K rows (b128, A operand) for

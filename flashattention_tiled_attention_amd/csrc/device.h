@@ -125,6 +125,26 @@ __device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_b
         : "v"(gsrc), "s"(lds)
         : "memory");
 }
+// The same copy from a wave-uniform base address held in scalar registers plus a
+// per-lane 32-bit byte offset (the instruction's saddr form): a tile copy whose
+// per-lane offsets are fixed then needs no vector address arithmetic per step.
+// sbase must be the same for every lane of the wave.
+__device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t lane_byte_off, void* lds_wave_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS void*)lds_wave_base);
+    // (readfirstlane returns a signed int: each half is taken back to 32 unsigned
+    // bits before widening, or a low half with bit 31 set would fill the high half)
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t base = ((uint64_t)hi << 32) | lo;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(lane_byte_off), "s"(base), "s"(lds)
+        : "memory");
+}
 // Wait until every copy this wave issued has landed in LDS (s_waitcnt 0). The
 // compiler sees this wait, so it also knows that every vector-memory load it
 // issued before is complete; otherwise it would keep counter waits for those
