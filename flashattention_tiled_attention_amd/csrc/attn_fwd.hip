@@ -50,6 +50,7 @@
 // band's lower edge.
 #include "device.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -222,10 +223,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     bf16x8 pl[4];   // their bf16 remainders (PRECISE only)
 
     // Matrix phase of tile j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
-    auto matrix_phase = [&](int j) {
+    // par: std::integral_constant holding j & 1, or -1 to take it from j at run time.
+    auto matrix_phase = [&](int j, auto par) {
+        constexpr int PC = decltype(par)::value;
+        const int P = PC < 0 ? (j & 1) : PC;  // a constant parity folds the slot into the reads' offsets
         __builtin_amdgcn_s_setprio(1);
         if (j - 1 >= wjstart && j - 1 < wjend) {
-            const __bf16* Vs = Vring + ((j - 1) & 1) * T::VTILE;
+            const __bf16* Vs = Vring + (PC < 0 ? ((j - 1) & 1) : (P ^ 1)) * T::VTILE;
             constexpr int MPER = PRECISE ? 2 : 1;  // MFMAs per V^T operand
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -249,7 +253,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             __builtin_amdgcn_sched_barrier(0);
         }
         if (j >= wjstart && j < wjend) {
-            const __bf16* Ks = Kring + (j & 1) * T::KTILE;
+            const __bf16* Ks = Kring + P * T::KTILE;
             sc[0] = zero16();
             sc[1] = zero16();
 #pragma unroll
@@ -377,10 +381,50 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             if (s < jend) copy_v(Vring + (s & 1) * T::VTILE, s);
         }
     };
-    if (grp == 0) {
+    //
+    // Causal (and windowed) at D = DV = 128, the steps run in pairs, so that each
+    // step's slot parity is a constant and the slot offsets fold into the LDS
+    // reads' immediate offsets (16 address additions fewer per matrix phase). At
+    // D = 64 the doubled loop body measured slower, and the non-causal D = 128
+    // kernel, whose exact body is larger, runs out of registers with it; there the
+    // parity stays a run-time value.
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    using AnyParity = std::integral_constant<int, -1>;
+    constexpr bool kPaired = CAUSAL && D == 128 && DV == 128;
+    if constexpr (kPaired) {
+        auto run_steps = [&](auto step) {
+            int s = jstart;
+            if (s & 1) step(s++, Odd{});
+            for (; s + 1 <= jend; s += 2) {
+                step(s, Even{});
+                step(s + 1, Odd{});
+            }
+            if (s <= jend) step(s, Even{});
+        };
+        if (grp == 0) {
+            run_steps([&](int s, auto par) {
+                refill(s);
+                matrix_phase(s, par);
+                __syncthreads();
+                softmax_phase(s);
+                wait_copies();
+                __syncthreads();
+            });
+        } else {
+            run_steps([&](int s, auto par) {
+                refill(s);
+                softmax_phase(s - 1);
+                __syncthreads();
+                matrix_phase(s, par);
+                wait_copies();
+                __syncthreads();
+            });
+        }
+    } else if (grp == 0) {
         for (int s = jstart; s <= jend; ++s) {
             refill(s);
-            matrix_phase(s);
+            matrix_phase(s, AnyParity{});
             __syncthreads();
             softmax_phase(s);
             wait_copies();
@@ -391,7 +435,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             refill(s);
             softmax_phase(s - 1);
             __syncthreads();
-            matrix_phase(s);
+            matrix_phase(s, AnyParity{});
             wait_copies();
             __syncthreads();
         }

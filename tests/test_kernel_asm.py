@@ -179,6 +179,9 @@ def test_m0_written_only_by_tile_copies(asm):
     for src, lines in asm.items():
         for k, l in enumerate(lines):
             if re.search(r"\bm0\b", l) and not l.strip().startswith(";"):
-                assert l.strip().startswith("s_mov_b32 m0, s"), "%s: unexpected M0 use: %s" % (src, l.strip())
+                # the copy's own M0 write; its source is whichever scalar register the
+                # compiler gave the asm operand (vcc_lo included)
+                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", l.strip()), \
+                    "%s: unexpected M0 use: %s" % (src, l.strip())
                 nxt = [x.strip() for x in lines[k + 1:k + 3]]
                 assert nxt[0] == "s_nop 0" and nxt[1].startswith("global_load_lds_dwordx4"), (src, nxt)
