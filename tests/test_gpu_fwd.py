@@ -109,3 +109,32 @@ def test_zero_query_gives_prefix_mean():
     assert_close(o, prefix, "Q=0 prefix mean")
     assert_close(lse, np.broadcast_to(np.log(np.arange(1, S + 1.0)), lse.shape), "Q=0 lse",
                  tol_max=TOL_LSE, tol_mean=TOL_LSE)
+
+
+@pytest.mark.parametrize("mode", ["ramp", "spike"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_maximum_moving_after_the_first_tile(mode, D, causal):
+    """Rows whose maximum keeps growing, or jumps, after their first key tile: past a
+    wave's first tile the forward takes the row maximum only when the tile's
+    probabilities against the running maximum sum past a bound, so these inputs
+    drive both the skipped and the full step, and the O rescale."""
+    from flashattention_tiled_attention_amd.inputs import bf16_bits, bf16_to_f32
+    B, Hq, Hkv, S = 1, 4, 2, 700
+    print("case mode=%s D=%d causal=%d S=%d" % (mode, D, causal, S), flush=True)
+    q, k, v = qkv(B, Hq, Hkv, S, D, 11)
+    qf, kf = bf16_to_f32(q), bf16_to_f32(k)
+    if mode == "ramp":   # key norms grow fourfold along the sequence
+        kf = kf * (1.0 + 3.0 * np.arange(S, dtype=np.float32) / S)[None, None, :, None]
+    else:                # queries share a direction that two late keys point along
+        qf = qf + 1.0
+        for t in (300, 650):
+            kf[:, :, t, :] = 2.5
+    # halved values keep |O| below 4 where a row is dominated by one or two keys: the
+    # bf16 store of O alone costs up to 2^-6 at |O| >= 4, more than the bar
+    q, k, v = bf16_bits(qf), bf16_bits(kf), bf16_bits(bf16_to_f32(v) * 0.5)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal, scale)
+    assert_close(o, o_ref, "O")
+    assert_close(lse, lse_ref, "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)

@@ -187,3 +187,26 @@ def test_full_size_csa_sampled(name):
     assert_close(dv.sum(axis=2), dof.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=(2, 3)), "sum_j dV_j",
                  tol_max=0.5, tol_mean=0.15)
     assert_close(dk.sum(axis=2), np.zeros((B, Hkv, D)), "sum_j dK_j", tol_max=0.5, tol_mean=0.15)
+
+
+@pytest.mark.parametrize("mode", ["ramp", "spike"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_row_maximum_moving_after_the_first_tile(mode, D):
+    """Lists whose later slots score far above their first 32: past a row block's first
+    tile the sparse forward takes the row maximum only when the probabilities against
+    the running maximum sum past a bound, so these lists drive both the skipped and
+    the full step, and the O rescale. Values are halved to keep |O| where the bf16
+    store of O stays within the bar."""
+    from flashattention_tiled_attention_amd.inputs import bf16_bits
+    B, Hq, Hkv, S, N, topk = 1, 4, 1, 48, 400, 300
+    q, k, v = sparse_qkv(B, Hq, Hkv, S, N, D, seed=21 + D)[:3]
+    qf, kf = bf16_to_f32(q), bf16_to_f32(k)
+    idx = np.tile(np.arange(topk, dtype=np.int32)[None, None, :], (B, S, 1))  # slot j lists row j
+    if mode == "ramp":   # row norms grow fourfold along the slots
+        kf[:, :, :topk] *= (1.0 + 3.0 * np.arange(topk, dtype=np.float32) / topk)[None, None, :, None]
+    else:                # queries share a direction that two late rows point along
+        qf = qf + 1.0
+        for r in (150, 290):
+            kf[:, :, r, :] = 2.5
+    q, k, v = bf16_bits(qf), bf16_bits(kf), bf16_bits(bf16_to_f32(v) * 0.5)
+    check(q, k, v, idx, None, 1.0 / math.sqrt(D), "max moving %s D=%d" % (mode, D))
