@@ -85,30 +85,29 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
     flops, secs = row_flops(rows), t_f
     sample = "forward: %d of %d query rows (uniform without replacement)" % (n, B * Hq * S)
     if with_bwd:
-        # one group's key rows: the group's per-row statistics plus dK/dV of sampled keys;
-        # a first call on 64 keys sizes the timed one to the rest of the budget
-        def bwd_sample(nk):
-            keys = np.sort(rng.choice(S, size=nk, replace=False)).astype(np.int64)
-            t = time.perf_counter()
-            oracle.bwd_rows(q, k, v, dout, np.zeros(0, np.int64), keys, causal, scale, W)
-            return keys, time.perf_counter() - t
-        nk = 64
-        keys, t_b = bwd_sample(nk)
-        rest = max(target_s - t_f - t_b, 0.0)
-        if rest > t_b:
-            nk = int(min(S, nk * rest / t_b))
-            keys, t_b = bwd_sample(nk)
+        # whole K/V groups, one oracle call each, until the budget is spent: a group's
+        # per-row statistics (S, P and dP rows of its query heads) and dK/dV of all its keys
         G = Hq // Hkv
-        stat_flops = G * row_flops(np.arange(S, dtype=np.int64))           # S, P and dP rows of the group
-        seen_by = (S - keys) if causal else np.full_like(keys, S)         # query rows that see each key
+        stat_flops = G * row_flops(np.arange(S, dtype=np.int64))
+        seen_by = (S - np.arange(S)) if causal else np.full(S, S)          # query rows that see each key
         if W:
             seen_by = np.minimum(seen_by, W)
         key_flops = float(np.sum(G * pf["dkv_kernel"] * seen_by))
-        # the group's statistics are counted as work at the forward rate; their time is in t_b
-        flops += stat_flops + key_flops
+        rest = max(target_s - t_f, 0.0)
+        t_b, groups = 0.0, 0
+        for g in range(B * Hkv):
+            keys = g * S + np.arange(S, dtype=np.int64)
+            t = time.perf_counter()
+            oracle.bwd_rows(q, k, v, dout, np.zeros(0, np.int64), keys, causal, scale, W)
+            t_b += time.perf_counter() - t
+            groups += 1
+            if t_b >= rest:
+                break
+        # the groups' statistics are counted as work at the forward rate; their time is in t_b
+        flops += groups * (stat_flops + key_flops)
         secs += t_b
-        sample += "; backward: row statistics of 1 of %d kv groups + dK/dV of %d of its %d keys" % (
-            B * Hkv, nk, S)
+        sample += "; backward: row statistics and dK/dV of all keys of %d of %d kv groups" % (
+            groups, B * Hkv)
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": sample, "seconds": round(secs, 2)}
 
