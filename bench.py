@@ -109,7 +109,7 @@ def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
         sample += "; backward: row statistics and dK/dV of all keys of %d of %d kv groups" % (
             groups, B * Hkv)
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": sample, "seconds": round(secs, 2)}
+            "kind": "oracle", "sample": sample, "seconds": round(secs, 2), "flop": flops}
 
 
 def cpu_baseline_sparse(q, k, v, dout, idx, cfg, target_s, with_bwd):

@@ -84,3 +84,25 @@ def test_traffic_record_follows_the_source_hash(tmp_path, monkeypatch, kernel):
     # no record, no figure
     rec.unlink()
     assert bench.hbm_traffic(kernel) is None
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 16)])
+def test_cpu_baseline_counts_whole_groups(causal, window):
+    """The oracle baseline on a small workload: with a generous budget it takes every
+    query row and every K/V group, and counts the oracle's own work: per visible pair,
+    the forward's products for every query row, and per K/V group its rows' statistics
+    (at the forward rate) plus the dK/dV kernel's products."""
+    from flashattention_tiled_attention_amd import inputs
+    B, Hq, Hkv, S, D = 1, 4, 2, 64, 64
+    cfg = dict(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, causal=causal, window=window)
+    q, k, v, do = inputs.qkv(B, Hq, Hkv, S, D, 0, with_dout=True)
+    r = bench.cpu_baseline(q, k, v, do, cfg, 30.0, True)
+    assert "%d of %d query rows" % (B * Hq * S, B * Hq * S) in r["sample"]
+    assert "%d of %d kv groups" % (B * Hkv, B * Hkv) in r["sample"]
+    # the oracle's own work: every visible pair (row i of a causal head sees i + 1 keys)
+    pairs = sum(min(i + 1, window) if window else (i + 1 if causal else S) for i in range(S))
+    pf = bench.pair_flops(D, D)
+    # forward rows + per group: the statistics (at the forward rate) and the dK/dV products
+    expect = B * Hq * pairs * pf["fwd"] + B * Hkv * (Hq // Hkv) * pairs * (pf["fwd"] + pf["dkv_kernel"])
+    assert r["flop"] == pytest.approx(expect, rel=1e-12)
+    assert r["kind"] == "oracle" and r["cores"] >= 1
