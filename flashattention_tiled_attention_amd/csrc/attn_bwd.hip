@@ -45,6 +45,7 @@
 // the band and mask the tiles that cross either of its edges.
 #include "device.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -214,11 +215,14 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
         copy_kv(jstart & 1, jstart);
         wait_copies();
         __syncthreads();
-        for (int j = jstart; j < jend; ++j) {
+        // Tiles in pairs, so that each tile's ring slot (par = j & 1) is a constant
+        // and the slot offset folds into the LDS reads' immediate offsets.
+        auto step = [&](int j, auto par) {
             if (j + 1 < jend) copy_kv((j + 1) & 1, j + 1);
             if (j >= wjstart && j < wjend) {
-                const __bf16* Ks = Kring + (j & 1) * T::KTILE;
-                const __bf16* Vs = Vring + (j & 1) * T::VTILE;
+                constexpr int P = decltype(par)::value;
+                const __bf16* Ks = Kring + P * T::KTILE;
+                const __bf16* Vs = Vring + P * T::VTILE;
                 const int k0 = j * kDqBK;
                 const bool need_mask = j == wjend - 1 || (W > 0 && k0 < row0 + 32 - W);
 #pragma unroll
@@ -273,7 +277,14 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
             }
             wait_copies();
             __syncthreads();
+        };
+        int j = jstart;
+        if (j & 1) step(j++, std::integral_constant<int, 1>{});
+        for (; j + 1 < jend; j += 2) {
+            step(j, std::integral_constant<int, 0>{});
+            step(j + 1, std::integral_constant<int, 1>{});
         }
+        if (j < jend) step(j, std::integral_constant<int, 0>{});
         if (pass == 0) delta = halves_sum(dacc);
     }
 
