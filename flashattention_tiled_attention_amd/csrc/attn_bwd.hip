@@ -177,6 +177,23 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
     }
     auto copy_kv = [&](int slot, int j) {
         const int k0 = j * kDqBK;
+        if (k0 + kDqBK <= S) {  // whole tile: scalar row address plus lane offsets made here
+            const uint16_t* kb = Kp + (size_t)k0 * D;
+            const uint16_t* vb = Vp + (size_t)k0 * DV;
+#pragma unroll
+            for (int n = 0; n < KC::N; ++n) {
+                const int row = (wave * KC::N + n) * KC::ROWS_PER_COPY + lane / KC::CH;
+                copy16_to_lds_s(kb, (uint32_t)(row * D + ((lane % KC::CH) ^ swz_f<D>(row)) * 8) * 2u,
+                                Kring + slot * T::KTILE + (wave * KC::N + n) * 512);
+            }
+#pragma unroll
+            for (int n = 0; n < VC::N; ++n) {
+                const int row = (wave * VC::N + n) * VC::ROWS_PER_COPY + lane / VC::CH;
+                copy16_to_lds_s(vb, (uint32_t)(row * DV + ((lane % VC::CH) ^ swz_f<DV>(row)) * 8) * 2u,
+                                Vring + slot * T::VTILE + (wave * VC::N + n) * 512);
+            }
+            return;
+        }
 #pragma unroll
         for (int n = 0; n < KC::N; ++n) {
             const int key = min(k0 + kcrow[n], S - 1);
