@@ -185,3 +185,19 @@ def test_m0_written_only_by_tile_copies(asm):
                     "%s: unexpected M0 use: %s" % (src, l.strip())
                 nxt = [x.strip() for x in lines[k + 1:k + 3]]
                 assert nxt[0] == "s_nop 0" and nxt[1].startswith("global_load_lds_dwordx4"), (src, nxt)
+
+
+def test_scalar_copy_bases_are_not_sign_extended(asm):
+    """The saddr tile copies take a 64-bit base rebuilt from two readfirstlane halves.
+    readfirstlane returns a signed int, and a low half widened as signed would fill the
+    high half with ones for any address with bit 31 set: the compiler then emits
+    s_bfe_i64 to build the base. None of the attention kernels needs a signed 64-bit
+    field extract, so its absence pins the unsigned widening."""
+    found = 0
+    for src, lines in asm.items():
+        for l in lines:
+            t = l.strip()
+            if re.match(r"global_load_lds_dwordx4 v\d+, s\[\d+:\d+\]", t):
+                found += 1
+            assert not t.startswith("s_bfe_i64"), "%s: sign-extending field extract: %s" % (src, t)
+    assert found > 0, "no saddr tile copies found"
