@@ -113,15 +113,15 @@ def test_zero_query_gives_prefix_mean():
 
 @pytest.mark.parametrize("mode", ["ramp", "spike"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("causal", [False, True])
-def test_row_maximum_moving_after_the_first_tile(mode, D, causal):
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 100), (True, 300)])
+def test_row_maximum_moving_after_the_first_tile(mode, D, causal, window):
     """Rows whose maximum keeps growing, or jumps, after their first key tile: past a
     wave's first tile the forward takes the row maximum only when the tile's
     probabilities against the running maximum sum past a bound, so these inputs
     drive both the skipped and the full step, and the O rescale."""
     from flashattention_tiled_attention_amd.inputs import bf16_bits, bf16_to_f32
     B, Hq, Hkv, S = 1, 4, 2, 700
-    print("case mode=%s D=%d causal=%d S=%d" % (mode, D, causal, S), flush=True)
+    print("case mode=%s D=%d causal=%d window=%d S=%d" % (mode, D, causal, window, S), flush=True)
     q, k, v = qkv(B, Hq, Hkv, S, D, 11)
     qf, kf = bf16_to_f32(q), bf16_to_f32(k)
     if mode == "ramp":   # key norms grow fourfold along the sequence
@@ -134,7 +134,13 @@ def test_row_maximum_moving_after_the_first_tile(mode, D, causal):
     # bf16 store of O alone costs up to 2^-6 at |O| >= 4, more than the bar
     q, k, v = bf16_bits(qf), bf16_bits(kf), bf16_bits(bf16_to_f32(v) * 0.5)
     scale = 1.0 / math.sqrt(D)
-    o, lse = run_fwd(q, k, v, causal, scale)
-    o_ref, lse_ref = oracle.fwd(q, k, v, causal, scale)
+    if window:   # the sliding-window kernel (several query heads per workgroup)
+        import torch
+        o, lse = fa.fwd(to_dev(q), to_dev(k), to_dev(v), causal=True, scale=scale, window=window)
+        torch.cuda.synchronize()
+        o, lse = bf16_dev_to_f64(o), f32_dev_to_f64(lse)
+    else:
+        o, lse = run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal, scale, window)
     assert_close(o, o_ref, "O")
     assert_close(lse, lse_ref, "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)
