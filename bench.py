@@ -282,7 +282,7 @@ def main():
         gq = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
         gk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
         gv = torch.empty((B, Hkv, S, Dv), dtype=torch.float32, device="cuda")
-        ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal),), dtype=torch.uint8, device="cuda")
+        ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D),), dtype=torch.uint8, device="cuda")
 
         bargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, causal, scale, ws, stream)
         wargs = (dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, W, scale, ws, stream)

@@ -77,7 +77,7 @@ def load_library(path=None):
     lib.attn_sparse_bwd.restype = I
     lib.attn_sparse_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.attn_sparse_bwd_workspace_bytes.restype = Z
-    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_status_str.argtypes = [I]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -158,8 +158,8 @@ def attn_fwd_vdim(q, k, v, o, lse, causal, window, scale, stream=None):
     _fwd_call("attn_fwd_vdim", q, k, v, o, lse, (bool(causal), window), scale, stream, vdim=True)
 
 
-def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal):
-    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, int(bool(causal))))
+def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D):
+    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D))
 
 
 def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, flags, scale, workspace, stream, vdim=False):
@@ -238,7 +238,7 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, window=0):
     dq = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=q.device)
     dv = torch.empty((B, Hkv, S, Dv), dtype=torch.float32, device=q.device)
-    ws = torch.empty((attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal or bool(window)),),
+    ws = torch.empty((attn_bwd_workspace_bytes(B, Hq, Hkv, S, D),),
                      dtype=torch.uint8, device=q.device)
     if Dv != D:
         attn_bwd_vdim(q, k, v, o, lse, dout, dq, dk, dv, causal or bool(window), window, scale, ws)

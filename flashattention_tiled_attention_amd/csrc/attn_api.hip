@@ -64,15 +64,25 @@ int check_sizes(int B, int Hq, int Hkv, int S, int D, int Dv) {
     if (elems >= 1099511627776.0) return ATTN_ERR_SHAPE;  // 2^40
     // row offsets within one head are 32-bit in the kernels' tile copies
     if ((double)S * (D > Dv ? D : Dv) >= 2147483648.0) return ATTN_ERR_SHAPE;  // 2^31
-    // grid size: B * Hq * ceil(S / 128) work groups must fit a 32-bit grid
-    if ((double)B * Hq * ((S + 127) / 128) >= 2147483647.0) return ATTN_ERR_SHAPE;
+    // Every launch's work-items (workgroups x threads) must fit the 32-bit grid.
+    // Per query head the forward launches at most 2*S + 512 of them (256 rows, or
+    // 256/HW rows of HW heads, per 512-thread workgroup) and the dQ kernel at most
+    // 2*S + 256 (128 rows per 256 threads); per kv head the dK/dV kernel launches
+    // ceil(S/64) workgroups of 512 threads, at most 8*S + 512.
+    if ((double)B * Hq * (2.0 * S + 512.0) >= 4294967296.0) return ATTN_ERR_SHAPE;
+    if ((double)B * Hkv * (8.0 * S + 512.0) >= 4294967296.0) return ATTN_ERR_SHAPE;
     if (Hq % Hkv != 0) return ATTN_ERR_GQA;
     if ((D != 64 && D != 128) || (Dv != 64 && Dv != 128)) return ATTN_ERR_UNSUPPORTED_D;
     return ATTN_OK;
 }
 
+// Dense backward workspace: delta [B][Hq][S] fp32, then the per-32-row-block
+// exact-path flags [B][Hq][ceil(S/32)] int32, each part 256-byte aligned.
 size_t delta_bytes(int B, int Hq, int S) {
     return (((size_t)B * Hq * S * sizeof(float)) + 255) & ~(size_t)255;
+}
+size_t peak_bytes(int B, int Hq, int S) {
+    return (((size_t)B * Hq * ((S + 31) / 32) * sizeof(int)) + 255) & ~(size_t)255;
 }
 
 constexpr int kSparseMaxTopk = 4096;
@@ -88,8 +98,14 @@ int check_sparse_sizes(int B, int Hq, int Hkv, int S, int N, int D, int topk) {
     if (topk > kSparseMaxTopk || Hq / Hkv > attn::sparse_max_heads_per_kv()) return ATTN_ERR_SPARSE;
     // 32-bit row offsets within a head, 32-bit list entries, 32-bit grids
     if ((double)N * D >= 2147483647.0 || (double)S * topk >= 2147483647.0) return ATTN_ERR_SPARSE;
-    if ((double)B * S * Hq * ((topk + 127) / 128 + 2) >= 2147483647.0) return ATTN_ERR_SPARSE;
-    if ((double)B * Hkv * N >= 2147483647.0) return ATTN_ERR_SPARSE;
+    // Work-items (workgroups x threads) of every launch within the 32-bit grid: the
+    // forward and dQ kernels (128 threads per 64 query heads of a token), the partial
+    // kernel (256 threads per 128 list slots of a token and kv head) and the reduction
+    // (256 threads per key/value row).
+    const double heads = (double)B * S * Hkv * ((Hq / Hkv + 63) / 64);
+    if (heads * 128.0 >= 4294967296.0) return ATTN_ERR_SPARSE;
+    if ((double)B * S * Hkv * ((topk + 127) / 128) * 256.0 >= 4294967296.0) return ATTN_ERR_SPARSE;
+    if ((double)B * Hkv * N * 256.0 >= 4294967296.0) return ATTN_ERR_SPARSE;
     return ATTN_OK;
 }
 
@@ -191,10 +207,9 @@ int attn_fwd_vdim(const void* q, const void* k, const void* v, void* o, float* l
                     scale, stream);
 }
 
-size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal) {
-    (void)causal;
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
     if (check_sizes(B, Hq, Hkv, S, D, D) != ATTN_OK) return 0;
-    return delta_bytes(B, Hq, S);
+    return delta_bytes(B, Hq, S) + peak_bytes(B, Hq, S);
 }
 
 static int bwd_stages(int stages, const void* q, const void* k, const void* v, const void* o,
@@ -205,7 +220,7 @@ static int bwd_stages(int stages, const void* q, const void* k, const void* v, c
     int rc = check_sizes(B, Hq, Hkv, S, D, Dv);
     if (rc) return rc;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
-    if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal))
+    if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, S, D))
         return ATTN_ERR_WORKSPACE;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
         misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
@@ -224,18 +239,20 @@ static int bwd_stages(int stages, const void* q, const void* k, const void* v, c
     a.dk = dk;
     a.dv = dv;
     a.delta = (float*)workspace;
+    a.peak = (int*)((unsigned char*)workspace + delta_bytes(B, Hq, S));
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.G = Hq / Hkv;
     a.causal = causal ? 1 : 0;
     a.window = window;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    // Every tile takes the exact path when rows can concentrate on few keys: a
-    // peaked softmax (score spread > 2 for unit-variance inputs), where bf16
-    // rounding of P, dS and the stored O would dominate, or a window of fewer than
-    // 128 keys, where every row sees fewer keys than the first causal rows do. A
-    // window of 128 keys or more leaves the exact path to the first rows, as the
-    // causal problem does: with every row on 128 keys, bf16 P and dS keep dQ, dK
-    // and dV within 5e-3 of fp64 at the Llama-3.1-8B shape (unit-variance inputs).
+    // Rows with a probability above kPeakP take the exact path wherever the data
+    // puts them (the dQ stage finds them). Every tile takes it from the start when
+    // most rows will need it: a score spread |scale| * sqrt(D) > 2 for
+    // unit-variance inputs, or a window of fewer than 128 keys, where every row sees
+    // fewer keys than the first causal rows do. A window of 128 keys or more is left
+    // to the data, as the causal problem is: with every row on 128 keys, bf16 P and
+    // dS keep dQ, dK and dV within 5e-3 of fp64 at the Llama-3.1-8B shape
+    // (unit-variance inputs).
     a.precise_all = (fabsf(scale) * sqrtf((float)D) > 2.0f || (window > 0 && window < 128)) ? 1 : 0;
     if (attn::launch_bwd(a, D, Dv, stages, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;

@@ -13,8 +13,9 @@
 // Two kernels, ordered on the caller's stream, no atomics (deterministic):
 //   dq_kernel   one workgroup per (b, hq, 128-row query tile); K/V tiles stream
 //               from HBM straight into double-buffered, swizzled LDS tiles
-//               (global_load_lds). It also computes delta for its rows and stores
-//               it in the workspace. With a sliding window, dq_win_kernel runs the
+//               (global_load_lds). It also computes the exact delta of its rows
+//               and a flag per 32-row block (below) and stores them in the
+//               workspace. With a sliding window, dq_win_kernel runs the
 //               same body with the query heads of one kv head side by side in a
 //               workgroup (fewer rows per head, so every wave uses nearly all of
 //               the workgroup's key tiles).
@@ -25,16 +26,19 @@
 //               sums are added in LDS at the end in a fixed order, so the
 //               grouped-query sum never leaves the chip and is deterministic.
 //
-// Rows whose visible keys all lie in the first 128 keys (the first query tile
-// of a causal problem, or every row when S <= 128) can carry probabilities near
-// 1, where bf16 rounding of P and dS and the rounding of the stored O inside
-// delta are largest. For those rows delta is recomputed exactly as
-// sum_j P_ij dP_ij in fp32, and the P and dS operands are split into a bf16 high
-// part plus a bf16 remainder (two MFMAs each). When |scale| * sqrt(D) > 2 the
-// scores of unit-variance inputs spread wide enough for any row to concentrate
-// on a few keys, and the host asks for this treatment on every tile; so it does
-// for a sliding window of fewer than 128 keys, where every row sees fewer keys
-// than the first causal rows do.
+// delta is always the exact sum_j P_ij dP_ij in fp32, accumulated by the dQ
+// kernel's pass (delta = rowsum(dO * O) from the bf16-stored O is off by up to
+// 2^-9 of |dO| |O|, which the GQA sum carries into dK on rows with a large
+// probability). Rows whose largest probability exceeds kPeakP, wherever the data
+// puts them (the first rows of a causal problem, a key every later query points
+// at, inputs of large norm), take the exact path: their P and dS operands are
+// split into a bf16 high part plus a bf16 remainder (two MFMAs each), and their
+// dQ pass is made with the exact delta. The dQ kernel finds such rows in its
+// pass, makes the pass again for that workgroup, and flags each 32-row block for
+// the dK/dV kernel, which chooses its body per workgroup from the flags of the
+// query tiles it meets. The host asks for the exact path on every tile when
+// |scale| * sqrt(D) > 2 (unit-variance inputs then spread their scores wide
+// enough that most rows need it) or for a sliding window of fewer than 128 keys.
 //
 // Queries and keys have D columns and values DV (the d and d_v of Eq. (1)); each
 // is 64 or 128, in any combination: Q, K, dQ and dK are D wide, V, O, dO and dV
@@ -51,7 +55,6 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPreciseRows = 128;
 
 // ---------------------------------------------------------------------------
 // dQ (+ delta) kernel
@@ -97,13 +100,21 @@ __device__ __forceinline__ void decode_q_item(int bid, int nQ, int qt_first, int
 }
 
 
-// The PRECISE body runs the tiles whose rows need the exact path (below); the
-// plain body never touches its registers.
 // One workgroup's share: query rows q0 .. q_last of the kv head that hq reads;
 // this wave takes head hq, rows row0 .. row0+31.
+//
+// The plain body (PRECISE false) makes one pass: dS = P (dP - delta) with delta
+// from the stored O and bf16 dS operands. In the same pass it accumulates the
+// exact delta_i = sum_j P_ij dP_ij and each row's largest probability; it stores
+// the exact delta and a flag per 32-row block (a row above kPeakP) for the dK/dV
+// stage, and returns whether any row of the workgroup was above kPeakP. Then dQ is
+// not stored: the caller runs the PRECISE body with delta_given, which makes the
+// dQ pass again with the exact delta and split dS operands. Called without
+// have_delta the PRECISE body first makes pass 0, which only accumulates the
+// exact delta.
 template <int D, int DV, bool CAUSAL, bool PRECISE>
-__device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, int hq, int q0, int q_last,
-                                        int row0) {
+__device__ __forceinline__ bool dq_body(const BwdArgs& a, __bf16* smem, int b, int hq, int q0, int q_last,
+                                        int row0, bool have_delta, float& delta_io) {
     using T = DqTile<D, DV>;
     using KC = typename T::KCopy;
     using VC = typename T::VCopy;
@@ -149,7 +160,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
 #pragma unroll
         for (int dk = 0; dk < DKV; ++dk) df[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
-    float delta = halves_sum(dpart);
+    float delta = PRECISE && have_delta ? delta_io : halves_sum(dpart);
     const float lse2 = live ? a.lse[rowbase + qrow] * kLog2e : INFINITY;
 
     const int nK = (S + kDqBK - 1) / kDqBK;
@@ -224,11 +235,14 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
 
-    // Pass 0 (precise tiles only) accumulates the exact delta; the last pass
-    // forms dS and accumulates dQ^T += K^T dS^T. Tile j+1 is copied into the other
-    // slot while tile j is multiplied.
-    for (int pass = precise ? 0 : 1; pass < 2; ++pass) {
-        float dacc = 0.0f;
+    // Pass 0 (exact body without a given delta) accumulates the exact delta; the
+    // last pass forms dS and accumulates dQ^T += K^T dS^T. Tile j+1 is copied into
+    // the other slot while tile j is multiplied.
+    float dacc = 0.0f;     // sum_j P_ij dP_ij over this lane's keys
+    bool peaked = false;   // plain body: some probability of the wave's rows above kPeakP
+                           // (a wave-wide ballot, held in scalar registers)
+    for (int pass = PRECISE && !have_delta ? 0 : 1; pass < 2; ++pass) {
+        dacc = 0.0f;
         copy_kv(jstart & 1, jstart);
         wait_copies();
         __syncthreads();
@@ -265,10 +279,23 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
                             s[r] = (off > lim || off < lo) ? 0.0f : s[r];
                         }
                     }
+                    if (precise) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        if (precise) dacc += s[r] * dp[r];  // used by pass 0 only
-                        s[r] = s[r] * (dp[r] - delta);
+                        for (int r = 0; r < 16; ++r) {
+                            dacc += s[r] * dp[r];  // used after pass 0 only
+                            s[r] = s[r] * (dp[r] - delta);
+                        }
+                    } else {
+                        float tmax = s[0];
+#pragma unroll
+                        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+                        peaked |= __builtin_amdgcn_ballot_w64(tmax > kPeakP) != 0;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float t = s[r] * dp[r];
+                            dacc += t;
+                            s[r] = fmaf(-s[r], delta, t);  // P (dP - delta)
+                        }
                     }
                     if (pass == 0) continue;
                     // dQ^T += K^T dS^T over two 16-key steps; K^T via transpose loads.
@@ -305,8 +332,29 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
         if (pass == 0) delta = halves_sum(dacc);
     }
 
+    const int nQB = (S + 31) / 32;
+    int* const peak = a.peak + ((size_t)b * a.Hq + hq) * nQB + row0 / 32;
+    bool redo = false;
+    if (!PRECISE) {
+        // The ring is idle after the last step's barrier: a workgroup vote on
+        // whether any row needs the exact path.
+        delta = halves_sum(dacc);
+        int* vote = (int*)smem;
+        if (lane == 0) vote[wave] = peaked ? 1 : 0;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kDqThreads / 64; ++w) redo |= vote[w] != 0;
+        redo = __builtin_amdgcn_readfirstlane(redo ? 1 : 0) != 0;  // the same in every lane
+        __syncthreads();  // the exact pass refills the ring
+        if (lane == 0 && row0 < S) *peak = peaked ? 1 : 0;
+        delta_io = delta;
+    } else if (!have_delta && lane == 0 && row0 < S) {
+        *peak = 1;
+    }
+
     if (live) {
         if (h == 0) a.delta[rowbase + qrow] = delta;
+        if (redo) return true;  // dQ is stored by the exact pass
         float* dst = a.dq + (rowbase + qrow) * D;
         const float sc = a.scale;
 #pragma unroll
@@ -321,10 +369,27 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, __bf16* smem, int b, i
                 *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * h) = v;
             }
     }
+    return redo;
 }
 
-// One launch over every query tile; tiles 0 .. a.precise_tiles-1 take the exact
-// path, so its few workgroups run in the tail of the longest-first schedule.
+// A workgroup's rows: the plain pass, then the exact one where the plain pass found
+// a row above kPeakP (or on every workgroup, when the host asks for it). The
+// exact workgroups run inside the same launch, in the tail of the longest-first
+// schedule.
+template <int D, int DV, bool CAUSAL>
+__device__ __forceinline__ void dq_rows(const BwdArgs& a, __bf16* smem, int b, int hq, int q0, int q_last,
+                                        int row0) {
+    float delta = 0.0f;
+    bool exact = a.precise_all != 0, have_delta = false;
+    if (!exact) {
+        exact = dq_body<D, DV, CAUSAL, false>(a, smem, b, hq, q0, q_last, row0, false, delta);
+        have_delta = true;
+    }
+    if (exact)  // one inlined copy of the exact body serves both cases
+        dq_body<D, DV, CAUSAL, true>(a, smem, b, hq, q0, q_last, row0, have_delta, delta);
+}
+
+// One launch over every query tile.
 template <int D, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
@@ -333,10 +398,7 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_kernel(BwdArgs a) {
     decode_q_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q0 = qt * kDqBQ;
-    if (qt < a.precise_tiles)
-        dq_body<D, DV, CAUSAL, true>(a, smem, b, hq, q0, q0 + kDqBQ - 1, q0 + 32 * wave);
-    else
-        dq_body<D, DV, CAUSAL, false>(a, smem, b, hq, q0, q0 + kDqBQ - 1, q0 + 32 * wave);
+    dq_rows<D, DV, CAUSAL>(a, smem, b, hq, q0, q0 + kDqBQ - 1, q0 + 32 * wave);
 }
 
 // Heads of one kv head that a sliding-window dQ workgroup takes together.
@@ -344,8 +406,8 @@ __host__ __device__ inline int dq_win_heads(int G) { return (G % 4 == 0) ? 4 : (
 
 // Sliding window (as fwd_win_kernel does for the forward): the 4 waves take HW
 // query heads of one kv head and 4/HW blocks of 32 rows, so every wave uses nearly
-// all of the workgroup's key tiles. Workgroups with rows below 128 take the exact
-// path, as do all of them when the window is under 128 keys (precise_all).
+// all of the workgroup's key tiles. Every workgroup takes the exact path when the
+// window is under 128 keys (precise_all), else as the rows' probabilities say.
 template <int D, int DV>
 __global__ void __launch_bounds__(kDqThreads, 2) dq_win_kernel(BwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
@@ -369,10 +431,7 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_win_kernel(BwdArgs a) {
     const int hq = hkv * a.G + blk * HW + wave % HW;
     const int q0 = qt * BQ;
     const int row0 = q0 + 32 * (wave / HW);
-    if (a.precise_all || q0 < kPreciseRows)
-        dq_body<D, DV, true, true>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
-    else
-        dq_body<D, DV, true, false>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
+    dq_rows<D, DV, true>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
 }
 
 // ---------------------------------------------------------------------------
@@ -420,11 +479,26 @@ __device__ __forceinline__ void dkv_item(const BwdArgs& a, int& b, int& hkv, int
     hkv = cgrp % a.Hkv;
 }
 
-// MAYBE_PRECISE: whether any iteration of this workgroup can take the exact path.
-// Without it the per-iteration test is compiled out and the dV/dK product loop is
-// straight-line code.
-template <int D, int DV, bool CAUSAL, bool MAYBE_PRECISE>
-__device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_raw, int b, int hkv, int kt) {
+// The 32-row query tiles that see some key of key tile kt: all of them, from the
+// tile holding key kt*64 on when causal, up to the last row that sees the tile's
+// last key through a window.
+template <bool CAUSAL>
+__device__ __forceinline__ void dkv_range(const BwdArgs& a, int kt, int& qi_first, int& qi_last) {
+    const int nQB = (a.S + kKvBQ - 1) / kKvBQ;
+    const int kv0 = kt * kKvBK;
+    const int W = CAUSAL ? a.window : 0;
+    qi_first = CAUSAL ? kv0 / kKvBQ : 0;
+    qi_last = W > 0 ? min(nQB - 1, (kv0 + kKvBK - 1 + W - 1) / kKvBQ) : nQB - 1;
+}
+
+// Query tiles qi_first .. qi_x - 1 (of every head of the group) run in a first loop
+// whose iterations take the exact path where the dQ stage flagged their tile (or
+// everywhere, when the host asks for it); tiles qi_x .. qi_last run in a second,
+// plain loop, where the per-iteration test is compiled out and the dV/dK product
+// loop is straight-line code. The accumulators carry from one loop into the other.
+template <int D, int DV, bool CAUSAL>
+__device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_raw, int b, int hkv, int kt,
+                                         int qi_x) {
     using T = KvTile<D, DV>;
     using QC = typename T::QCopy;
     using DC = typename T::DCopy;
@@ -448,7 +522,6 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
     const int key = kw0 + l32;      // this lane's key (column of S, dP)
     const size_t kvrow = ((size_t)b * a.Hkv + hkv) * (size_t)S;
     const float c = a.scale_log2;
-    const bool precise_problem = CAUSAL || S <= kPreciseRows;
 
     // K rows of this lane's key as B operands (zero past the end).
     bf16x8 kf[DK];
@@ -481,108 +554,11 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
         copy16_to_lds(a.v + (kvrow + kr) * DV + col, Vs + (wave * VC::N + n) * 512);
     }
 
-    // Iterations: (g, query tile qi) for the query tiles that see some key of the
-    // tile; split p takes iterations p, p + kKvSplits, ...
+    // Iterations of a loop over query tiles q_lo .. q_lo + nq - 1: (g, query tile qi)
+    // for every head g of the group; split p takes iterations p, p + kKvSplits, ...
     const int W = CAUSAL ? a.window : 0;
-    const int qi_first = CAUSAL ? kv0 / kKvBQ : 0;
-    const int qi_last = W > 0 ? min(nQB - 1, (kv0 + kKvBK - 1 + W - 1) / kKvBQ) : nQB - 1;
-    const int per_g = qi_last - qi_first + 1;
-    const int total = G * per_g;
-    const int steps = (total + kKvSplits - 1) / kKvSplits;
-
-    // Q / dO copies of a pair: copy n of wave w2 fills tile rows (w2*N + n) *
-    // ROWS_PER_COPY + lane / CH, kept as this lane's byte offset within a tile of
-    // whole rows. Rows past S repeat row S-1; their lse is +inf, so their
-    // probabilities, and every term they touch, are exactly 0.
-    uint32_t qcoff[QC::N], dcoff[DC::N];
-#pragma unroll
-    for (int n = 0; n < QC::N; ++n) {
-        const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
-        qcoff[n] = (uint32_t)(row * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8) * 2u;
-    }
-#pragma unroll
-    for (int n = 0; n < DC::N; ++n) {  // the same as qcoff when D == DV
-        const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
-        dcoff[n] = D == DV ? 0u : (uint32_t)(row * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8) * 2u;
-    }
-    float lst = 0.f, dlst = 0.f;
-    auto fetch = [&](int step) {  // async copies of Q/dO + lse/delta into registers
-        const int it = kKvSplits * step + split;
-        if (it >= total) return;
-        const int st = step & 1;
-        const int g = it / per_g, qi = qi_first + it % per_g;
-        const size_t rb = ((size_t)b * a.Hq + hkv * G + g) * (size_t)S;
-        const int qr0 = qi * kKvBQ;
-        // A whole tile inside S: its first row's address (scalar) plus lane offsets.
-        // The body with the exact path keeps per-lane addresses: it has no
-        // registers to spare for the scalar form's.
-        if (!MAYBE_PRECISE && qr0 + kKvBQ <= S) {
-            const uint16_t* qb = a.q + (rb + qr0) * D;
-            const uint16_t* db = a.dout + (rb + qr0) * DV;
-#pragma unroll
-            for (int n = 0; n < QC::N; ++n)
-                copy16_to_lds_s(qb, qcoff[n], stage_q(st) + (w2 * QC::N + n) * 512);
-#pragma unroll
-            for (int n = 0; n < DC::N; ++n)
-                copy16_to_lds_s(db, D == DV ? qcoff[n] : dcoff[n], stage_do(st) + (w2 * DC::N + n) * 512);
-        } else if (D == DV) {  // one address for both tensors
-#pragma unroll
-            for (int n = 0; n < QC::N; ++n) {
-                const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
-                const size_t off = (rb + min(qr0 + row, S - 1)) * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8;
-                copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
-                copy16_to_lds(a.dout + off, stage_do(st) + (w2 * QC::N + n) * 512);
-            }
-        } else {
-#pragma unroll
-            for (int n = 0; n < QC::N; ++n) {
-                const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
-                const size_t off = (rb + min(qr0 + row, S - 1)) * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8;
-                copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
-            }
-#pragma unroll
-            for (int n = 0; n < DC::N; ++n) {
-                const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
-                const size_t off = (rb + min(qr0 + row, S - 1)) * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8;
-                copy16_to_lds(a.dout + off, stage_do(st) + (w2 * DC::N + n) * 512);
-            }
-        }
-        if (ptid < kKvBQ) {
-            // raw values only: any use of a loaded value here would make the wave
-            // wait for its vector-memory counter, which also counts the tile
-            // copies just issued, and so for the whole prefetch
-            const int qr = qr0 + ptid;
-            lst = qr < S ? a.lse[rb + qr] : INFINITY;
-            dlst = qr < S ? a.delta[rb + qr] : 0.0f;
-        }
-    };
-    auto publish = [&](int step) {  // row statistics into the stage the copies fill
-        const int it = kKvSplits * step + split;
-        if (it >= total) return;
-        if (ptid < kKvBQ) {
-            stage_lse(step & 1)[ptid] = lst * kLog2e;
-            stage_dl(step & 1)[ptid] = dlst;
-        }
-    };
-
-    // Per-lane LDS offsets: A-operand rows (Q; dO and V) per k-step; transpose
-    // quads (Q^T; dO^T) per 32-column block and row half.
-    int roff[DK], rvoff[DKV], toff[2][DBK], tvoff[2][DBV];
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
-#pragma unroll
-    for (int dk = 0; dk < DKV; ++dk) rvoff[dk] = swz<DV>(l32, dk * 16 + 8 * h);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int db = 0; db < DBK; ++db)
-            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
-                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-#pragma unroll
-        for (int db = 0; db < DBV; ++db)
-            tvoff[hf][db] = swz<DV>(4 * h + ((lane & 15) >> 2) + 8 * hf,
-                                    db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-    }
+    int qi_first, qi_last;
+    dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
 
     f32x16 dk[DBK], dv[DBV];
 #pragma unroll
@@ -590,94 +566,206 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
 #pragma unroll
     for (int db = 0; db < DBV; ++db) dv[db] = zero16();
 
-    fetch(0);
-    publish(0);
-    wait_copies();
-    __syncthreads();
-    for (int step = 0; step < steps; ++step) {
-        if (step + 1 < steps) fetch(step + 1);
-        const int it = kKvSplits * step + split;
-        if (it < total) {
+    auto run = [&](int q_lo, int nq, auto exact_tag) {
+        constexpr bool MAYBE_PRECISE = decltype(exact_tag)::value;
+        const int total = G * nq;
+        const int steps = (total + kKvSplits - 1) / kKvSplits;
+        if (steps == 0) return;  // the same in every wave of the workgroup
+        // per-lane offsets are made in each loop: live across both, they would be
+        // spilled in both
+        // Q / dO copies of a pair: copy n of wave w2 fills tile rows (w2*N + n) *
+        // ROWS_PER_COPY + lane / CH, kept as this lane's byte offset within a tile of
+        // whole rows. Rows past S repeat row S-1; their lse is +inf, so their
+        // probabilities, and every term they touch, are exactly 0.
+        uint32_t qcoff[QC::N], dcoff[DC::N];
+    #pragma unroll
+        for (int n = 0; n < QC::N; ++n) {
+            const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+            qcoff[n] = (uint32_t)(row * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8) * 2u;
+        }
+    #pragma unroll
+        for (int n = 0; n < DC::N; ++n) {  // the same as qcoff when D == DV
+            const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
+            dcoff[n] = D == DV ? 0u : (uint32_t)(row * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8) * 2u;
+        }
+        // Per-lane LDS offsets: A-operand rows (Q; dO and V) per k-step; transpose
+        // quads (Q^T; dO^T) per 32-column block and row half.
+        int roff[DK], rvoff[DKV], toff[2][DBK], tvoff[2][DBV];
+    #pragma unroll
+        for (int dk = 0; dk < DK; ++dk) roff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+    #pragma unroll
+        for (int dk = 0; dk < DKV; ++dk) rvoff[dk] = swz<DV>(l32, dk * 16 + 8 * h);
+    #pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+    #pragma unroll
+            for (int db = 0; db < DBK; ++db)
+                toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                      db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    #pragma unroll
+            for (int db = 0; db < DBV; ++db)
+                tvoff[hf][db] = swz<DV>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                        db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+        }
+        float lst = 0.f, dlst = 0.f;
+        int peak_next = 0;  // exact body: the dQ stage's flag of the iteration being fetched
+        auto fetch = [&](int step) {  // async copies of Q/dO + lse/delta into registers
+            const int it = kKvSplits * step + split;
+            if (it >= total) return;
             const int st = step & 1;
-            const __bf16* Qs = stage_q(st);
-            const __bf16* Ds = stage_do(st);
-            const float* Ls = stage_lse(st);
-            const float* Dl = stage_dl(st);
-            const int qs0 = (qi_first + it % per_g) * kKvBQ;
-            const bool precise = MAYBE_PRECISE && (a.precise_all || (precise_problem && qs0 < kPreciseRows));
-            // skip when every query precedes every key of the wave, or (window)
-            // every query lies past the band of the wave's last key
-            const bool skip = (CAUSAL && qs0 + 31 < kw0) || qs0 >= S || (W > 0 && qs0 > kw0 + 31 + W - 1);
-            if (!skip) {
-                const bool need_mask = (CAUSAL && qs0 < kw0 + 31) || (W > 0 && qs0 + 31 > kw0 + W - 1);
-                f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-                for (int dd = 0; dd < DKM; ++dd) {
-                    bf16x8 qa, da, vb;
-                    if (dd < DK) qa = lds_read8(Qs + roff[dd]);
-                    if (dd < DKV) {
-                        da = lds_read8(Ds + rvoff[dd]);
-                        vb = lds_read8(Vs + rvoff[dd] + w2 * 32 * DV);
-                    }
-                    if (dd < DK) s = mfma32(qa, kf[dd], s);
-                    if (dd < DKV) dp = mfma32(da, vb, dp);
+            const int g = it / nq, qi = q_lo + it % nq;
+            const size_t hrow = (size_t)b * a.Hq + hkv * G + g;  // the query head's index
+            const size_t rb = hrow * (size_t)S;
+            const int qr0 = qi * kKvBQ;
+            // A whole tile inside S: its first row's address (scalar) plus lane offsets.
+            // The body with the exact path keeps per-lane addresses: it has no
+            // registers to spare for the scalar form's.
+            if (!MAYBE_PRECISE && qr0 + kKvBQ <= S) {
+                const uint16_t* qb = a.q + (rb + qr0) * D;
+                const uint16_t* db = a.dout + (rb + qr0) * DV;
+    #pragma unroll
+                for (int n = 0; n < QC::N; ++n)
+                    copy16_to_lds_s(qb, qcoff[n], stage_q(st) + (w2 * QC::N + n) * 512);
+    #pragma unroll
+                for (int n = 0; n < DC::N; ++n)
+                    copy16_to_lds_s(db, D == DV ? qcoff[n] : dcoff[n], stage_do(st) + (w2 * DC::N + n) * 512);
+            } else if (D == DV) {  // one address for both tensors
+    #pragma unroll
+                for (int n = 0; n < QC::N; ++n) {
+                    const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+                    const size_t off = (rb + min(qr0 + row, S - 1)) * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8;
+                    copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
+                    copy16_to_lds(a.dout + off, stage_do(st) + (w2 * QC::N + n) * 512);
                 }
-                // rows of s/dp are queries 8(r/4) + 4h + r%4; the column is this lane's key.
-                // dV^T += dO^T P and dK^T += Q^T dS over two 16-query steps.
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    float pv[8], dsv[8], dl[8];
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const int rg = 2 * t2 + half;
-                        const f32x4 l4 = *(const f32x4*)(Ls + 8 * rg + 4 * h);
-                        const f32x4 d4 = *(const f32x4*)(Dl + 8 * rg + 4 * h);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            pv[4 * half + e] = fast_exp2(fmaf(s[4 * rg + e], c, -l4[e]));
-                            dl[4 * half + e] = d4[e];
+            } else {
+    #pragma unroll
+                for (int n = 0; n < QC::N; ++n) {
+                    const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+                    const size_t off = (rb + min(qr0 + row, S - 1)) * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8;
+                    copy16_to_lds(a.q + off, stage_q(st) + (w2 * QC::N + n) * 512);
+                }
+    #pragma unroll
+                for (int n = 0; n < DC::N; ++n) {
+                    const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
+                    const size_t off = (rb + min(qr0 + row, S - 1)) * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8;
+                    copy16_to_lds(a.dout + off, stage_do(st) + (w2 * DC::N + n) * 512);
+                }
+            }
+            if (ptid < kKvBQ) {
+                // raw values only: any use of a loaded value here would make the wave
+                // wait for its vector-memory counter, which also counts the tile
+                // copies just issued, and so for the whole prefetch
+                const int qr = qr0 + ptid;
+                lst = qr < S ? a.lse[rb + qr] : INFINITY;
+                dlst = qr < S ? a.delta[rb + qr] : 0.0f;
+            }
+            // The flag's address is the same in every lane: a scalar load through the
+            // constant address space (the dQ stage wrote it before this launch) keeps it
+            // in a scalar register; it is read one step later.
+            if (MAYBE_PRECISE)
+                peak_next = *(const __attribute__((address_space(4))) int*)(uintptr_t)(a.peak + hrow * nQB + qi);
+        };
+        auto publish = [&](int step) {  // row statistics into the stage the copies fill
+            const int it = kKvSplits * step + split;
+            if (it >= total) return;
+            if (ptid < kKvBQ) {
+                stage_lse(step & 1)[ptid] = lst * kLog2e;
+                stage_dl(step & 1)[ptid] = dlst;
+            }
+        };
+
+        fetch(0);
+        publish(0);
+        wait_copies();
+        __syncthreads();
+        for (int step = 0; step < steps; ++step) {
+            // this iteration's flag, loaded one step ago (complete since the last wait)
+            const bool peak_cur = MAYBE_PRECISE && peak_next != 0;
+            if (step + 1 < steps) fetch(step + 1);
+            const int it = kKvSplits * step + split;
+            if (it < total) {
+                const int st = step & 1;
+                const __bf16* Qs = stage_q(st);
+                const __bf16* Ds = stage_do(st);
+                const float* Ls = stage_lse(st);
+                const float* Dl = stage_dl(st);
+                const int qs0 = (q_lo + it % nq) * kKvBQ;
+                const bool precise = MAYBE_PRECISE && (a.precise_all || peak_cur);
+                // skip when every query precedes every key of the wave, or (window)
+                // every query lies past the band of the wave's last key
+                const bool skip = (CAUSAL && qs0 + 31 < kw0) || qs0 >= S || (W > 0 && qs0 > kw0 + 31 + W - 1);
+                if (!skip) {
+                    const bool need_mask = (CAUSAL && qs0 < kw0 + 31) || (W > 0 && qs0 + 31 > kw0 + W - 1);
+                    f32x16 s = zero16(), dp = zero16();
+    #pragma unroll
+                    for (int dd = 0; dd < DKM; ++dd) {
+                        bf16x8 qa, da, vb;
+                        if (dd < DK) qa = lds_read8(Qs + roff[dd]);
+                        if (dd < DKV) {
+                            da = lds_read8(Ds + rvoff[dd]);
+                            vb = lds_read8(Vs + rvoff[dd] + w2 * 32 * DV);
                         }
+                        if (dd < DK) s = mfma32(qa, kf[dd], s);
+                        if (dd < DKV) dp = mfma32(da, vb, dp);
                     }
-                    if (need_mask) {  // one uniform branch, taken on edge tiles only
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const int qrow = qs0 + 8 * (2 * t2 + (i >> 2)) + 4 * h + (i & 3);
-                            pv[i] = (key > qrow || (W > 0 && qrow >= key + W)) ? 0.0f : pv[i];
+                    // rows of s/dp are queries 8(r/4) + 4h + r%4; the column is this lane's key.
+                    // dV^T += dO^T P and dK^T += Q^T dS over two 16-query steps.
+    #pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        float pv[8], dsv[8], dl[8];
+    #pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int rg = 2 * t2 + half;
+                            const f32x4 l4 = *(const f32x4*)(Ls + 8 * rg + 4 * h);
+                            const f32x4 d4 = *(const f32x4*)(Dl + 8 * rg + 4 * h);
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                pv[4 * half + e] = fast_exp2(fmaf(s[4 * rg + e], c, -l4[e]));
+                                dl[4 * half + e] = d4[e];
+                            }
                         }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) dsv[i] = pv[i] * (dp[8 * t2 + i] - dl[i]);
-                    const bf16x8 ph = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-                    const bf16x8 sh = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-                    bf16x8 pl, sl;
-                    if (precise) {
-                        pl = pack8(bf_lo(pv[0]), bf_lo(pv[1]), bf_lo(pv[2]), bf_lo(pv[3]), bf_lo(pv[4]),
-                                   bf_lo(pv[5]), bf_lo(pv[6]), bf_lo(pv[7]));
-                        sl = pack8(bf_lo(dsv[0]), bf_lo(dsv[1]), bf_lo(dsv[2]), bf_lo(dsv[3]), bf_lo(dsv[4]),
-                                   bf_lo(dsv[5]), bf_lo(dsv[6]), bf_lo(dsv[7]));
-                    }
-                    const int rbk = 16 * t2 * D, rbv = 16 * t2 * DV;
-#pragma unroll
-                    for (int db = 0; db < DBM; ++db) {
-                        bf16x8 dot, qt;
-                        if (db < DBV)
-                            dot = concat(lds_read_tr(Ds + tvoff[0][db] + rbv), lds_read_tr(Ds + tvoff[1][db] + rbv));
-                        if (db < DBK)
-                            qt = concat(lds_read_tr(Qs + toff[0][db] + rbk), lds_read_tr(Qs + toff[1][db] + rbk));
-                        if (db < DBV) dv[db] = mfma32(dot, ph, dv[db]);
-                        if (db < DBK) dk[db] = mfma32(qt, sh, dk[db]);
+                        if (need_mask) {  // one uniform branch, taken on edge tiles only
+    #pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                const int qrow = qs0 + 8 * (2 * t2 + (i >> 2)) + 4 * h + (i & 3);
+                                pv[i] = (key > qrow || (W > 0 && qrow >= key + W)) ? 0.0f : pv[i];
+                            }
+                        }
+    #pragma unroll
+                        for (int i = 0; i < 8; ++i) dsv[i] = pv[i] * (dp[8 * t2 + i] - dl[i]);
+                        const bf16x8 ph = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+                        const bf16x8 sh = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+                        bf16x8 pl, sl;
                         if (precise) {
-                            if (db < DBV) dv[db] = mfma32(dot, pl, dv[db]);
-                            if (db < DBK) dk[db] = mfma32(qt, sl, dk[db]);
+                            pl = pack8(bf_lo(pv[0]), bf_lo(pv[1]), bf_lo(pv[2]), bf_lo(pv[3]), bf_lo(pv[4]),
+                                       bf_lo(pv[5]), bf_lo(pv[6]), bf_lo(pv[7]));
+                            sl = pack8(bf_lo(dsv[0]), bf_lo(dsv[1]), bf_lo(dsv[2]), bf_lo(dsv[3]), bf_lo(dsv[4]),
+                                       bf_lo(dsv[5]), bf_lo(dsv[6]), bf_lo(dsv[7]));
+                        }
+                        const int rbk = 16 * t2 * D, rbv = 16 * t2 * DV;
+    #pragma unroll
+                        for (int db = 0; db < DBM; ++db) {
+                            bf16x8 dot, qt;
+                            if (db < DBV)
+                                dot = concat(lds_read_tr(Ds + tvoff[0][db] + rbv), lds_read_tr(Ds + tvoff[1][db] + rbv));
+                            if (db < DBK)
+                                qt = concat(lds_read_tr(Qs + toff[0][db] + rbk), lds_read_tr(Qs + toff[1][db] + rbk));
+                            if (db < DBV) dv[db] = mfma32(dot, ph, dv[db]);
+                            if (db < DBK) dk[db] = mfma32(qt, sh, dk[db]);
+                            if (precise) {
+                                if (db < DBV) dv[db] = mfma32(dot, pl, dv[db]);
+                                if (db < DBK) dk[db] = mfma32(qt, sl, dk[db]);
+                            }
                         }
                     }
                 }
             }
+            if (step + 1 < steps) publish(step + 1);
+            wait_copies();
+            __syncthreads();
         }
-        if (step + 1 < steps) publish(step + 1);
-        wait_copies();
-        __syncthreads();
-    }
+    };
+    run(qi_first, qi_x - qi_first, std::true_type{});
+    run(qi_x, qi_last + 1 - qi_x, std::false_type{});
 
     // Sum the four splits' partials (same keys, disjoint iterations) in a fixed
     // order: splits 2,3 hand over to splits 0,1; then split 1 hands dK to split 0
@@ -743,18 +831,44 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
     }
 }
 
+// One past the last query tile, among those key tile kt meets, that the dQ stage
+// flagged in any head of the group (qi_first when none is). Every wave scans the
+// flags on its own with scalar loads (wave-uniform addresses, read through the
+// constant address space: the dQ stage wrote them before this launch), so the scan
+// needs no vector registers, no LDS and no barrier.
+template <bool CAUSAL>
+__device__ __forceinline__ int dkv_exact_end(const BwdArgs& a, int b, int hkv, int kt) {
+    typedef const __attribute__((address_space(4))) int cint;
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    typedef const __attribute__((address_space(4))) i32x8 cint8;
+    int qi_first, qi_last;
+    dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
+    const int per_g = qi_last - qi_first + 1, nQB = (a.S + kKvBQ - 1) / kKvBQ;
+    int end = 0;  // one past the last flagged tile, relative to qi_first
+    for (int g = 0; g < a.G; ++g) {
+        const int* row = a.peak + ((size_t)b * a.Hq + (size_t)hkv * a.G + g) * nQB + qi_first;
+        int i = 0;
+        for (; i + 8 <= per_g; i += 8) {
+            const i32x8 f = *(cint8*)(uintptr_t)(row + i);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) end = f[e] ? i + e + 1 : end;
+        }
+        for (; i < per_g; ++i) end = *(cint*)(uintptr_t)(row + i) ? i + 1 : end;
+    }
+    return qi_first + end;
+}
+
 template <int D, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     int b, hkv, kt;
     dkv_item(a, b, hkv, kt);
-    // Exact-path iterations have query rows below kPreciseRows; a causal (or
-    // windowed) key tile only sees queries at or past its first key.
-    const bool precise_problem = CAUSAL || a.S <= kPreciseRows;
-    if (a.precise_all || (precise_problem && kt * kKvBK < kPreciseRows))
-        dkv_body<D, DV, CAUSAL, true>(a, lds_raw, b, hkv, kt);
-    else
-        dkv_body<D, DV, CAUSAL, false>(a, lds_raw, b, hkv, kt);
+    // The exact loop covers the query tiles up to the last one the dQ stage flagged
+    // (a row with a probability above kPeakP), or every tile on request.
+    int qi_first, qi_last;
+    dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
+    const int qi_x = a.precise_all ? qi_last + 1 : dkv_exact_end<CAUSAL>(a, b, hkv, kt);
+    dkv_body<D, DV, CAUSAL>(a, lds_raw, b, hkv, kt, qi_x);
 }
 
 template <int D, int DV, bool CAUSAL>
@@ -764,7 +878,6 @@ hipError_t launch_bwd_t(const BwdArgs& args, int stages, hipStream_t stream) {
         // Query tiles whose rows need the exact path: all of them when asked for,
         // else tile 0 of a causal problem or the single tile of S <= 128.
         const int nQ = (a.S + kDqBQ - 1) / kDqBQ;
-        a.precise_tiles = a.precise_all ? nQ : (CAUSAL || a.S <= kPreciseRows) ? 1 : 0;
         constexpr int lds = DqTile<D, DV>::LDS_BYTES;
         if (CAUSAL && a.window > 0) {
             const int HW = dq_win_heads(a.G), BQ = 32 * (4 / HW);

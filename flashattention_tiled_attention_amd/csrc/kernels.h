@@ -30,15 +30,22 @@ struct BwdArgs {
     float* dq;
     float* dk;
     float* dv;
-    float* delta;        // workspace: [B][Hq][S]
+    float* delta;        // workspace: [B][Hq][S], the exact delta_i = sum_j P_ij dP_ij
+    int* peak;           // workspace: [B][Hq][ceil(S/32)], 1 where a row of the 32-row block has
+                         // a probability above kPeakP (written by the dQ stage)
     int B, Hq, Hkv, S, G;
     int causal;
     int window;          // as in FwdArgs
     float scale;         // signed scale
     float scale_log2;    // scale * log2(e) (signed)
-    int precise_all;     // exact delta and split P/dS operands on every tile
-    int precise_tiles;   // dQ query tiles 0 .. precise_tiles-1 take that exact path (set by launch_bwd)
+    int precise_all;     // split P/dS operands on every tile, whatever the data
 };
+
+// A row whose largest probability exceeds this takes the backward's exact path: its
+// P and dS operands are split into a bf16 high part and a bf16 remainder. Below it,
+// bf16 rounding of P and dS (at most 2^-9 of each) keeps dQ, dK and dV within a
+// quarter of the 1e-2 bar on the workloads measured.
+constexpr float kPeakP = 0.125f;
 
 // Sparse attention over per-token index lists (attn_sparse_* entry points).
 struct SparseArgs {

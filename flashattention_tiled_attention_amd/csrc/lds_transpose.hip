@@ -21,8 +21,8 @@
 //      of 8 lanes in three XOR butterfly stages of DPP lane moves.
 // Methods 1-3 deliver the same transposed operand, element e of lane (c, h)
 // being V[8 (e / 4) + 4h + e % 4][c], the row order the transpose load produces
-// and the attention kernels use (the check output holds each lane's first
-// operand). Every method reads 16 bytes of operand per lane per load. Each
+// and the attention kernels use (the check output holds every lane's operand at
+// each of the eight positions a loop iteration loads). Every method reads 16 bytes of operand per lane per load. Each
 // method reads the 64 x 64 bf16 tile in a layout free of bank conflicts for its
 // access shape (checked with the LDS bank-conflict counter): the kernels'
 // XOR-swizzled chunk order for the 16-byte row reads and the transpose load, a
@@ -162,9 +162,12 @@ __global__ void __launch_bounds__(kThreads) lds_bench_kernel(int iters, uint32_t
     const int lane = threadIdx.x & 63;
     uint32_t acc[4] = {0u, 0u, 0u, 0u};  // four independent XOR chains
     if (blockIdx.x == 0 && threadIdx.x < 64) {
-        const u32x4 v = load_operand<METHOD>(tile, 0, lane);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) operand_out[lane * 4 + k] = v[k];
+        for (int p = 0; p < kUnroll; ++p) {
+            const u32x4 v = load_operand<METHOD>(tile, p, lane);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) operand_out[(p * 64 + lane) * 4 + k] = v[k];
+        }
     }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll

@@ -21,8 +21,11 @@
  *    both S). causal == 0: every row sees all S keys.
  *  - scale: any finite float; the usual value is 1/sqrt(D).
  *  - D must be 64 or 128. S, B, Hq, Hkv >= 1, B*Hq*S*D < 2^40 and S*D < 2^31
- *    (the kernels address rows within one head with 32-bit offsets).
- *  - stream: a hipStream_t passed as void*; NULL means the null stream.
+ *    (the kernels address rows within one head with 32-bit offsets), and every
+ *    launch must fit a grid of fewer than 2^32 work-items (ATTN_ERR_SHAPE).
+ *  - stream: a hipStream_t passed as void*; NULL means the null stream. The
+ *    header uses void* so that C callers and foreign-function bindings need no
+ *    HIP header; the value is cast back to hipStream_t inside the library.
  *    Calls are asynchronous: ATTN_OK means the kernels were enqueued. A device
  *    fault surfaces at the caller's next synchronisation.
  *  - The caller owns every buffer (inputs, outputs, workspace) and keeps it
@@ -46,7 +49,8 @@ enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,          /* a required pointer is NULL */
     ATTN_ERR_SHAPE = 2,         /* B, Hq, Hkv, S, D or Dv < 1, B*Hq*S*max(D, Dv) >= 2^40,
-                                   or S*max(D, Dv) >= 2^31 */
+                                   S*max(D, Dv) >= 2^31, or a launch grid of 2^32
+                                   work-items or more: B*Hq*(2S+512) or B*Hkv*(8S+512) */
     ATTN_ERR_GQA = 3,           /* Hq is not a multiple of Hkv */
     ATTN_ERR_UNSUPPORTED_D = 4, /* D (or Dv) is neither 64 nor 128 */
     ATTN_ERR_ALIGN = 5,         /* a tensor or workspace pointer is not 16-byte aligned */
@@ -55,7 +59,10 @@ enum attn_status {
     ATTN_ERR_HIP = 8,           /* the HIP runtime failed (no device, launch error) */
     ATTN_ERR_DEVICE = 9,        /* the current device is not a gfx950 GPU */
     ATTN_ERR_WINDOW = 10,       /* a sliding window of fewer than 1 key (vdim: < 0, or set without causal) */
-    ATTN_ERR_SPARSE = 11        /* sparse: topk > 4096, Hq/Hkv > 128, N*D or S*topk >= 2^31 */
+    ATTN_ERR_SPARSE = 11        /* sparse: topk > 4096, Hq/Hkv > 128, N*D or S*topk >= 2^31,
+                                   or a launch grid of 2^32 work-items or more:
+                                   B*S*Hkv*ceil(Hq/Hkv/64)*128, B*S*Hkv*ceil(topk/128)*256
+                                   or B*Hkv*N*256 */
 };
 
 /*
@@ -72,11 +79,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int S, int D, int causal, float scale, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes (the per-row
- * delta_i = sum_d dO_id * O_id, fp32, plus alignment). Returns 0 when the
- * sizes are invalid (attn_bwd would reject them).
+ * Bytes of device workspace attn_bwd needs for these sizes: the per-row
+ * delta_i = sum_j P_ij dP_ij (fp32, [B][Hq][S]) and one int32 flag per block of
+ * 32 query rows ([B][Hq][ceil(S/32)]: 1 where a row of the block has a
+ * probability above 1/8, whose gradient terms then take the exact path), each
+ * part 256-byte aligned. Returns 0 when the sizes are invalid (attn_bwd would
+ * reject them).
  */
-size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int causal);
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 
 /*
  * Backward pass: exact gradient of Eq. (1) (section 2.1; Table 3 lists its
@@ -103,12 +113,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * The two stages attn_bwd runs, for callers that schedule them separately
  * (attn_bwd is exactly attn_bwd_dq followed by attn_bwd_dkdv on one stream).
  * Arguments and errors are those of attn_bwd.
- *   attn_bwd_dq    writes delta_i = sum_d dO_id O_id (exact sum_j P_ij dP_ij for
- *                  rows whose visible keys all lie among the first 128) into the
- *                  workspace, and dq = scale * dS K (section 2.1, Table 3, query
- *                  gradient row). dk and dv are not touched.
- *   attn_bwd_dkdv  reads delta from the workspace (it must hold attn_bwd_dq's
- *                  result for the same inputs) and writes dk = scale * dS^T Q
+ *   attn_bwd_dq    writes delta_i = sum_j P_ij dP_ij and the per-block flags into
+ *                  the workspace, and dq = scale * dS K (section 2.1, Table 3,
+ *                  query gradient row). dk and dv are not touched.
+ *   attn_bwd_dkdv  reads delta and the flags from the workspace (it must hold
+ *                  attn_bwd_dq's result for the same inputs) and writes
+ *                  dk = scale * dS^T Q
  *                  (Table 3, key gradient row) and dv = P^T dO, each summed over
  *                  the query heads of its group. dq is not touched.
  */
@@ -132,7 +142,7 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, co
  *   window  >= 1, else ATTN_ERR_WINDOW (checked before anything else)
  * Every other argument, the layouts and the errors are those of attn_fwd and
  * attn_bwd; attn_bwd_window takes a workspace of
- * attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, 1) bytes, and needs o and lse
+ * attn_bwd_workspace_bytes(B, Hq, Hkv, S, D) bytes, and needs o and lse
  * from attn_fwd_window with the same window.
  */
 int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -152,7 +162,7 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
  * window; window >= 1 needs causal != 0 (else, or for window < 0,
  * ATTN_ERR_WINDOW). Scores are q . k over D columns, so the usual scale is
  * 1/sqrt(D). attn_bwd_vdim's workspace is attn_bwd_workspace_bytes(B, Hq, Hkv,
- * S, D, causal) bytes (delta has one value per query row whatever Dv is), and it
+ * S, D) bytes (delta has one value per query row whatever Dv is), and it
  * needs o and lse from attn_fwd_vdim with the same arguments. With Dv == D these
  * are attn_fwd / attn_bwd (window = 0) and attn_fwd_window / attn_bwd_window.
  * Every other rule, layout and error is that of attn_fwd and attn_bwd, with
@@ -187,8 +197,9 @@ int attn_bwd_vdim(const void* q, const void* k, const void* v, const void* o, co
  *                  restriction; nothing else masks.
  *   lse            [B][Hq][S] fp32 (natural log); -inf for a token whose list is
  *                  empty, whose O row is 0 (and whose dQ row is 0)
- * D is 64 or 128, topk in [1, 4096], Hq/Hkv <= 128, N*D and S*topk < 2^31
- * (ATTN_ERR_SPARSE otherwise). attn_sparse_bwd needs o and lse from
+ * D is 64 or 128, topk in [1, 4096], Hq/Hkv <= 128, N*D and S*topk < 2^31,
+ * and every launch within a grid of fewer than 2^32 work-items (the reduction
+ * takes 256 per key/value row, so B*Hkv*N < 2^24) (ATTN_ERR_SPARSE otherwise). attn_sparse_bwd needs o and lse from
  * attn_sparse_fwd with the same arguments, and a workspace of
  * attn_sparse_bwd_workspace_bytes() bytes: delta, the per-(token, slot)
  * contributions (2 * B*Hkv*S*topk*D fp32) and the inverse map; its contents on

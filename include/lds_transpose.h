@@ -26,8 +26,10 @@ extern "C" {
  *   blocks        workgroups of 256 threads; each wave loads `iters` x 8 operands
  *                 of 16 bytes per lane from a 64 x 64 bf16 tile in LDS
  *   ms_out        host pointer: the fastest launch's duration in milliseconds
- *   operand_out   device pointer, 16-byte aligned, 256 words: lane l's first
- *                 operand in words 4l .. 4l+3 (methods 1-3 give the same values)
+ *   operand_out   device pointer, 16-byte aligned, 2048 words: the operand
+ *                 lane l loads at position p (0..7, the eight 16-row x 32-column
+ *                 blocks one loop iteration reads) in words 4(64p + l) .. +3
+ *                 (methods 1-3 give the same values)
  *   checksum_out  device pointer, blocks * 256 words: per-thread XOR of every
  *                 loaded word (keeps the loads live)
  *   stream        hipStream_t as void*; the call synchronises on it

@@ -55,3 +55,43 @@ def sample_rows(B, H, S, n, seed=0, tile=128):
             rows.add(bh * S + i + 1)
     rows.update(int(x) for x in rng.integers(0, B * H * S, size=n))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def peaked(q, k, v, mode, spike_rows, key_axis_len=None):
+    """Inputs whose softmax rows concentrate on few keys at the usual scale 1/sqrt(D),
+    as bf16 bits (q, k, v in, q, k, v out; dO is left as drawn):
+      ramp   key norms grow fourfold along the key axis, so a row's maximum keeps moving;
+      spike  every query gets +1 in each component and the keys in `spike_rows` are
+             2.5 in every component, so rows that see one of them put nearly all their
+             weight on it;
+      wide   Q and K scaled by 2.5: score variance 39 instead of 1.
+    V is halved so that |O| stays below 4, where the bf16 store of O alone could miss
+    the 1e-2 bar (the bf16 spacing there is 2^-5)."""
+    from flashattention_tiled_attention_amd.inputs import bf16_bits
+    qf, kf = bf16_to_f32(q), bf16_to_f32(k)
+    n = kf.shape[2] if key_axis_len is None else key_axis_len
+    if mode == "ramp":
+        kf = kf.copy()
+        kf[:, :, :n] *= (1.0 + 3.0 * np.arange(n, dtype=np.float32) / n)[None, None, :, None]
+    elif mode == "spike":
+        qf = qf + 1.0
+        kf = kf.copy()
+        for t in spike_rows:
+            kf[:, :, t, :] = 2.5
+    elif mode == "wide":
+        qf, kf = qf * 2.5, kf * 2.5
+    else:
+        raise ValueError(mode)
+    return bf16_bits(qf), bf16_bits(kf), bf16_bits(bf16_to_f32(v) * 0.5)
+
+
+def head_offset_rows(B, H, S, stride):
+    """Flat row indices (b*H + h)*S + i with i = (b*H + h) % stride (mod stride): every
+    stride-th query row of each head, the residue moving from head to head so every
+    lane position of a row tile is covered, plus each head's last row."""
+    rows = []
+    for bh in range(B * H):
+        i = np.arange(bh % stride, S, stride, dtype=np.int64)
+        rows.append(bh * S + i)
+        rows.append(np.array([bh * S + S - 1], np.int64))
+    return np.unique(np.concatenate(rows))

@@ -64,7 +64,7 @@ def fwd(*, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, 
 def bwd(*, ptrs=None, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, scale=0.088, ws=P, wsb=None):
     lib = fa.load_library()
     if wsb is None:
-        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal)
+        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
     p = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P)
     p.update(ptrs or {})
     return lib.attn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"], p["dv"],
@@ -83,6 +83,10 @@ def test_fwd_null(name):
     # one head's rows must be addressable with 32-bit offsets: S * D < 2^31
     (dict(B=1, Hq=1, Hkv=1, S=1 << 24, D=128), fa.ATTN_ERR_SHAPE),
     (dict(B=1, Hq=1, Hkv=1, S=(1 << 25) + 1, D=64), fa.ATTN_ERR_SHAPE),
+    # launch grids: 2*S + 512 forward work-items per query head, 8*S + 512 dK/dV
+    # work-items per kv head, each total below 2^32
+    (dict(B=1, Hq=1 << 10, Hkv=1 << 10, S=1 << 21, D=64), fa.ATTN_ERR_SHAPE),
+    (dict(B=64, Hq=64, Hkv=64, S=1 << 17, D=64), fa.ATTN_ERR_SHAPE),
     (dict(Hq=6, Hkv=4), fa.ATTN_ERR_GQA), (dict(D=96), fa.ATTN_ERR_UNSUPPORTED_D),
     (dict(D=256), fa.ATTN_ERR_UNSUPPORTED_D), (dict(scale=math.nan), fa.ATTN_ERR_SCALE),
     (dict(scale=math.inf), fa.ATTN_ERR_SCALE), (dict(q=MIS), fa.ATTN_ERR_ALIGN),
@@ -104,7 +108,7 @@ def test_bwd_misaligned(name):
 
 def test_bwd_workspace():
     lib = fa.load_library()
-    need = lib.attn_bwd_workspace_bytes(1, 4, 2, 128, 128, 1)
+    need = lib.attn_bwd_workspace_bytes(1, 4, 2, 128, 128)
     assert need >= 4 * 4 * 128
     assert bwd(ws=None) == fa.ATTN_ERR_WORKSPACE
     assert bwd(wsb=need - 1) == fa.ATTN_ERR_WORKSPACE
@@ -112,8 +116,8 @@ def test_bwd_workspace():
     assert bwd(Hq=6, Hkv=4) == fa.ATTN_ERR_GQA
     assert bwd(D=80) == fa.ATTN_ERR_UNSUPPORTED_D
     assert bwd(scale=-math.inf) == fa.ATTN_ERR_SCALE
-    assert lib.attn_bwd_workspace_bytes(0, 4, 2, 128, 128, 1) == 0
-    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 128, 96, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(0, 4, 2, 128, 128) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 128, 96) == 0
 
 
 def fwd_window(*, window=128, q=P, B=1, Hq=4, Hkv=2, S=128, D=128, scale=0.088):
@@ -123,7 +127,7 @@ def fwd_window(*, window=128, q=P, B=1, Hq=4, Hkv=2, S=128, D=128, scale=0.088):
 def bwd_window(*, window=128, dq=P, B=1, Hq=4, Hkv=2, S=128, D=128, scale=0.088, wsb=None):
     lib = fa.load_library()
     if wsb is None:
-        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, 1)
+        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
     return lib.attn_bwd_window(P, P, P, P, P, P, dq, P, P, B, Hq, Hkv, S, D, window, scale, P, wsb, None)
 
 
@@ -152,7 +156,7 @@ def fwd_vdim(*, window=0, causal=1, o=P, B=1, Hq=4, Hkv=2, S=128, D=128, Dv=64, 
 def bwd_vdim(*, window=0, causal=1, dv=P, B=1, Hq=4, Hkv=2, S=128, D=128, Dv=64, scale=0.088, wsb=None):
     lib = fa.load_library()
     if wsb is None:
-        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, causal)
+        wsb = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
     return lib.attn_bwd_vdim(P, P, P, P, P, P, P, P, dv, B, Hq, Hkv, S, D, Dv, causal, window, scale, P, wsb,
                              None)
 
@@ -195,11 +199,31 @@ def sp_bwd(*, dk=P, B=1, Hq=8, Hkv=1, S=256, N=320, D=128, topk=64, scale=0.088,
     (dict(D=96), fa.ATTN_ERR_UNSUPPORTED_D), (dict(Hq=6, Hkv=4), fa.ATTN_ERR_GQA),
     (dict(topk=4097), fa.ATTN_ERR_SPARSE), (dict(Hq=256, Hkv=1), fa.ATTN_ERR_SPARSE),
     (dict(N=1 << 24), fa.ATTN_ERR_SPARSE), (dict(S=1 << 20, topk=4096), fa.ATTN_ERR_SPARSE),
+    # the reduction's grid: 256 work-items per key/value row must stay under 2^32
+    (dict(Hkv=8, Hq=8, N=(1 << 21)), fa.ATTN_ERR_SPARSE), (dict(B=2, Hkv=4, Hq=8, N=(1 << 21)), fa.ATTN_ERR_SPARSE),
     (dict(scale=math.inf), fa.ATTN_ERR_SCALE),
 ])
 def test_sparse_rejects(kw, code):
     assert sp_fwd(**kw) == code
     assert sp_bwd(**kw) == code
+
+
+def test_grid_limits_at_the_boundary():
+    """The largest sizes whose every launch fits a 32-bit grid of work-items pass
+    validation (and then fail at the device step here, with no GPU); one more kv
+    head or key/value row is rejected before anything is launched."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid sizes would launch")
+    ok = (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
+    # dK/dV grid: B*Hkv*(8*S + 512) work-items; S = 2^16 gives 2^19 + 512 per kv head
+    per = 8 * (1 << 16) + 512
+    top = ((1 << 32) - 1) // per
+    assert fwd(B=1, Hq=top, Hkv=top, S=1 << 16, D=64) in ok
+    assert fwd(B=1, Hq=top + 1, Hkv=top + 1, S=1 << 16, D=64) == fa.ATTN_ERR_SHAPE
+    # sparse reduction grid: 256 work-items per key/value row, B*Hkv*N < 2^24
+    assert sp_fwd(Hq=4, Hkv=4, N=(1 << 22) - 1) in ok
+    assert sp_fwd(Hq=4, Hkv=4, N=1 << 22) == fa.ATTN_ERR_SPARSE
 
 
 def test_sparse_validates_pointers_and_workspace():

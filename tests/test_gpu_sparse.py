@@ -210,3 +210,21 @@ def test_row_maximum_moving_after_the_first_tile(mode, D):
             kf[:, :, r, :] = 2.5
     q, k, v = bf16_bits(qf), bf16_bits(kf), bf16_bits(bf16_to_f32(v) * 0.5)
     check(q, k, v, idx, None, 1.0 / math.sqrt(D), "max moving %s D=%d" % (mode, D))
+
+
+@pytest.mark.parametrize("mode", ["ramp", "spike", "wide"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_peaked_rows_backward(mode, D):
+    """The sparse backward on lists whose rows put most of their weight on one or a few
+    slots at the usual scale 1/sqrt(D) (the inputs of the dense test of the same name):
+    growing row norms along the pool, two pool rows every query points at, and inputs of
+    standard deviation 2.5. Lists are the compressed-attention shape (a 128-token window
+    plus up to 256 pool rows): tokens past 515 list more than 256 rows, beyond which the
+    sparse kernels leave the exact path to the data."""
+    from tests.gpu_util import peaked
+    B, Hq, Hkv, S = 1, 16, 1, 1200
+    idx, N = csa_index_lists(B, S, window=128, ratio=4, pool_topk=256, seed=23)
+    assert (idx >= 0).sum(axis=2).max() > 256
+    q, k, v, do = sparse_qkv(B, Hq, Hkv, S, N, D, seed=24 + D, with_dout=True)
+    q, k, v = peaked(q, k, v, mode, spike_rows=(S + 10, S + 140))
+    check(q, k, v, idx, do, 1.0 / math.sqrt(D), "peaked backward %s D=%d" % (mode, D))
