@@ -338,9 +338,16 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_fwd_kernel(SparseArgs a)
 // ---------------------------------------------------------------------------
 // dQ (+ delta)
 // ---------------------------------------------------------------------------
+// The plain body (PRECISE false) makes one pass with delta from the stored O and
+// bf16 dS operands; in the same pass it accumulates the exact delta = sum_s P dP,
+// which it stores for the contribution kernel, and looks for a probability above
+// kPeakP in any of the workgroup's rows. It returns whether it found one: then dQ is
+// not stored and the caller runs the PRECISE body with that delta (have_delta),
+// which makes the pass again with split dS operands. Called without have_delta the
+// PRECISE body first makes a pass that only accumulates the exact delta.
 template <int D, bool PRECISE>
-__device__ __forceinline__ void sparse_dq_body(const SparseArgs& a, unsigned char* lds_raw, const SpItem& it,
-                                               const int* list, int n) {
+__device__ __forceinline__ bool sparse_dq_body(const SparseArgs& a, unsigned char* lds_raw, const SpItem& it,
+                                               const int* list, int n, bool have_delta, float& delta_io) {
     using T = SpTile<D>;
     using C = typename T::Copy;
     constexpr int DK = D / 16;
@@ -380,7 +387,7 @@ __device__ __forceinline__ void sparse_dq_body(const SparseArgs& a, unsigned cha
             df[dk] = qf[dk];
         }
     }
-    float delta = halves_sum(dpart);
+    float delta = PRECISE && have_delta ? delta_io : halves_sum(dpart);
     const float lse2 = (live && n > 0) ? a.lse[row] * kLog2e : INFINITY;
 
     const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
@@ -415,11 +422,13 @@ __device__ __forceinline__ void sparse_dq_body(const SparseArgs& a, unsigned cha
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
 
-    // Pass 0 (exact path only) accumulates delta = sum_s P dP; the last pass forms
-    // dS and accumulates dQ^T += K^T dS^T.
+    // Pass 0 (exact body without a given delta) accumulates delta = sum_s P dP; the
+    // last pass forms dS and accumulates dQ^T += K^T dS^T.
     const int nT = (n + kSpBK - 1) / kSpBK;
-    for (int pass = PRECISE ? 0 : 1; pass < 2; ++pass) {
-        float dacc = 0.0f;
+    float dacc = 0.0f;
+    bool peaked = false;  // plain body: a probability above kPeakP (a wave-wide ballot)
+    for (int pass = PRECISE && !have_delta ? 0 : 1; pass < 2; ++pass) {
+        dacc = 0.0f;
         if (nT > 0) {
             copy_tile(0, 0);
             wait_copies();
@@ -442,10 +451,23 @@ __device__ __forceinline__ void sparse_dq_body(const SparseArgs& a, unsigned cha
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) >= lim) ? 0.0f : s[r];
             }
+            if (PRECISE) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (PRECISE) dacc += s[r] * dp[r];  // used by pass 0 only
-                s[r] = s[r] * (dp[r] - delta);
+                for (int r = 0; r < 16; ++r) {
+                    dacc += s[r] * dp[r];  // used after pass 0 only
+                    s[r] = s[r] * (dp[r] - delta);
+                }
+            } else {
+                float tmax = s[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+                peaked |= __builtin_amdgcn_ballot_w64(tmax > kPeakP) != 0;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float t = s[r] * dp[r];
+                    dacc += t;
+                    s[r] = fmaf(-s[r], delta, t);  // P (dP - delta)
+                }
             }
             if (pass == 1) {
 #pragma unroll
@@ -472,8 +494,23 @@ __device__ __forceinline__ void sparse_dq_body(const SparseArgs& a, unsigned cha
         if (pass == 0) delta = halves_sum(dacc);
     }
 
+    bool redo = false;
+    if (!PRECISE) {
+        // a workgroup vote in the K/V ring, idle once every wave is past its last
+        // tile (the barrier; with no tiles the ring was never used)
+        delta = halves_sum(dacc);
+        int* vote = (int*)lds_raw;
+        __syncthreads();
+        if (lane == 0) vote[wave] = peaked ? 1 : 0;
+        __syncthreads();
+        redo = __builtin_amdgcn_readfirstlane((vote[0] | vote[1]) ? 1 : 0) != 0;
+        __syncthreads();  // the exact pass refills the ring
+        delta_io = delta;
+    }
+
     if (live) {
         if (h == 0) a.delta[row] = delta;
+        if (redo) return true;  // dQ is stored by the exact pass
         float* dst = a.dq + row * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -485,6 +522,7 @@ __device__ __forceinline__ void sparse_dq_body(const SparseArgs& a, unsigned cha
                 *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * h) = v;
             }
     }
+    return redo;
 }
 
 template <int D>
@@ -495,10 +533,16 @@ __global__ void __launch_bounds__(kSpThreads, 2) sparse_dq_kernel(SparseArgs a) 
     int* const red = list + ((a.topk + 3) & ~3);
     const SpItem it = sp_item(a);
     const int n = compact_list(a.idx + ((size_t)it.b * a.S + it.i) * a.topk, a.topk, a.N, list, red);
-    if (a.precise_all || n <= kSpPreciseSlots)
-        sparse_dq_body<D, true>(a, lds_raw, it, list, n);
-    else
-        sparse_dq_body<D, false>(a, lds_raw, it, list, n);
+    // Tokens with at most kSpPreciseSlots keys (or all, on request) take the exact
+    // body from the start; the others when their pass finds a probability above
+    // kPeakP.
+    float delta = 0.0f;
+    bool exact = a.precise_all || n <= kSpPreciseSlots, have_delta = false;
+    if (!exact) {
+        exact = sparse_dq_body<D, false>(a, lds_raw, it, list, n, false, delta);
+        have_delta = true;
+    }
+    if (exact) sparse_dq_body<D, true>(a, lds_raw, it, list, n, have_delta, delta);
 }
 
 // ---------------------------------------------------------------------------
