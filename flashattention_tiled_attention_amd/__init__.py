@@ -32,10 +32,12 @@ ATTN_ERR_HIP = 8
 ATTN_ERR_DEVICE = 9
 ATTN_ERR_WINDOW = 10
 ATTN_ERR_SPARSE = 11
+ATTN_ERR_SCRATCH = 12
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_window",
                     "attn_bwd_window", "attn_fwd_vdim", "attn_bwd_vdim", "attn_bwd_workspace_bytes",
-                    "attn_sparse_fwd", "attn_sparse_bwd", "attn_sparse_bwd_workspace_bytes", "attn_status_str")
+                    "attn_sparse_fwd", "attn_sparse_bwd", "attn_sparse_bwd_workspace_bytes", "attn_status_str",
+                    "attn_bwd_noalloc", "attn_bwd_noalloc_max_workspace_bytes")
 
 
 class AttnError(RuntimeError):
@@ -79,6 +81,10 @@ def load_library(path=None):
     lib.attn_sparse_bwd_workspace_bytes.restype = Z
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
+    lib.attn_bwd_noalloc.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, F, V]
+    lib.attn_bwd_noalloc.restype = I
+    lib.attn_bwd_noalloc_max_workspace_bytes.argtypes = []
+    lib.attn_bwd_noalloc_max_workspace_bytes.restype = Z
     lib.attn_status_str.argtypes = [I]
     lib.attn_status_str.restype = ctypes.c_char_p
     if path is None:
@@ -185,6 +191,28 @@ def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, flags, scale, workspace, 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):
     """C attn_bwd on torch tensors; dq/dk/dv are fp32; workspace is a uint8 GPU tensor."""
     _bwd_call("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, (bool(causal),), scale, workspace, stream)
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, stream=None):
+    """C attn_bwd_noalloc: attn_bwd with the library's static per-GPU scratch as its
+    workspace (nothing is allocated); calls that overlap on one GPU race."""
+    import torch
+    B, Hq, Hkv, S, D, Dv = _dims(q, k)
+    for t, n, dt, sh in ((q, "q", torch.bfloat16, (B, Hq, S, D)), (k, "k", torch.bfloat16, (B, Hkv, S, D)),
+                         (v, "v", torch.bfloat16, (B, Hkv, S, D)), (o, "o", torch.bfloat16, (B, Hq, S, D)),
+                         (lse, "lse", torch.float32, (B, Hq, S)), (dout, "dout", torch.bfloat16, (B, Hq, S, D)),
+                         (dq, "dq", torch.float32, (B, Hq, S, D)), (dk, "dk", torch.float32, (B, Hkv, S, D)),
+                         (dv, "dv", torch.float32, (B, Hkv, S, D))):
+        _check(t, n, dt, sh)
+    rc = load_library().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), float(scale),
+                                         _stream(stream))
+    if rc:
+        raise AttnError(rc, "attn_bwd_noalloc")
+
+
+def attn_bwd_noalloc_max_workspace_bytes():
+    return int(load_library().attn_bwd_noalloc_max_workspace_bytes())
 
 
 def attn_bwd_dq(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None):

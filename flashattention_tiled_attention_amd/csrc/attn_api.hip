@@ -24,6 +24,14 @@ constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_status[kMaxDevices];
 
+// Backward scratch of attn_bwd_noalloc: one copy per GPU, held until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory; the
+// device address of each GPU's copy is taken once per device at set-up
+// (g_scratch) and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch[kMaxDevices];
+
 // Once per device: check that it is a gfx950 GPU and raise the kernels'
 // dynamic-LDS limit. Returns an attn_status.
 int setup_current_device() {
@@ -50,6 +58,14 @@ int setup_current_device() {
             g_dev_status[dev] = ATTN_ERR_HIP;
             return;
         }
+        // this device's copy of the no-allocation scratch (the device is current)
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            g_dev_status[dev] = ATTN_ERR_HIP;
+            return;
+        }
+        g_scratch[dev] = ptr;
         g_dev_status[dev] = ATTN_OK;
     });
     return g_dev_status[dev];
@@ -150,6 +166,8 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_WINDOW: return "window must be >= 1 (>= 0 and causal for the vdim entry points)";
         case ATTN_ERR_SPARSE:
             return "sparse sizes out of range: topk <= 4096, Hq/Hkv <= 128, N*D and S*topk < 2^31";
+        case ATTN_ERR_SCRATCH:
+            return "attn_bwd_noalloc: attn_bwd_workspace_bytes() for these sizes exceeds its 8 MiB static scratch";
         default: return "unknown attn status";
     }
 }
@@ -212,21 +230,34 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
     return delta_bytes(B, Hq, S) + peak_bytes(B, Hq, S);
 }
 
+// use_scratch: the workspace is this device's static scratch (attn_bwd_noalloc);
+// workspace and workspace_bytes are then ignored.
 static int bwd_stages(int stages, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv, int B,
                       int Hq, int Hkv, int S, int D, int Dv, int causal, int window, float scale,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
     int rc = check_sizes(B, Hq, Hkv, S, D, Dv);
     if (rc) return rc;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
-    if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, S, D))
+    if (use_scratch) {
+        if (attn_bwd_workspace_bytes(B, Hq, Hkv, S, D) > kScratchBytes) return ATTN_ERR_SCRATCH;
+    } else if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)) {
         return ATTN_ERR_WORKSPACE;
+    }
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
         misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
-        misaligned(workspace))
+        (!use_scratch && misaligned(workspace)))
         return ATTN_ERR_ALIGN;
     if ((rc = setup_current_device())) return rc;
+    if (use_scratch) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices || !g_scratch[dev]) {
+            (void)hipGetLastError();
+            return ATTN_ERR_HIP;
+        }
+        workspace = g_scratch[dev];
+    }
 
     attn::BwdArgs a;
     a.q = (const uint16_t*)q;
@@ -265,6 +296,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, D, causal, 0, scale,
                       workspace, workspace_bytes, stream);
 }
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,
+                     int D, int causal, float scale, void* stream) {
+    return bwd_stages(3, q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, S, D, D, causal, 0, scale,
+                      nullptr, 0, stream, true);
+}
+
+size_t attn_bwd_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
 
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
                 const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int S,

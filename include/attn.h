@@ -59,10 +59,12 @@ enum attn_status {
     ATTN_ERR_HIP = 8,           /* the HIP runtime failed (no device, launch error) */
     ATTN_ERR_DEVICE = 9,        /* the current device is not a gfx950 GPU */
     ATTN_ERR_WINDOW = 10,       /* a sliding window of fewer than 1 key (vdim: < 0, or set without causal) */
-    ATTN_ERR_SPARSE = 11        /* sparse: topk > 4096, Hq/Hkv > 128, N*D or S*topk >= 2^31,
+    ATTN_ERR_SPARSE = 11,       /* sparse: topk > 4096, Hq/Hkv > 128, N*D or S*topk >= 2^31,
                                    or a launch grid of 2^32 work-items or more:
                                    B*S*Hkv*ceil(Hq/Hkv/64)*128, B*S*Hkv*ceil(topk/128)*256
                                    or B*Hkv*N*256 */
+    ATTN_ERR_SCRATCH = 12       /* attn_bwd_noalloc: the sizes need more workspace than its
+                                   static scratch holds */
 };
 
 /*
@@ -108,6 +110,25 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, float* dq, float* dk, float* dv,
              int B, int Hq, int Hkv, int S, int D, int causal, float scale,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments and results as attn_bwd, without the workspace
+ * arguments. Its workspace is a static device array of the library, 8 MiB per
+ * GPU (attn_bwd_noalloc_max_workspace_bytes()), held from the first call on a
+ * device until the process ends; the call itself allocates nothing. Sizes with
+ * attn_bwd_workspace_bytes() above that limit return ATTN_ERR_SCRATCH before
+ * anything is launched (for example B*Hq*S up to 2,000,000 query rows fit). Every
+ * call on one GPU shares that GPU's array: calls that may overlap on one GPU
+ * (different streams, or other threads) race and must be ordered by the caller.
+ * Nothing in the array needs clearing between calls: each call writes every
+ * value it later reads.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, float* dq, float* dk, float* dv,
+                     int B, int Hq, int Hkv, int S, int D, int causal, float scale, void* stream);
+size_t attn_bwd_noalloc_max_workspace_bytes(void);
 
 /*
  * The two stages attn_bwd runs, for callers that schedule them separately

@@ -50,7 +50,7 @@ def test_lds_transpose_library_exports_its_header():
 
 
 def test_status_strings():
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = fa.attn_status_str(code)
         assert isinstance(s, str) and s
     assert fa.attn_status_str(0) == "ok"
@@ -240,6 +240,31 @@ def test_sparse_validates_pointers_and_workspace():
     assert lib.attn_sparse_bwd_workspace_bytes(1, 8, 1, 256, 320, 128, 0) == 0
 
 
+def bwd_noalloc(*, ptrs=None, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, scale=0.088):
+    p = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P)
+    p.update(ptrs or {})
+    return fa.load_library().attn_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"],
+                                              p["dk"], p["dv"], B, Hq, Hkv, S, D, causal, scale, None)
+
+
+def test_noalloc_validates_before_any_call():
+    """attn_bwd_noalloc checks its arguments like attn_bwd, and rejects sizes whose
+    workspace exceeds its static scratch, before touching the GPU."""
+    lib = fa.load_library()
+    limit = lib.attn_bwd_noalloc_max_workspace_bytes()
+    assert limit == 8 << 20
+    assert bwd_noalloc(ptrs={"dq": None}) == fa.ATTN_ERR_NULL
+    assert bwd_noalloc(ptrs={"dv": MIS}) == fa.ATTN_ERR_ALIGN
+    assert bwd_noalloc(Hq=6, Hkv=4) == fa.ATTN_ERR_GQA
+    assert bwd_noalloc(D=96) == fa.ATTN_ERR_UNSUPPORTED_D
+    assert bwd_noalloc(scale=math.nan) == fa.ATTN_ERR_SCALE
+    # two million query rows fit; 2^21 + 32 per head over four heads do not
+    assert lib.attn_bwd_workspace_bytes(1, 32, 8, 62500, 128) <= limit
+    assert lib.attn_bwd_workspace_bytes(1, 4, 1, (1 << 19) + 32, 128) > limit
+    assert bwd_noalloc(B=1, Hq=4, Hkv=1, S=(1 << 19) + 32) == fa.ATTN_ERR_SCRATCH
+    assert "scratch" in fa.attn_status_str(fa.ATTN_ERR_SCRATCH)
+
+
 def test_no_gpu_reports_hip_error():
     """Valid arguments on a machine without a usable gfx950 device end in a HIP or device
     error from the set-up step, never in a launch."""
@@ -251,3 +276,4 @@ def test_no_gpu_reports_hip_error():
     assert fwd_vdim() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
     assert fwd_vdim(D=64, Dv=128, window=16) in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
     assert sp_fwd() in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
+    assert bwd_noalloc(B=1, Hq=32, Hkv=8, S=62500) in (fa.ATTN_ERR_HIP, fa.ATTN_ERR_DEVICE)
