@@ -52,6 +52,115 @@ def pair_flops(D, Dv):
             "bwd": 6.0 * D + 4.0 * Dv}
 
 
+def algorithmic_pair_flops(D, Dv):
+    """The share of the algorithmic work (forward 2D + 2Dv, backward 6D + 4Dv per pair)
+    each launch computes: the dQ kernel recomputes S and dP, which the dK/dV kernel also
+    computes, so only its dQ = dS K product counts as its own."""
+    return {"fwd_kernel": 2.0 * (D + Dv), "dq_kernel": 2.0 * D, "dkv_kernel": 4.0 * (D + Dv),
+            "bwd_kernels": 6.0 * D + 4.0 * Dv}
+
+
+def host_cpu():
+    """CPU model and the cores this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "cores": len(os.sched_getaffinity(0))}
+
+
+def time_calls(fn, n, stream):
+    """Durations of fn (one or more launches on `stream`) with HIP events recorded on
+    that stream: the mean over n back-to-back calls, then the median and minimum of n
+    calls with an event between consecutive calls."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    mean = e0.elapsed_time(e1) / n
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        fn()
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+    return mean, per[n // 2], per[0]
+
+
+# The other dense workloads, reported beside the headline step: forward for all three,
+# the backward too for the non-causal D = 64 one.
+SIDE_CONFIGS = (("single_head_s128_d64", False), ("long_causal_gqa_s8192", False),
+                ("mha_noncausal_s2048_d64", True))
+
+
+def side_configs(n_rep):
+    """Per-entry-point figures of SIDE_CONFIGS, timed like the headline's."""
+    import torch
+    import flashattention_tiled_attention_amd as fa
+    from flashattention_tiled_attention_amd.inputs import CONFIGS, qkv
+    from tests.gpu_util import to_dev
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, with_bwd in SIDE_CONFIGS:
+        c = CONFIGS[name]
+        B, Hq, Hkv, S, D, causal = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], c["causal"]
+        log("side workload %s" % name)
+        scale = 1.0 / math.sqrt(D)
+        q, k, v, dout = qkv(B, Hq, Hkv, S, D, seed=0, with_dout=True)
+        tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(dout)
+        o = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        fns = {"fwd_kernel": lambda: fa.attn_fwd(tq, tk, tv, o, lse, causal, scale, stream)}
+        if with_bwd:
+            gq = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+            gk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
+            gv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device="cuda")
+            ws = torch.empty((fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D),), dtype=torch.uint8, device="cuda")
+            bargs = (tq, tk, tv, o, lse, tdo, gq, gk, gv, causal, scale, ws, stream)
+            fns["dq_kernel"] = lambda: fa.attn_bwd_dq(*bargs)
+            fns["dkv_kernel"] = lambda: fa.attn_bwd_dkdv(*bargs)
+        pairs = B * Hq * visible_pairs(S, causal)
+        pf = pair_flops(D, D)
+        entry = {"B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "causal": bool(causal)}
+        ms = {}
+        for kname, fn in fns.items():   # the forward runs first: the backward reads its o, lse
+            mean, med, mn = time_calls(fn, n_rep, stream)
+            ms[kname] = mean
+            tf = pf[kname] * pairs / (mean * 1e-3) / 1e12
+            entry[kname] = {"ms": round(mean, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+                            "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        entry["fwd"] = {k: entry["fwd_kernel"][k] for k in ("ms", "tflops", "frac_of_peak")}
+        if with_bwd:
+            bms = ms["dq_kernel"] + ms["dkv_kernel"]
+            tf = pf["bwd"] * pairs / (bms * 1e-3) / 1e12
+            entry["bwd"] = {"ms": round(bms, 4), "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        out[name] = entry
+        del tq, tk, tv, tdo, o, lse
+        if with_bwd:
+            del gq, gk, gv, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def clock_probe():
+    """The chip's matrix-core rate and shader clock on a register-only MFMA loop with
+    random bf16 operands (libmfma_rate), measured in the same run as the kernels."""
+    from flashattention_tiled_attention_amd import mfma_rate
+    r = mfma_rate.run("random", waves_per_simd=2, iters=50000)
+    return {"source": "register-only v_mfma_f32_32x32x16_bf16 loop, random bf16 operands, 2 waves/SIMD",
+            "shader_clock_ghz": r["shader_clock_ghz"], "mfma_tflops": r["tflops"],
+            "frac_of_peak": r["frac_of_peak"]}
+
+
 def cpu_baseline(q, k, v, dout, cfg, target_s, with_bwd):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload's query
     rows (forward) and key rows (backward); scale to TFLOP/s of the same convention."""
@@ -210,11 +319,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-configs", action="store_true",
+                    help="skip the clock probe and the other dense workloads' figures (profiling runs)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward kernel alone")
     ap.add_argument("--workload", default=WORKLOAD, help="an entry of inputs.CONFIGS (default %(default)s)")
     ap.add_argument("--copy-probe", action="store_true", help="run only the HBM counter calibration copy")
     ap.add_argument("--lds-transpose", action="store_true",
                     help="run only the LDS-to-register transpose microbenchmark (one JSON line)")
+    ap.add_argument("--mfma-rate", action="store_true",
+                    help="run only the matrix-core rate microbenchmark (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path; use --gpus 1",
@@ -228,6 +341,13 @@ def main():
         rows = lds_transpose.table()
         print(json.dumps({"metric": "LDS-to-register operand bandwidth, normalized to ds_read_b128",
                           "unit": "GB/s", "device": "MI355X (gfx950)", "methods": rows}), flush=True)
+        return
+
+    if args.mfma_rate:
+        from flashattention_tiled_attention_amd import mfma_rate
+        print(json.dumps({"metric": "v_mfma_f32_32x32x16_bf16 rate with operands in registers, whole chip",
+                          "unit": "TFLOP/s", "device": "MI355X (gfx950)", "peak": PEAK_BF16_TFLOPS,
+                          "runs": mfma_rate.table()}), flush=True)
         return
 
     import torch
@@ -333,29 +453,9 @@ def main():
     # Per-entry-point durations with HIP events recorded on the stream the kernels run
     # on: attn_fwd, attn_bwd_dq and attn_bwd_dkdv are one launch each (the exact-path
     # tiles run inside the same launch); a windowed, d_v or sparse workload times its
-    # forward and its whole backward entry point. The mean is over n back-to-back
-    # calls; then an event between consecutive calls gives each call's own duration,
-    # for the median and the minimum.
-    def time_calls(fn, n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        e1.synchronize()
-        mean = e0.elapsed_time(e1) / n
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        evs[0].record(stream)
-        for i in range(n):
-            fn()
-            evs[i + 1].record(stream)
-        evs[-1].synchronize()
-        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
-        return mean, per[n // 2], per[0]
-
+    # forward and its whole backward entry point.
     n_rep = max(args.steps, 10)
-    kernel_stats = {name: time_calls(fn, n_rep) for name, fn in calls.items()}
+    kernel_stats = {name: time_calls(fn, n_rep, stream) for name, fn in calls.items()}
     kernel_ms = {name: st[0] for name, st in kernel_stats.items()}
 
     # FLOP convention (pair_flops): each launch's products over the visible pairs; the
@@ -375,12 +475,19 @@ def main():
                 "flop_per_launch": dom_flops, "launch_ms": round(kernel_ms[dominant], 4)}
 
     kernels = {}
+    apf = algorithmic_pair_flops(D, Dv)
     for kname, ms in kernel_ms.items():
         fl = pf[kname] * pairs
         kernels[kname] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
-                         "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "ms_median": round(kernel_stats[kname][1], 4), "ms_min": round(kernel_stats[kname][2], 4),
-                         "calls": n_rep, "hbm_bytes": hbm_traffic(kname) if headline else None}
+                          "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "ms_median": round(kernel_stats[kname][1], 4), "ms_min": round(kernel_stats[kname][2], 4),
+                          "calls": n_rep, "hbm_bytes": hbm_traffic(kname) if headline else None}
+        if not sparse and kname in apf:
+            # the kernel's share of the algorithmic work: below its executed work only
+            # where it recomputes products another launch also computes (dQ's S and dP)
+            atf = apf[kname] * pairs / (ms * 1e-3) / 1e12
+            kernels[kname]["algorithmic_tflops"] = round(atf, 2)
+            kernels[kname]["algorithmic_frac_of_peak"] = round(atf / PEAK_BF16_TFLOPS, 4)
 
     result = {
         "metric": "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak on 1 MI355X",
@@ -403,6 +510,10 @@ def main():
         bwd_ms = kernel_ms["bwd_kernels"] if "bwd_kernels" in kernel_ms else kernel_ms["dq_kernel"] + kernel_ms["dkv_kernel"]
         result["bwd"] = {"tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2), "ms": round(bwd_ms, 4),
                          "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    result["host_cpu"] = host_cpu()
+    if headline and not args.no_side_configs:
+        result["clock"] = clock_probe()
+        result["side_configs"] = side_configs(n_rep)
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (~%.0f s)" % args.cpu_seconds)
         if sparse:

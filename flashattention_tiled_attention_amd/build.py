@@ -1,5 +1,6 @@
-"""Build the HIP attention library (libattn.so) and the LDS transpose
-microbenchmark (liblds_transpose.so) in-tree for gfx950 with hipcc."""
+"""Build the HIP attention library (libattn.so) and the two microbenchmarks, the
+LDS transpose one (liblds_transpose.so) and the matrix-core rate one
+(libmfma_rate.so), in-tree for gfx950 with hipcc."""
 import os
 import subprocess
 import sys
@@ -13,6 +14,8 @@ LIB = os.path.join(HERE, "libattn.so")
 SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_sparse.hip"]
 LDS_LIB = os.path.join(HERE, "liblds_transpose.so")
 LDS_SOURCES = ["lds_transpose.hip"]
+MFMA_LIB = os.path.join(HERE, "libmfma_rate.so")
+MFMA_SOURCES = ["mfma_rate.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -29,12 +32,12 @@ def _compile(src, obj, extra):
 
 
 def build(extra=None, verbose=False):
-    """Compile every source and link libattn.so and liblds_transpose.so; raises on any
-    compiler error. Returns the path of libattn.so."""
+    """Compile every source and link libattn.so, liblds_transpose.so and libmfma_rate.so;
+    raises on any compiler error. Returns the path of libattn.so."""
     extra = list(extra or [])
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    srcs = SOURCES + LDS_SOURCES
+    srcs = SOURCES + LDS_SOURCES + MFMA_SOURCES
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in srcs]
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
         results = list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(srcs, objs)))
@@ -43,7 +46,8 @@ def build(extra=None, verbose=False):
             sys.stderr.write(err + "\n")
         if rc:
             raise RuntimeError("hipcc failed: " + " ".join(cmd))
-    for lib, members in ((LIB, objs[:len(SOURCES)]), (LDS_LIB, objs[len(SOURCES):])):
+    n1, n2 = len(SOURCES), len(SOURCES) + len(LDS_SOURCES)
+    for lib, members in ((LIB, objs[:n1]), (LDS_LIB, objs[n1:n2]), (MFMA_LIB, objs[n2:])):
         tmp = lib + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + members
         subprocess.run(cmd, check=True)

@@ -49,6 +49,20 @@ def test_lds_transpose_library_exports_its_header():
     assert lib.lds_transpose_bench(0, 1, 1, 1, ctypes.byref(ms), MIS, P, None) == 2
 
 
+def test_mfma_rate_library_exports_its_header():
+    from flashattention_tiled_attention_amd import mfma_rate
+    text = open(os.path.join(ROOT, "include", "mfma_rate.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(mfma_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["mfma_rate_bench"]
+    lib = mfma_rate.load_library()
+    ms = ctypes.c_float(0)
+    # argument checks happen before any HIP call
+    assert lib.mfma_rate_bench(None, 1, 1, ctypes.byref(ms), P, P, None) == 2
+    assert lib.mfma_rate_bench(P, 0, 1, ctypes.byref(ms), P, P, None) == 2
+    assert lib.mfma_rate_bench(MIS, 1, 1, ctypes.byref(ms), P, P, None) == 2
+
+
 def test_status_strings():
     for code in range(0, 13):
         s = fa.attn_status_str(code)
