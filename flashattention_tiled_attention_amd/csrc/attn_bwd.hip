@@ -491,14 +491,52 @@ __device__ __forceinline__ void dkv_range(const BwdArgs& a, int kt, int& qi_firs
     qi_last = W > 0 ? min(nQB - 1, (kv0 + kKvBK - 1 + W - 1) / kKvBQ) : nQB - 1;
 }
 
+// One past the last query tile, among those key tile kt meets, that the dQ stage
+// flagged in any head of the group (qi_first when none is). Every wave scans the
+// flags on its own with scalar loads (wave-uniform addresses, read through the
+// constant address space: the dQ stage wrote them before this launch), so the scan
+// needs no vector registers, no LDS and no barrier. Four 8-flag loads are in flight
+// per round trip to the cache.
+template <bool CAUSAL>
+__device__ __forceinline__ int dkv_exact_end(const BwdArgs& a, int b, int hkv, int kt) {
+    typedef const __attribute__((address_space(4))) int cint;
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    typedef const __attribute__((address_space(4))) i32x8 cint8;
+    int qi_first, qi_last;
+    dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
+    const int per_g = qi_last - qi_first + 1, nQB = (a.S + kKvBQ - 1) / kKvBQ;
+    int end = 0;  // one past the last flagged tile, relative to qi_first
+    for (int g = 0; g < a.G; ++g) {
+        const int* row = a.peak + ((size_t)b * a.Hq + (size_t)hkv * a.G + g) * nQB + qi_first;
+        int i = 0;
+        for (; i + 32 <= per_g; i += 32) {
+            i32x8 f[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) f[u] = *(cint8*)(uintptr_t)(row + i + 8 * u);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) end = f[u][e] ? i + 8 * u + e + 1 : end;
+        }
+        for (; i + 8 <= per_g; i += 8) {
+            const i32x8 f = *(cint8*)(uintptr_t)(row + i);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) end = f[e] ? i + e + 1 : end;
+        }
+        for (; i < per_g; ++i) end = *(cint*)(uintptr_t)(row + i) ? i + 1 : end;
+    }
+    return qi_first + end;
+}
+
 // Query tiles qi_first .. qi_x - 1 (of every head of the group) run in a first loop
 // whose iterations take the exact path where the dQ stage flagged their tile (or
 // everywhere, when the host asks for it); tiles qi_x .. qi_last run in a second,
 // plain loop, where the per-iteration test is compiled out and the dV/dK product
 // loop is straight-line code. The accumulators carry from one loop into the other.
+// qi_x comes from the flags (dkv_exact_end), read once the K rows and the V tile
+// are on their way, so that their latencies overlap.
 template <int D, int DV, bool CAUSAL>
-__device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_raw, int b, int hkv, int kt,
-                                         int qi_x) {
+__device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_raw, int b, int hkv, int kt) {
     using T = KvTile<D, DV>;
     using QC = typename T::QCopy;
     using DC = typename T::DCopy;
@@ -559,6 +597,7 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
     const int W = CAUSAL ? a.window : 0;
     int qi_first, qi_last;
     dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
+    const int qi_x = a.precise_all ? qi_last + 1 : dkv_exact_end<CAUSAL>(a, b, hkv, kt);
 
     f32x16 dk[DBK], dv[DBV];
 #pragma unroll
@@ -831,44 +870,12 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
     }
 }
 
-// One past the last query tile, among those key tile kt meets, that the dQ stage
-// flagged in any head of the group (qi_first when none is). Every wave scans the
-// flags on its own with scalar loads (wave-uniform addresses, read through the
-// constant address space: the dQ stage wrote them before this launch), so the scan
-// needs no vector registers, no LDS and no barrier.
-template <bool CAUSAL>
-__device__ __forceinline__ int dkv_exact_end(const BwdArgs& a, int b, int hkv, int kt) {
-    typedef const __attribute__((address_space(4))) int cint;
-    typedef int i32x8 __attribute__((ext_vector_type(8)));
-    typedef const __attribute__((address_space(4))) i32x8 cint8;
-    int qi_first, qi_last;
-    dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
-    const int per_g = qi_last - qi_first + 1, nQB = (a.S + kKvBQ - 1) / kKvBQ;
-    int end = 0;  // one past the last flagged tile, relative to qi_first
-    for (int g = 0; g < a.G; ++g) {
-        const int* row = a.peak + ((size_t)b * a.Hq + (size_t)hkv * a.G + g) * nQB + qi_first;
-        int i = 0;
-        for (; i + 8 <= per_g; i += 8) {
-            const i32x8 f = *(cint8*)(uintptr_t)(row + i);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) end = f[e] ? i + e + 1 : end;
-        }
-        for (; i < per_g; ++i) end = *(cint*)(uintptr_t)(row + i) ? i + 1 : end;
-    }
-    return qi_first + end;
-}
-
 template <int D, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(kKvThreads, 1) dkv_kernel(BwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     int b, hkv, kt;
     dkv_item(a, b, hkv, kt);
-    // The exact loop covers the query tiles up to the last one the dQ stage flagged
-    // (a row with a probability above kPeakP), or every tile on request.
-    int qi_first, qi_last;
-    dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
-    const int qi_x = a.precise_all ? qi_last + 1 : dkv_exact_end<CAUSAL>(a, b, hkv, kt);
-    dkv_body<D, DV, CAUSAL>(a, lds_raw, b, hkv, kt, qi_x);
+    dkv_body<D, DV, CAUSAL>(a, lds_raw, b, hkv, kt);
 }
 
 template <int D, int DV, bool CAUSAL>

@@ -10,8 +10,8 @@
 //
 // One workgroup = 8 waves = one tile of 256 query rows of one (batch, head);
 // each wave owns 32 rows (with a sliding window, fwd_win_kernel gives the 8
-// waves several query heads of one kv head instead, see there). Per 64-key tile
-// j, a wave does
+// waves several query heads of one kv head instead, see there). Per key tile j
+// (64 keys; 128 when queries, keys and values are all 64 wide), a wave does
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in registers (B)
 //                      -> every lane holds one query column and 32 of its keys,
 //                         so the row max/sum are lane-local plus one permlane32 swap
@@ -22,7 +22,7 @@
 // Ping-pong: the waves form two groups of four, and each SIMD holds one wave of
 // each group. Time is cut into phases separated by workgroup barriers; in every
 // phase one group runs its matrix work (the P V product of tile j-1 and the
-// score product of tile j: 32 MFMAs at D=128) while the other group runs the
+// score product of tile j: 32 MFMAs) while the other group runs the
 // softmax of its previous tile on the vector unit, so each SIMD's matrix unit
 // always has one wave feeding it. The matrix-phase wave raises its issue
 // priority so its MFMAs are not starved by the softmax wave.
@@ -56,22 +56,34 @@ namespace attn {
 namespace {
 
 constexpr int kFwdBQ = 256;     // query rows per workgroup
-constexpr int kFwdBK = 64;      // keys per LDS tile
 constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kLook = 4;        // LDS operand reads in flight ahead of the MFMAs
 
-template <int D, int DV>
+// Keys per LDS tile of a body: 128 for the plain body when queries, keys and
+// values are all 64 wide, so a matrix phase has 32 MFMAs as it does at 128 (with
+// 64-key tiles a D = 64 phase had 16, too few to cover the softmax phase and the
+// barriers); 64 otherwise. The exact body keeps 64: its split probabilities need
+// the registers that 128-key scores would take.
+template <int D, int DV, bool PRECISE>
+constexpr int fwd_keys_per_tile() { return (D == 64 && DV == 64 && !PRECISE) ? 128 : 64; }
+
+template <int D, int DV, int BK_ = 64>
 struct FwdTile {
-    // K tiles are unpadded [64][D] and V tiles [64][DV] bf16, in the chunk order
+    static constexpr int BK = BK_;
+    // K tiles are unpadded [BK][D] and V tiles [BK][DV] bf16, in the chunk order
     // of swz<D> and swz<DV>, so each 1 KB run of rows is contiguous, as the
     // direct copies need.
-    static constexpr int KTILE = kFwdBK * D;                      // elements
-    static constexpr int VTILE = kFwdBK * DV;
+    static constexpr int KTILE = BK * D;                          // elements
+    static constexpr int VTILE = BK * DV;
     static constexpr int LDS_BYTES = 2 * (KTILE + VTILE) * 2;     // 2 K slots + 2 V slots
-    using KCopy = CopyPlan<D, kFwdBK, kFwdWaves>;
-    using VCopy = CopyPlan<DV, kFwdBK, kFwdWaves>;
+    using KCopy = CopyPlan<D, BK, kFwdWaves>;
+    using VCopy = CopyPlan<DV, BK, kFwdWaves>;
 };
+
+// Dynamic LDS of a forward launch: the larger of its two bodies' rings.
+template <int D, int DV>
+constexpr int fwd_lds_bytes() { return FwdTile<D, DV, fwd_keys_per_tile<D, DV, false>()>::LDS_BYTES; }
 
 // Work item of workgroup `bid` among nQ query-tile ranks: rank r is query tile
 // qt_first - r when causal (longest first), qt_first + r otherwise. When the
@@ -105,9 +117,12 @@ __device__ __forceinline__ void decode_item(int bid, int nQ, int qt_first, int B
 template <int D, int DV, bool CAUSAL, bool PRECISE>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, int hq, int q0, int q_last,
                                          int row0) {
-    using T = FwdTile<D, DV>;
+    using T = FwdTile<D, DV, fwd_keys_per_tile<D, DV, PRECISE>()>;
     using KC = typename T::KCopy;
     using VC = typename T::VCopy;
+    constexpr int BK = T::BK;    // keys per tile
+    constexpr int NKB = BK / 32; // 32-key blocks of a tile's scores
+    constexpr int NT = BK / 16;  // 16-key steps of its P V product
     constexpr int DK = D / 16;   // k-steps of the score product
     constexpr int DB = DV / 32;  // 32-row blocks of O^T
 
@@ -140,15 +155,15 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
         for (int dk = 0; dk < DK; ++dk) qf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
 
-    const int nK = (S + kFwdBK - 1) / kFwdBK;
-    const int jend = CAUSAL ? min(nK, q_last / kFwdBK + 1) : nK;
-    int wjend = CAUSAL ? min(jend, (row0 + 31) / kFwdBK + 1) : jend;
+    const int nK = (S + BK - 1) / BK;
+    const int jend = CAUSAL ? min(nK, q_last / BK + 1) : nK;
+    int wjend = CAUSAL ? min(jend, (row0 + 31) / BK + 1) : jend;
     if (row0 >= S) wjend = 0;  // a wave with no live rows only helps load
     // Window: the workgroup's first tile holds the first row's first key, a wave's
     // first tile its first row's; tiles with keys below row0 + 32 - W are masked.
     const int W = CAUSAL ? a.window : 0;
-    const int jstart = W > 0 ? max(0, q0 - W + 1) / kFwdBK : 0;
-    const int wjstart = W > 0 ? max(0, row0 - W + 1) / kFwdBK : 0;
+    const int jstart = W > 0 ? max(0, q0 - W + 1) / BK : 0;
+    const int wjstart = W > 0 ? max(0, row0 - W + 1) / BK : 0;
 
     __bf16* const Kring = smem;
     __bf16* const Vring = smem + 2 * T::KTILE;
@@ -171,8 +186,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
         vcoff[n] = (uint32_t)(row * DV + ((lane % VC::CH) ^ swz_f<DV>(row)) * 8) * 2u;
     }
     auto copy_k = [&](__bf16* dst, int j) {
-        const int k0 = j * kFwdBK;
-        if (k0 + kFwdBK <= S) {
+        const int k0 = j * BK;
+        if (k0 + BK <= S) {
             const uint16_t* base = Kp + (size_t)k0 * D;
 #pragma unroll
             for (int n = 0; n < KC::N; ++n) copy16_to_lds_s(base, kcoff[n], dst + (wave * KC::N + n) * 512);
@@ -185,8 +200,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
         }
     };
     auto copy_v = [&](__bf16* dst, int j) {
-        const int k0 = j * kFwdBK;
-        if (k0 + kFwdBK <= S) {
+        const int k0 = j * BK;
+        if (k0 + BK <= S) {
             const uint16_t* base = Vp + (size_t)k0 * DV;
 #pragma unroll
             for (int n = 0; n < VC::N; ++n) copy16_to_lds_s(base, vcoff[n], dst + (wave * VC::N + n) * 512);
@@ -218,9 +233,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     // window keeps m, and exp2(-inf - m) is then 0 rather than NaN; the first
     // visible key moves it, and exp2(m - mnew) is 0 as it would be from -inf.
     float m = -1e30f, l = 0.0f;
-    f32x16 sc[2];   // scores of the tile between its matrix and softmax phases
-    bf16x8 pk[4];   // probabilities of the tile between its softmax and P V phases
-    bf16x8 pl[4];   // their bf16 remainders (PRECISE only)
+    f32x16 sc[NKB];  // scores of the tile between its matrix and softmax phases
+    bf16x8 pk[NT];   // probabilities of the tile between its softmax and P V phases
+    bf16x8 pl[NT];   // their bf16 remainders (PRECISE only)
 
     // Matrix phase of tile j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
     // par: std::integral_constant holding j & 1, or -1 to take it from j at run time.
@@ -232,7 +247,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             const __bf16* Vs = Vring + (PC < 0 ? ((j - 1) & 1) : (P ^ 1)) * T::VTILE;
             constexpr int MPER = PRECISE ? 2 : 1;  // MFMAs per V^T operand
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const bf16x4 v1 = lds_read_tr(Vs + voff[0][db] + 16 * t * DV);
@@ -245,7 +260,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             // cover LDS latency with bounded register use
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 0);
 #pragma unroll
-            for (int i = 0; i < 4 * DB - kLook; ++i) {
+            for (int i = 0; i < NT * DB - kLook; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, MPER, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
@@ -254,18 +269,18 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
         }
         if (j >= wjstart && j < wjend) {
             const __bf16* Ks = Kring + P * T::KTILE;
-            sc[0] = zero16();
-            sc[1] = zero16();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sc[kb] = zero16();
 #pragma unroll
             for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
                     const bf16x8 kf = lds_read8(Ks + koff[dk] + kb * 32 * D);
                     sc[kb] = mfma32(kf, qf[dk], sc[kb]);
                 }
             __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);
 #pragma unroll
-            for (int i = 0; i < 2 * DK - kLook; ++i) {
+            for (int i = 0; i < NKB * DK - kLook; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
@@ -276,11 +291,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     };
 
     // Probabilities exp2(s c - m) of the tile as bf16 B operands (and their bf16
-    // remainders on the exact path); returns this lane's sum of the 32.
+    // remainders on the exact path); returns this lane's sum of its BK/2.
     auto probs = [&]() {
         float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NT; ++t) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -303,21 +318,25 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
     // the running maximum, probabilities as bf16 B operands, row sums.
     auto softmax_phase = [&](int j) {
         if (j < wjstart || j >= wjend) return;
-        if (j == wjend - 1 || (W > 0 && j * kFwdBK < row0 + 32 - W)) {
-            // key j*64 + 4h + off is visible iff lo <= off <= lim
-            const int base = j * kFwdBK + 4 * h;
+        if (j == wjend - 1 || (W > 0 && j * BK < row0 + 32 - W)) {
+            // key j*BK + 4h + off is visible iff lo <= off <= lim
+            const int base = j * BK + 4 * h;
             const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - base;
             const int lo = W > 0 ? qrow - W + 1 - base : -(1 << 30);
+            // -inf is added, not selected: adding the bit pattern 0xff800000 (or
+            // +0.0) under a sign-extended mask keeps the 2 * BK/2 comparisons out
+            // of the scalar registers, which a select would fill with lane masks
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-                    if (off > lim || off < lo) sc[kb][r] = -INFINITY;
+                    const int hidden = ((lim - off) | (off - lo)) >> 31;  // all ones iff off > lim or off < lo
+                    sc[kb][r] += __int_as_float(hidden & (int)0xff800000u);
                 }
         }
         // Past a wave's first tile the maximum is usually not needed: if every
-        // lane's 32 probabilities against the current m sum to at most
+        // lane's BK/2 probabilities against the current m sum to at most
         // 2^(slack-1), each of them is at most that, so the tile maximum is
         // within slack-1 of m (one unit of margin covers the rounding of the two
         // forms) and the rule below would leave m alone. The probabilities and
@@ -331,13 +350,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             need_max = __any(!(tot <= max_bound));
         }
         if (need_max) {
-            float mx0 = fmaxf(sc[0][0], sc[0][1]), mx1 = fmaxf(sc[1][0], sc[1][1]);
+            float mx[NKB];
 #pragma unroll
-            for (int r = 2; r < 16; ++r) {
-                mx0 = fmaxf(mx0, sc[0][r]);
-                mx1 = fmaxf(mx1, sc[1][r]);
+            for (int kb = 0; kb < NKB; ++kb) {
+                mx[kb] = fmaxf(sc[kb][0], sc[kb][1]);
+#pragma unroll
+                for (int r = 2; r < 16; ++r) mx[kb] = fmaxf(mx[kb], sc[kb][r]);
             }
-            const float mt = halves_max(fmaxf(mx0, mx1)) * c;  // c > 0
+#pragma unroll
+            for (int kb = 1; kb < NKB; ++kb) mx[0] = fmaxf(mx[0], mx[kb]);
+            const float mt = halves_max(mx[0]) * c;  // c > 0
             // The running maximum only moves when some row's grows by more than
             // max_slack (log2 units; 8 for ordinary score spreads): until then
             // every exp2(t - m) <= 2^slack, carried by fp32 and bf16 without
@@ -526,7 +548,7 @@ hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
     // problems go to fwd_win_kernel, which makes that choice per workgroup.
     const int nQ = (args.S + kFwdBQ - 1) / kFwdBQ;
     FwdArgs a = args;
-    constexpr int lds = FwdTile<D, DV>::LDS_BYTES;
+    constexpr int lds = fwd_lds_bytes<D, DV>();
     if (CAUSAL && a.window > 0) {
         const int HW = win_heads(a.G), BQ = 32 * (8 / HW);
         const long long wblocks = (long long)((a.S + BQ - 1) / BQ) * a.B * a.Hkv * (a.G / HW);
@@ -546,9 +568,9 @@ hipError_t set_lds(K kernel, int bytes) {
 
 template <int D, int DV>
 hipError_t setup_pair() {
-    hipError_t e = set_lds(fwd_kernel<D, DV, false>, FwdTile<D, DV>::LDS_BYTES);
-    if (!e) e = set_lds(fwd_kernel<D, DV, true>, FwdTile<D, DV>::LDS_BYTES);
-    return e ? e : set_lds(fwd_win_kernel<D, DV>, FwdTile<D, DV>::LDS_BYTES);
+    hipError_t e = set_lds(fwd_kernel<D, DV, false>, fwd_lds_bytes<D, DV>());
+    if (!e) e = set_lds(fwd_kernel<D, DV, true>, fwd_lds_bytes<D, DV>());
+    return e ? e : set_lds(fwd_win_kernel<D, DV>, fwd_lds_bytes<D, DV>());
 }
 
 template <int D, int DV>
