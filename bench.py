@@ -133,6 +133,9 @@ def side_configs(n_rep):
         entry = {"B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "causal": bool(causal)}
         ms = {}
         for kname, fn in fns.items():   # the forward runs first: the backward reads its o, lse
+            for _ in range(5):          # warm-up: the clocks ramp up from the host-side set-up
+                fn()
+            torch.cuda.synchronize()
             mean, med, mn = time_calls(fn, n_rep, stream)
             ms[kname] = mean
             tf = pf[kname] * pairs / (mean * 1e-3) / 1e12
