@@ -28,7 +28,7 @@ int g_dev_status[kMaxDevices];
 // ends. In host code `scratch` names a host-side stand-in, not device memory; the
 // device address of each GPU's copy is taken once per device at set-up
 // (g_scratch) and only that address is ever passed to a kernel.
-constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr size_t kScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 void* g_scratch[kMaxDevices];
 
@@ -92,10 +92,12 @@ int check_sizes(int B, int Hq, int Hkv, int S, int D, int Dv) {
     return ATTN_OK;
 }
 
-// Dense backward workspace: delta [B][Hq][S] fp32, then the per-32-row-block
-// exact-path flags [B][Hq][ceil(S/32)] int32, each part 256-byte aligned.
-size_t delta_bytes(int B, int Hq, int S) {
-    return (((size_t)B * Hq * S * sizeof(float)) + 255) & ~(size_t)255;
+// Dense backward workspace: the row statistics [B][Hq][ceil(S/32)][64] fp32 (per
+// block of 32 query rows their lse * log2(e), then their -delta; rows past S hold
+// +inf and -0), then the per-32-row-block exact-path flags [B][Hq][ceil(S/32)]
+// int32, each part 256-byte aligned.
+size_t rowstat_bytes(int B, int Hq, int S) {
+    return (((size_t)B * Hq * ((S + 31) / 32) * 32 * 2 * sizeof(float)) + 255) & ~(size_t)255;
 }
 size_t peak_bytes(int B, int Hq, int S) {
     return (((size_t)B * Hq * ((S + 31) / 32) * sizeof(int)) + 255) & ~(size_t)255;
@@ -167,7 +169,7 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_SPARSE:
             return "sparse sizes out of range: topk <= 4096, Hq/Hkv <= 128, N*D and S*topk < 2^31";
         case ATTN_ERR_SCRATCH:
-            return "attn_bwd_noalloc: attn_bwd_workspace_bytes() for these sizes exceeds its 8 MiB static scratch";
+            return "attn_bwd_noalloc: attn_bwd_workspace_bytes() for these sizes exceeds its 16 MiB static scratch";
         default: return "unknown attn status";
     }
 }
@@ -227,7 +229,7 @@ int attn_fwd_vdim(const void* q, const void* k, const void* v, void* o, float* l
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
     if (check_sizes(B, Hq, Hkv, S, D, D) != ATTN_OK) return 0;
-    return delta_bytes(B, Hq, S) + peak_bytes(B, Hq, S);
+    return rowstat_bytes(B, Hq, S) + peak_bytes(B, Hq, S);
 }
 
 // use_scratch: the workspace is this device's static scratch (attn_bwd_noalloc);
@@ -269,8 +271,8 @@ static int bwd_stages(int stages, const void* q, const void* k, const void* v, c
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    a.delta = (float*)workspace;
-    a.peak = (int*)((unsigned char*)workspace + delta_bytes(B, Hq, S));
+    a.rowstat = (float*)workspace;
+    a.peak = (int*)((unsigned char*)workspace + rowstat_bytes(B, Hq, S));
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.G = Hq / Hkv;
     a.causal = causal ? 1 : 0;
     a.window = window;

@@ -10,22 +10,29 @@
 // transposed operand read it with the gfx950 transpose load
 // (ds_read_b64_tr_b16) from the row-major tile in LDS.
 //
-// Two kernels, ordered on the caller's stream, no atomics (deterministic):
+// Two stages, ordered on the caller's stream, no atomics (deterministic):
 //   dq_kernel   one workgroup per (b, hq, 128-row query tile); K/V tiles stream
 //               from HBM straight into double-buffered, swizzled LDS tiles
 //               (global_load_lds). It also computes the exact delta of its rows
 //               and a flag per 32-row block (below) and stores them in the
-//               workspace. With a sliding window, dq_win_kernel runs the
+//               workspace, with lse * log2(e), as the row statistics of each
+//               32-row block. With a sliding window, dq_win_kernel runs the
 //               same body with the query heads of one kv head side by side in a
 //               workgroup (fewer rows per head, so every wave uses nearly all of
 //               the workgroup's key tiles).
-//   dkv_kernel  one workgroup of 8 waves per (b, kv head, 64-key tile). K stays
-//               in registers and V in LDS; 32-row Q/dO tiles of every query head of
-//               the group stream from HBM into double-buffered LDS. Four wave pairs
-//               split the (head, query tile) iterations and their dK/dV partial
+//   dK/dV       one workgroup per (b, kv head, 64-key tile); 32-row Q/dO tiles of
+//               every query head of the group stream from HBM into LDS, and wave
+//               pairs split the (head, query tile) iterations; their dK/dV partial
 //               sums are added in LDS at the end in a fixed order, so the
 //               grouped-query sum never leaves the chip and is deterministic.
-//
+//               dkv_kernel (D or DV = 128): 8 waves, two per SIMD, in lock-step
+//               through one barrier per step, K in registers, V in LDS, a
+//               double-buffered stage per pair. dkv1_kernel (D = DV = 64): 4
+//               waves, one per SIMD, K and V in registers, a ring of four stages
+//               per pair fed three steps ahead, each wave software-pipelined
+//               (the S/dP products of the next step under the vector work of this
+//               one).
+
 // delta is always the exact sum_j P_ij dP_ij in fp32, accumulated by the dQ
 // kernel's pass (delta = rowsum(dO * O) from the bf16-stored O is off by up to
 // 2^-9 of |dO| |O|, which the GQA sum carries into dK on rows with a large
@@ -352,8 +359,13 @@ __device__ __forceinline__ bool dq_body(const BwdArgs& a, __bf16* smem, int b, i
         *peak = 1;
     }
 
+    if (h == 0 && row0 < S) {  // every row of the 32-row block, those past S as (+inf, -0)
+        const size_t S32 = (size_t)nQB * 32;
+        float* blk = a.rowstat + (((size_t)b * a.Hq + hq) * S32 + row0) * 2;  // this block's 64 words
+        blk[l32] = live ? a.lse[rowbase + qrow] * kLog2e : INFINITY;  // loaded again: not held across the loop
+        blk[32 + l32] = live ? -delta : -0.0f;
+    }
     if (live) {
-        if (h == 0) a.delta[rowbase + qrow] = delta;
         if (redo) return true;  // dQ is stored by the exact pass
         float* dst = a.dq + (rowbase + qrow) * D;
         const float sc = a.scale;
@@ -435,31 +447,43 @@ __global__ void __launch_bounds__(kDqThreads, 2) dq_win_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV kernel
+// dK/dV kernels: the work split both use, then dkv1_kernel (one wave per SIMD)
 // ---------------------------------------------------------------------------
 constexpr int kKvBK = 64;      // keys per workgroup (2 waves x 32)
 constexpr int kKvBQ = 32;      // query rows per streamed tile
-constexpr int kKvSplits = 4;   // wave pairs that split the (head, query tile) iterations
-constexpr int kKvThreads = 64 * 2 * kKvSplits;
+constexpr int kKv1Splits = 2;   // wave pairs that split the (head, query tile) iterations
+constexpr int kKv1Ring = 4;     // stages per pair: the copies run three steps ahead
+constexpr int kKv1Threads = 64 * 2 * kKv1Splits;   // one wave per SIMD
 
 template <int D, int DV>
-struct KvTile {
-    // V tile [64][DV] and per-split double-buffered Q [32][D] and dO [32][DV]
-    // tiles, all bf16 in the swizzled chunk order of swz; lse*log2e and delta per
-    // query row.
+struct Kv1Tile {
+    // Per pair a ring of kKv1Ring stages {Q [32][D], dO [32][DV], the 32 rows'
+    // lse*log2e then their -delta}, the tiles bf16 in the swizzled chunk order of
+    // swz (K and V rows of the workgroup's keys are held in registers).
     static constexpr int QTILE = kKvBQ * D;                          // elements
     static constexpr int DTILE = kKvBQ * DV;
-    static constexpr int STAGE_BYTES = (QTILE + DTILE) * 2 + 2 * kKvBQ * 4;
-    static constexpr int SPLIT_BYTES = 2 * STAGE_BYTES;
-    static constexpr int VTILE_BYTES = kKvBK * DV * 2;
-    static constexpr int TILE_BYTES = VTILE_BYTES + kKvSplits * SPLIT_BYTES;
-    // final sum: two splits hand over dK and dV of both key halves
-    static constexpr int XCHG_BYTES = 2 * 2 * (D / 32 + DV / 32) * 16 * 64 * 4;
+    static constexpr int STAGE_BYTES = (QTILE + DTILE) * 2 + kKvBQ * 8;
+    static constexpr int SPLIT_BYTES = kKv1Ring * STAGE_BYTES;
+    static constexpr int TILE_BYTES = kKv1Splits * SPLIT_BYTES;
+    // final sum: one pair hands over dK, the other dV, of both key halves
+    static constexpr int XCHG_BYTES = 2 * (D / 32 + DV / 32) * 16 * 64 * 4;
     static constexpr int LDS_BYTES = TILE_BYTES > XCHG_BYTES ? TILE_BYTES : XCHG_BYTES;
     using QCopy = CopyPlan<D, kKvBQ, 2>;                             // per wave of a pair
     using DCopy = CopyPlan<DV, kKvBQ, 2>;
-    using VCopy = CopyPlan<DV, kKvBK, 2 * kKvSplits>;                // per wave
+    // vector-memory operations of one stage fetch, per wave
+    static constexpr int NF = QCopy::N + DCopy::N + 1;
 };
+
+// Which dK/dV kernel runs: the one-wave-per-SIMD pipelined kernel below for
+// D = DV = 64, the two-waves-per-SIMD kernel further down otherwise. Measured on an
+// MI355X in one process, the one-wave kernel takes 0.34 ms against 0.43 ms on a
+// non-causal B=8, H=16, S=2048, D=64 problem, but 0.32 ms against 0.30 ms on the
+// causal Llama-3.1-8B shape (D = 128): a single wave issues its instructions in
+// order, and at D = 128 its vector work, copies and bookkeeping per step no longer
+// fit under its matrix instructions, where two waves per SIMD issue theirs side by
+// side.
+template <int D, int DV>
+constexpr bool kDkvOneWave = D == 64 && DV == 64;
 
 // Work item of a dK/dV workgroup: (b, hkv, key tile); causal tiles issued longest
 // (lowest) first, groups dealt to XCDs as in the forward.
@@ -527,6 +551,607 @@ __device__ __forceinline__ int dkv_exact_end(const BwdArgs& a, int b, int hkv, i
     }
     return qi_first + end;
 }
+
+// Query tiles qi_first .. qi_x - 1 (of every head of the group) run in a first loop
+// whose iterations take the exact path where the dQ stage flagged their tile (or
+// everywhere, when the host asks for it); tiles qi_x .. qi_last run in a second,
+// plain loop. The accumulators carry from one loop into the other. qi_x comes from
+// the flags (dkv_exact_end), read once the K rows and the V tile are on their way.
+//
+// One wave per SIMD: the wave keeps its own matrix core busy by software
+// pipelining. The plain loop's step j issues the S/dP products of step j+1 with,
+// between its matrix instructions (explicitly ordered scheduling regions), the
+// vector work that turns step j's S/dP into bf16 P and dS operands and the copies
+// of a stage three steps ahead; then step j's dV/dK products, in whose regions the
+// next step's bookkeeping runs. Stage copies (Q, dO and the row statistics) go
+// through a ring of four stages per pair, and every wait on them is a count of
+// this wave's vector-memory operations. dP - delta is formed by the dP products
+// themselves, their accumulator starting at -delta.
+template <int D, int DV, bool CAUSAL>
+__device__ __forceinline__ void dkv1_body(const BwdArgs& a, unsigned char* lds_raw, int b, int hkv, int kt) {
+    using T = Kv1Tile<D, DV>;
+    using QC = typename T::QCopy;
+    using DC = typename T::DCopy;
+    constexpr int NF = T::NF;
+    constexpr int DK = D / 16;     // k-steps of the score product
+    constexpr int DKV = DV / 16;   // k-steps of the dP product
+    constexpr int DKM = DK > DKV ? DK : DKV;
+    constexpr int DBK = D / 32;    // 32-row blocks of dK^T
+    constexpr int DBV = DV / 32;   // 32-row blocks of dV^T
+    constexpr int DBM = DBK > DBV ? DBK : DBV;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int split = wave >> 1, w2 = wave & 1;
+    const int S = a.S, G = a.G;
+    const int nQB = (S + kKvBQ - 1) / kKvBQ;
+    const size_t S32 = (size_t)nQB * kKvBQ;
+
+    const int kv0 = kt * kKvBK;
+    const int kw0 = kv0 + 32 * w2;  // this wave's first key
+    const int key = kw0 + l32;      // this lane's key (column of S, dP)
+    const size_t kvrow = ((size_t)b * a.Hkv + hkv) * (size_t)S;
+    const float c = a.scale_log2;
+
+    // K and V rows of this lane's key as B operands (zero past the end).
+    bf16x8 kf[DK], vf[DKV];
+    if (key < S) {
+        const u32x4* ks = (const u32x4*)(a.k + (kvrow + key) * D + 8 * h);  // K is D wide
+        const u32x4* vs = (const u32x4*)(a.v + (kvrow + key) * DV + 8 * h);  // V is DV wide
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) kf[dk] = __builtin_bit_cast(bf16x8, ks[2 * dk]);
+#pragma unroll
+        for (int dk = 0; dk < DKV; ++dk) vf[dk] = __builtin_bit_cast(bf16x8, vs[2 * dk]);
+    } else {
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) kf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int dk = 0; dk < DKV; ++dk) vf[dk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+
+    // LDS: per pair the ring of stages.
+    unsigned char* const split_base = lds_raw + split * T::SPLIT_BYTES;
+    auto stage_q = [&](int sl) { return (__bf16*)(split_base + sl * T::STAGE_BYTES); };
+    auto stage_do = [&](int sl) { return stage_q(sl) + T::QTILE; };
+    auto stage_st = [&](int sl) {  // lse*log2e of the 32 rows, then their -delta
+        return (float*)(split_base + sl * T::STAGE_BYTES + (T::QTILE + T::DTILE) * 2);
+    };
+
+    // Iterations of a loop over query tiles q_lo .. q_lo + nq - 1: (g, query tile qi)
+    // for every head g of the group; pair p takes iterations p, p + kKv1Splits, ...
+    const int W = CAUSAL ? a.window : 0;
+    int qi_first, qi_last;
+    dkv_range<CAUSAL>(a, kt, qi_first, qi_last);
+    const int qi_x = a.precise_all ? qi_last + 1 : dkv_exact_end<CAUSAL>(a, b, hkv, kt);
+
+    f32x16 dk[DBK], dv[DBV];
+#pragma unroll
+    for (int db = 0; db < DBK; ++db) dk[db] = zero16();
+#pragma unroll
+    for (int db = 0; db < DBV; ++db) dv[db] = zero16();
+
+    // Per-lane LDS offsets: A-operand rows (Q; dO and V) per k-step; transpose
+    // quads (Q^T; dO^T) per 32-column block and row half.
+    int roff[DK], rvoff[DKV], toff[2][DBK], tvoff[2][DBV];
+#pragma unroll
+    for (int dk2 = 0; dk2 < DK; ++dk2) roff[dk2] = swz<D>(l32, dk2 * 16 + 8 * h);
+#pragma unroll
+    for (int dk2 = 0; dk2 < DKV; ++dk2) rvoff[dk2] = swz<DV>(l32, dk2 * 16 + 8 * h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int db = 0; db < DBK; ++db)
+            toff[hf][db] = swz<D>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                  db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+#pragma unroll
+        for (int db = 0; db < DBV; ++db)
+            tvoff[hf][db] = swz<DV>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                    db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    }
+
+    // -delta of this lane's 16 rows (8(r/4) + 4h + r%4, r = 0..15) of the stage in
+    // slot sl, as the initial value of the dP accumulator
+    auto neg_delta = [&](int sl) {
+        const float* Nd = stage_st(sl) + kKvBQ;
+        f32x16 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 x = *(const f32x4*)(Nd + 8 * q + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+        }
+        return v;
+    };
+    // S = Q K^T and dP - delta = dO V^T - delta of the stage in ring slot sl (32
+    // queries x this wave's keys)
+    auto sdp = [&](int sl, f32x16& sv, f32x16& dpv) {
+        const __bf16* Qs = stage_q(sl);
+        const __bf16* Ds = stage_do(sl);
+        sv = zero16();
+        dpv = neg_delta(sl);  // dP - delta: the products add onto -delta
+#pragma unroll
+        for (int dd = 0; dd < DKM; ++dd) {
+            bf16x8 qa, da;
+            if (dd < DK) qa = lds_read8(Qs + roff[dd]);
+            if (dd < DKV) da = lds_read8(Ds + rvoff[dd]);
+            if (dd < DK) sv = mfma32(qa, kf[dd], sv);
+            if (dd < DKV) dpv = mfma32(da, vf[dd], dpv);
+        }
+    };
+    // P = exp2(S c - lse log2 e) and dS = P (dP - delta) of the 16-query half t2
+    // (dpv holds dP - delta); rows of sv/dpv are queries 8(r/4) + 4h + r%4, the
+    // column is this lane's key. With the mask, keys outside a row's causal (or
+    // window) range get P = 0.
+    auto pds = [&](int sl, int qs0, auto mask_tag, const f32x16& sv, const f32x16& dpv, int t2,
+                   float (&pv)[8], float (&dsv)[8]) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const float* St = stage_st(sl);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int r0 = 8 * (2 * t2 + half) + 4 * h;  // first of this lane's 4 rows
+            const f32x4 l4 = *(const f32x4*)(St + r0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * half + e;
+                float p = fast_exp2(fmaf(sv[8 * t2 + i], c, -l4[e]));
+                if (MASK) {
+                    const int qrow = qs0 + r0 + e;
+                    p = (key > qrow || (W > 0 && qrow >= key + W)) ? 0.0f : p;
+                }
+                pv[i] = p;
+                dsv[i] = p * dpv[8 * t2 + i];
+            }
+        }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS for the 16-query half t2 (plus the remainder
+    // operands on the exact path)
+    auto dvdk = [&](int sl, int t2, const bf16x8& ph, const bf16x8& sh, bool precise, const bf16x8& pl,
+                    const bf16x8& sl_) {
+        const __bf16* Qs = stage_q(sl);
+        const __bf16* Ds = stage_do(sl);
+        const int rbk = 16 * t2 * D, rbv = 16 * t2 * DV;
+#pragma unroll
+        for (int db = 0; db < DBM; ++db) {
+            bf16x8 dot, qt;
+            if (db < DBV)
+                dot = concat(lds_read_tr(Ds + tvoff[0][db] + rbv), lds_read_tr(Ds + tvoff[1][db] + rbv));
+            if (db < DBK)
+                qt = concat(lds_read_tr(Qs + toff[0][db] + rbk), lds_read_tr(Qs + toff[1][db] + rbk));
+            if (db < DBV) dv[db] = mfma32(dot, ph, dv[db]);
+            if (db < DBK) dk[db] = mfma32(qt, sh, dk[db]);
+            if (precise) {
+                if (db < DBV) dv[db] = mfma32(dot, pl, dv[db]);
+                if (db < DBK) dk[db] = mfma32(qt, sl_, dk[db]);
+            }
+        }
+    };
+    auto pack_pv = [&](const float (&x)[8]) { return pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]); };
+    auto pack_lo = [&](const float (&x)[8]) {
+        return pack8(bf_lo(x[0]), bf_lo(x[1]), bf_lo(x[2]), bf_lo(x[3]), bf_lo(x[4]), bf_lo(x[5]), bf_lo(x[6]),
+                     bf_lo(x[7]));
+    };
+
+    // A plain step without a mask, in explicitly ordered scheduling regions (the
+    // compiler may not move instructions across a sched_barrier): one region per
+    // k-step of the S/dP products of the next step (slot sln), each with two matrix
+    // instructions, the LDS reads of the k-step two ahead, copy_k(dd) and the vector
+    // work of 16/DKM of this step's 16 P/dS elements per lane (row statistics from
+    // slot sl): P (fma, exp) of an element in its region, its dS and the bf16
+    // packing of P and dS in the next, so that the exp's latency passes under the
+    // next matrix instructions. Element e of a lane is query row 8(e/4) + 4h + e%4
+    // of the tile, in the 16-query half e/8. The dV/dK products follow (dvdk_step).
+    auto fast_sdp_pds = [&](int sl, int sln, const f32x16& sc, const f32x16& dc, f32x16& sn, f32x16& dn,
+                            bf16x8 (&ph)[2], bf16x8 (&sh)[2], auto&& copy_k) {
+        constexpr int EPK = 16 / DKM;  // elements per k-step
+        const __bf16* Qn = stage_q(sln);
+        const __bf16* Dn = stage_do(sln);
+        const float* St = stage_st(sl);
+        f32x4 xs[4];  // lse*log2e of this lane's 16 rows: row group q (rows 8q + 4h + 0..3)
+        auto rds = [&](int q) { xs[q] = *(const f32x4*)(St + 8 * q + 4 * h); };  // one group ahead
+        rds(0);
+        bf16x8 qa[DKM], da[DKM];
+        auto rd = [&](int dd) {
+            if (dd < DK) qa[dd] = lds_read8(Qn + roff[dd]);
+            if (dd < DKV) da[dd] = lds_read8(Dn + rvoff[dd]);
+        };
+        rd(0);
+        if (DKM > 1) rd(1);
+        sn = zero16();
+        dn = neg_delta(sln);  // dP - delta: the products add onto -delta
+        // Element e: P in region e / EPK (fma, exp), then dS and the bf16 packing of
+        // P and dS in the next region, so that the exp's latency passes under the
+        // next matrix instructions.
+        float pe[16];
+        uint32_t phw[8], shw[8];  // words of ph[0] (0..3) and ph[1] (4..7), likewise sh
+        auto stage2 = [&](int dd) {  // dS and packing of region dd's elements
+#pragma unroll
+            for (int u = 0; u < EPK; u += 2) {
+                const int e = dd * EPK + u;
+                const float ds0 = pe[e] * dc[e], ds1 = pe[e + 1] * dc[e + 1];  // dc holds dP - delta
+                phw[e >> 1] = pack2_bf16(pe[e], pe[e + 1]);
+                shw[e >> 1] = pack2_bf16(ds0, ds1);
+                asm volatile("" ::"v"(phw[e >> 1]), "v"(shw[e >> 1]));
+            }
+        };
+#pragma unroll
+        for (int dd = 0; dd < DKM; ++dd) {
+            if (dd + 2 < DKM) rd(dd + 2);
+            if ((dd * EPK) % 4 == 0 && dd * EPK / 4 + 1 < 4) rds(dd * EPK / 4 + 1);
+            copy_k(dd);  // a share of the copies of the stage three steps ahead
+            if (dd < DK) sn = mfma32(qa[dd], kf[dd], sn);
+            if (dd < DKV) dn = mfma32(da[dd], vf[dd], dn);
+#pragma unroll
+            for (int u = 0; u < EPK; ++u) {
+                const int e = dd * EPK + u;
+                pe[e] = fast_exp2(fmaf(sc[e], c, -xs[e >> 2][e & 3]));
+                // keeps the element's arithmetic in this region (pure arithmetic
+                // could otherwise be placed anywhere before its first use)
+                asm volatile("" ::"v"(pe[e]));
+            }
+            if (dd > 0) stage2(dd - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        stage2(DKM - 1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            ph[t2] = __builtin_bit_cast(bf16x8, u32x4{phw[4 * t2], phw[4 * t2 + 1], phw[4 * t2 + 2], phw[4 * t2 + 3]});
+            sh[t2] = __builtin_bit_cast(bf16x8, u32x4{shw[4 * t2], shw[4 * t2 + 1], shw[4 * t2 + 2], shw[4 * t2 + 3]});
+        }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS of the stage in slot sl, one region per
+    // (16-query half, 32-column block) pair, the transpose reads of the pair two
+    // ahead; hook(pp) is the caller's work placed in region pp
+    auto dvdk_step = [&](int sl, const bf16x8 (&ph)[2], const bf16x8 (&sh)[2], auto&& hook) {
+        const __bf16* Qs = stage_q(sl);
+        const __bf16* Ds = stage_do(sl);
+        constexpr int NP = 2 * DBM;  // (t2, block) pairs
+        bf16x8 dot[NP], qt[NP];
+        auto rdt = [&](int pp) {
+            const int t2 = pp / DBM, db = pp % DBM;
+            const int rbk = 16 * t2 * D, rbv = 16 * t2 * DV;
+            if (db < DBV)
+                dot[pp] = concat(lds_read_tr(Ds + tvoff[0][db] + rbv), lds_read_tr(Ds + tvoff[1][db] + rbv));
+            if (db < DBK)
+                qt[pp] = concat(lds_read_tr(Qs + toff[0][db] + rbk), lds_read_tr(Qs + toff[1][db] + rbk));
+        };
+        rdt(0);
+        rdt(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+            if (pp + 2 < NP) rdt(pp + 2);
+            const int t2 = pp / DBM, db = pp % DBM;
+            if (db < DBV) dv[db] = mfma32(dot[pp], ph[t2], dv[db]);
+            if (db < DBK) dk[db] = mfma32(qt[pp], sh[t2], dk[db]);
+            hook(pp);  // the caller's work for region pp
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    auto run = [&](int q_lo, int nq, auto exact_tag) {
+        constexpr bool MAYBE_PRECISE = decltype(exact_tag)::value;
+        const int total = G * nq;
+        const int steps = (total + kKv1Splits - 1) / kKv1Splits;
+        if (steps == 0) return;  // the same in every wave of the workgroup
+        // Q / dO copies of a pair: copy n of wave w2 fills tile rows (w2*N + n) *
+        // ROWS_PER_COPY + lane / CH, kept as this lane's byte offset within a tile of
+        // whole rows. Rows past S repeat row S-1; their lse is +inf, so their
+        // probabilities, and every term they touch, are exactly 0.
+        uint32_t qcoff[QC::N], dcoff[DC::N];
+#pragma unroll
+        for (int n = 0; n < QC::N; ++n) {
+            const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+            qcoff[n] = (uint32_t)(row * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8) * 2u;
+        }
+#pragma unroll
+        for (int n = 0; n < DC::N; ++n) {  // the same as qcoff when D == DV
+            const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
+            dcoff[n] = D == DV ? 0u : (uint32_t)(row * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8) * 2u;
+        }
+        // The (head g, query tile q_lo + r) of a step's iteration it = g nq + r,
+        // walked with counters (no division per step): one walk for the fetches,
+        // which run kKv1Ring - 1 steps ahead, one for the steps computed. Every loop
+        // iteration fetches, past the last step too (the last iteration again, into a
+        // slot no later step reads), so that every fetch is NF vector-memory
+        // operations of every wave and every wait is the same count.
+        // A walk also carries the tile's first row among all query rows (row) and
+        // among the padded rows of the row statistics (srow).
+        struct Walk {
+            int g, r;
+            long long row, srow;
+        };
+        const long long head0 = (long long)b * a.Hq + (long long)hkv * G;  // the group's first query head
+        auto walk_start = [&](Walk& w) {
+            w.g = split / nq;
+            w.r = split - w.g * nq;
+            w.row = (head0 + w.g) * S + (long long)(q_lo + w.r) * kKvBQ;
+            w.srow = (head0 + w.g) * (long long)S32 + (long long)(q_lo + w.r) * kKvBQ;
+        };
+        auto walk_next = [&](Walk& w) {
+            w.r += kKv1Splits;
+            w.row += kKv1Splits * kKvBQ;
+            w.srow += kKv1Splits * kKvBQ;
+            while (w.r >= nq) {
+                w.r -= nq;
+                ++w.g;
+                w.row += S - (long long)nq * kKvBQ;
+                w.srow += (long long)S32 - (long long)nq * kKvBQ;
+            }
+        };
+        const uint32_t lds0 = lds_addr_of(split_base);  // this pair's ring, as an LDS address
+        Walk wf;  // next step to fetch
+        walk_start(wf);
+        int fstep = 0;
+        // the last iteration, which a fetch past the end copies again
+        const long long last_row = (head0 + G - 1) * S + (long long)(q_lo + nq - 1) * kKvBQ;
+        const long long last_srow = (head0 + G - 1) * (long long)S32 + (long long)(q_lo + nq - 1) * kKvBQ;
+        // A fetch is planned once (addresses) and its NF copies issued one at a time,
+        // so that the plain loop can spread them over its matrix instructions.
+        struct Fetch {
+            const uint16_t* qb;   // first row of the Q tile
+            const uint16_t* db;   // first row of the dO tile
+            const float* stat;    // this lane's word of the row statistics
+            long long rb;         // the query head's first row
+            int qr0;              // first query row of the tile within its head
+            uint32_t st0;         // LDS address of the stage
+            bool whole;           // the tile lies inside S
+        };
+        auto fetch_plan = [&]() {
+            Fetch f;
+            f.st0 = lds0 + (uint32_t)((fstep % kKv1Ring) * T::STAGE_BYTES);
+            const bool past = wf.g >= G;  // past the last iteration: fetch the last one again
+            const long long row = past ? last_row : wf.row, srow = past ? last_srow : wf.srow;
+            f.qr0 = (q_lo + (past ? nq - 1 : wf.r)) * kKvBQ;
+            f.rb = row - f.qr0;
+            f.whole = f.qr0 + kKvBQ <= S;
+            f.qb = a.q + row * D;
+            f.db = a.dout + row * DV;
+            // the 32 rows' (lse*log2e, delta): 256 bytes, one word per lane; both waves
+            // of the pair copy the same words to the same place
+            f.stat = a.rowstat + srow * 2 + lane;
+            walk_next(wf);
+            ++fstep;
+            return f;
+        };
+        // copy k of NF; WHOLE: the tile lies inside S (known to the caller)
+        auto fetch_copy_t = [&](const Fetch& f, int k, auto whole_tag) {
+            constexpr bool WHOLE = decltype(whole_tag)::value;
+            if (k < QC::N) {
+                const int n = k;
+                if (WHOLE) {  // scalar row address plus lane offsets
+                    copy16_to_lds_sa(f.qb, qcoff[n], f.st0 + (w2 * QC::N + n) * 1024);
+                } else {
+                    const int row = (w2 * QC::N + n) * QC::ROWS_PER_COPY + lane / QC::CH;
+                    const size_t off = (f.rb + min(f.qr0 + row, S - 1)) * D + ((lane % QC::CH) ^ swz_f<D>(row)) * 8;
+                    copy16_to_lds_a(a.q + off, f.st0 + (w2 * QC::N + n) * 1024);
+                }
+            } else if (k < QC::N + DC::N) {
+                const int n = k - QC::N;
+                const uint32_t dst = f.st0 + T::QTILE * 2 + (w2 * DC::N + n) * 1024;
+                if (WHOLE) {
+                    copy16_to_lds_sa(f.db, D == DV ? qcoff[n] : dcoff[n], dst);
+                } else {
+                    const int row = (w2 * DC::N + n) * DC::ROWS_PER_COPY + lane / DC::CH;
+                    const size_t off = (f.rb + min(f.qr0 + row, S - 1)) * DV + ((lane % DC::CH) ^ swz_f<DV>(row)) * 8;
+                    copy16_to_lds_a(a.dout + off, dst);
+                }
+            } else {
+                copy4_to_lds_a(f.stat, f.st0 + (T::QTILE + T::DTILE) * 2);
+            }
+        };
+        auto fetch_all = [&](const Fetch& f) {
+            if (f.whole) {
+#pragma unroll
+                for (int k = 0; k < NF; ++k) fetch_copy_t(f, k, std::true_type{});
+            } else {
+#pragma unroll
+                for (int k = 0; k < NF; ++k) fetch_copy_t(f, k, std::false_type{});
+            }
+        };
+        auto fetch = [&]() { fetch_all(fetch_plan()); };  // plan and issue all copies
+        // Does the wave work at the step of walk w, and with which rows? It skips a
+        // step whose queries all precede its keys, or (window) all lie past the band
+        // of its last key; the mask is needed where the rows cross either edge.
+        Walk wi;  // the step computed
+        walk_start(wi);
+        auto item = [&](int& qs0, bool& need_mask) {
+            qs0 = (q_lo + wi.r) * kKvBQ;
+            need_mask = (CAUSAL && qs0 < kw0 + 31) || (W > 0 && qs0 + 31 > kw0 + W - 1);
+            const bool skip = (CAUSAL && qs0 + 31 < kw0) || qs0 >= S || (W > 0 && qs0 > kw0 + 31 + W - 1);
+            return wi.g < G && !skip;
+        };
+
+        // prologue: the first kKv1Ring - 1 fetches; wait for the first
+#pragma unroll
+        for (int p = 0; p < kKv1Ring - 1; ++p) fetch();
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm((kKv1Ring - 2) * NF));
+        barrier_lds();
+
+        if constexpr (MAYBE_PRECISE) {
+            for (int j = 0; j < steps; ++j) {
+                if (j > 0) {  // step j's stage has landed; every wave is done with step j-1's
+                    __builtin_amdgcn_s_waitcnt(vm_wait_imm((kKv1Ring - 2) * NF));
+                    barrier_lds();
+                }
+                fetch();
+                int qs0;
+                bool msk;
+                if (item(qs0, msk)) {
+                    const int sl = j % kKv1Ring;
+                    const size_t hrow = (size_t)b * a.Hq + hkv * G + wi.g;
+                    const bool precise = a.precise_all ||
+                        *(const __attribute__((address_space(4))) int*)(uintptr_t)(a.peak + hrow * nQB + q_lo + wi.r) != 0;
+                    f32x16 sv, dpv;
+                    sdp(sl, sv, dpv);
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        float pv[8], dsv[8];
+                        if (msk)
+                            pds(sl, qs0, std::true_type{}, sv, dpv, t2, pv, dsv);
+                        else
+                            pds(sl, qs0, std::false_type{}, sv, dpv, t2, pv, dsv);
+                        const bf16x8 ph = pack_pv(pv), sh = pack_pv(dsv);
+                        bf16x8 pl = ph, sl2 = sh;
+                        if (precise) {
+                            pl = pack_lo(pv);
+                            sl2 = pack_lo(dsv);
+                        }
+                        dvdk(sl, t2, ph, sh, precise, pl, sl2);
+                    }
+                }
+                walk_next(wi);
+            }
+        } else {
+            f32x16 sc, dc;  // S/dP of the current step
+            sdp(0, sc, dc);
+            // the bookkeeping of a step (its fetch's addresses, whether and how it
+            // works) is done in the previous step's dV/dK region, whose matrix
+            // instructions leave the wave's issue slots free
+            Fetch f = fetch_plan();
+            int qs0;
+            bool msk;
+            bool act = item(qs0, msk);
+            for (int j = 0; j < steps; ++j) {
+                // step j+1's stage has landed (own copies, then everyone's); every
+                // wave is done with step j-1's stage, which the next fetch refills
+                __builtin_amdgcn_s_waitcnt(vm_wait_imm((kKv1Ring - 3) * NF));
+                barrier_lds();
+                const int sl = j % kKv1Ring, sn_ = (j + 1) % kKv1Ring;
+                f32x16 sn, dn;
+                bf16x8 ph[2], sh[2];
+                if (act && !msk && f.whole) {
+                    // S/dP of step j+1 (on a stale stage past the last step, never
+                    // used) with P and dS of step j between its matrix instructions,
+                    // and the copies of the stage three steps ahead spread over them
+                    constexpr int DKM_ = DKM;
+                    fast_sdp_pds(sl, sn_, sc, dc, sn, dn, ph, sh, [&](int dd) {
+#pragma unroll
+                        for (int k = dd * NF / DKM_; k < (dd + 1) * NF / DKM_; ++k)
+                            fetch_copy_t(f, k, std::true_type{});
+                    });
+                } else {
+                    fetch_all(f);
+                    sdp(sn_, sn, dn);
+                    if (act) {  // an edge step (the mask), or the stage ahead is a ragged tile
+#pragma unroll
+                        for (int t2 = 0; t2 < 2; ++t2) {
+                            float pv[8], dsv[8];
+                            if (msk)
+                                pds(sl, qs0, std::true_type{}, sc, dc, t2, pv, dsv);
+                            else
+                                pds(sl, qs0, std::false_type{}, sc, dc, t2, pv, dsv);
+                            ph[t2] = pack_pv(pv);
+                            sh[t2] = pack_pv(dsv);
+                        }
+                    } else {  // nothing to add
+                        const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+                        ph[0] = ph[1] = sh[0] = sh[1] = z;
+                    }
+                }
+                // one copy of the dV/dK products for every path, with the next step's
+                // bookkeeping in its regions
+                dvdk_step(sl, ph, sh, [&](int pp) {
+                    if (pp == 0) {
+                        walk_next(wi);
+                        f = fetch_plan();
+                    } else if (pp == 1) {
+                        act = item(qs0, msk);
+                    }
+                });
+                sc = sn;
+                dc = dn;
+            }
+        }
+        // the ring is reused by the next loop (or the final sum): every copy has
+        // landed and every wave is done reading
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        barrier_lds();
+    };
+    run(qi_first, qi_x - qi_first, std::true_type{});
+    run(qi_x, qi_last + 1 - qi_x, std::false_type{});
+
+    // Sum the two pairs' partials (same keys, disjoint iterations) in a fixed order:
+    // pair 1 hands its dK to pair 0 and pair 0 its dV to pair 1, then each adds the
+    // other's partial to its own. Layout [w2][blocks][r][lane].
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    barrier_lds();
+    float* const xk = (float*)lds_raw;                 // pair 1's dK
+    float* const xv = xk + 2 * DBK * 16 * 64;          // pair 0's dV
+    if (split == 1) {
+#pragma unroll
+        for (int db = 0; db < DBK; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xk[((w2 * DBK + db) * 16 + r) * 64 + lane] = dk[db][r];
+    } else {
+#pragma unroll
+        for (int db = 0; db < DBV; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xv[((w2 * DBV + db) * 16 + r) * 64 + lane] = dv[db][r];
+    }
+    barrier_lds();
+    if (split == 0 && key < S) {  // dK = scale * (own + pair 1's), D wide
+        float* out = a.dk + (kvrow + key) * D;
+#pragma unroll
+        for (int db = 0; db < DBK; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = (dk[db][4 * g4 + e] + xk[((w2 * DBK + db) * 16 + 4 * g4 + e) * 64 + lane]) * a.scale;
+                *(f32x4*)(out + db * 32 + 8 * g4 + 4 * h) = v;
+            }
+    } else if (split == 1 && key < S) {  // dV = own + pair 0's, DV wide
+        float* out = a.dv + (kvrow + key) * DV;
+#pragma unroll
+        for (int db = 0; db < DBV; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = dv[db][4 * g4 + e] + xv[((w2 * DBV + db) * 16 + 4 * g4 + e) * 64 + lane];
+                *(f32x4*)(out + db * 32 + 8 * g4 + 4 * h) = v;
+            }
+    }
+}
+
+template <int D, int DV, bool CAUSAL>
+__global__ void __launch_bounds__(kKv1Threads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+dkv1_kernel(BwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    int b, hkv, kt;
+    dkv_item(a, b, hkv, kt);
+    dkv1_body<D, DV, CAUSAL>(a, lds_raw, b, hkv, kt);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel with two waves per SIMD (for D or DV = 128): 8 waves = 4 pairs,
+// each pair a double-buffered Q/dO stage, the waves in lock-step through one
+// barrier per step; the two waves on a SIMD cover each other's latencies.
+// ---------------------------------------------------------------------------
+constexpr int kKvSplits = 4;   // wave pairs that split the (head, query tile) iterations
+constexpr int kKvThreads = 64 * 2 * kKvSplits;   // two waves per SIMD
+
+template <int D, int DV>
+struct KvTile {
+    // V tile [64][DV] and per-split double-buffered Q [32][D] and dO [32][DV]
+    // tiles, all bf16 in the swizzled chunk order of swz; lse*log2e and delta per
+    // query row.
+    static constexpr int QTILE = kKvBQ * D;                          // elements
+    static constexpr int DTILE = kKvBQ * DV;
+    static constexpr int STAGE_BYTES = (QTILE + DTILE) * 2 + 2 * kKvBQ * 4;
+    static constexpr int SPLIT_BYTES = 2 * STAGE_BYTES;
+    static constexpr int VTILE_BYTES = kKvBK * DV * 2;
+    static constexpr int TILE_BYTES = VTILE_BYTES + kKvSplits * SPLIT_BYTES;
+    // final sum: two splits hand over dK and dV of both key halves
+    static constexpr int XCHG_BYTES = 2 * 2 * (D / 32 + DV / 32) * 16 * 64 * 4;
+    static constexpr int LDS_BYTES = TILE_BYTES > XCHG_BYTES ? TILE_BYTES : XCHG_BYTES;
+    using QCopy = CopyPlan<D, kKvBQ, 2>;                             // per wave of a pair
+    using DCopy = CopyPlan<DV, kKvBQ, 2>;
+    using VCopy = CopyPlan<DV, kKvBK, 2 * kKvSplits>;                // per wave
+};
 
 // Query tiles qi_first .. qi_x - 1 (of every head of the group) run in a first loop
 // whose iterations take the exact path where the dQ stage flagged their tile (or
@@ -695,7 +1320,9 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
                 // copies just issued, and so for the whole prefetch
                 const int qr = qr0 + ptid;
                 lst = qr < S ? a.lse[rb + qr] : INFINITY;
-                dlst = qr < S ? a.delta[rb + qr] : 0.0f;
+                // -delta of the row (0 past S), negated at publish; the index is below
+                // B*Hq*(2S + 64) < 2^32
+                dlst = a.rowstat[(uint32_t)hrow * (uint32_t)(nQB * kKvBQ * 2) + (uint32_t)(qr0 * 2 + kKvBQ + ptid)];
             }
             // The flag's address is the same in every lane: a scalar load through the
             // constant address space (the dQ stage wrote it before this launch) keeps it
@@ -708,7 +1335,7 @@ __device__ __forceinline__ void dkv_body(const BwdArgs& a, unsigned char* lds_ra
             if (it >= total) return;
             if (ptid < kKvBQ) {
                 stage_lse(step & 1)[ptid] = lst * kLog2e;
-                stage_dl(step & 1)[ptid] = dlst;
+                stage_dl(step & 1)[ptid] = -dlst;
             }
         };
 
@@ -900,8 +1527,14 @@ hipError_t launch_bwd_t(const BwdArgs& args, int stages, hipStream_t stream) {
     if (stages & 2) {
         const int nKB = (a.S + kKvBK - 1) / kKvBK;
         const long long kvblocks = (long long)a.B * a.Hkv * nKB;
-        constexpr int lds = KvTile<D, DV>::LDS_BYTES;
-        hipLaunchKernelGGL((dkv_kernel<D, DV, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKvThreads), lds, stream, a);
+        if constexpr (kDkvOneWave<D, DV>) {
+            constexpr int lds = Kv1Tile<D, DV>::LDS_BYTES;
+            hipLaunchKernelGGL((dkv1_kernel<D, DV, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKv1Threads), lds, stream, a);
+        } else {
+            constexpr int lds = KvTile<D, DV>::LDS_BYTES;
+            hipLaunchKernelGGL((dkv_kernel<D, DV, CAUSAL>), dim3((unsigned)kvblocks), dim3(kKvThreads), lds, stream,
+                               a);
+        }
         return hipGetLastError();
     }
     return hipSuccess;
@@ -918,8 +1551,13 @@ hipError_t setup_pair() {
     if ((e = set_lds(dq_kernel<D, DV, false>, DqTile<D, DV>::LDS_BYTES))) return e;
     if ((e = set_lds(dq_kernel<D, DV, true>, DqTile<D, DV>::LDS_BYTES))) return e;
     if ((e = set_lds(dq_win_kernel<D, DV>, DqTile<D, DV>::LDS_BYTES))) return e;
-    if ((e = set_lds(dkv_kernel<D, DV, false>, KvTile<D, DV>::LDS_BYTES))) return e;
-    return set_lds(dkv_kernel<D, DV, true>, KvTile<D, DV>::LDS_BYTES);
+    if constexpr (kDkvOneWave<D, DV>) {
+        if ((e = set_lds(dkv1_kernel<D, DV, false>, Kv1Tile<D, DV>::LDS_BYTES))) return e;
+        return set_lds(dkv1_kernel<D, DV, true>, Kv1Tile<D, DV>::LDS_BYTES);
+    } else {
+        if ((e = set_lds(dkv_kernel<D, DV, false>, KvTile<D, DV>::LDS_BYTES))) return e;
+        return set_lds(dkv_kernel<D, DV, true>, KvTile<D, DV>::LDS_BYTES);
+    }
 }
 
 template <int D, int DV>

@@ -21,6 +21,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -44,6 +45,15 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
     r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
     r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
     return r;
+}
+
+// Two fp32 values as one word of two bf16 (round to nearest even; x in the low half).
+__device__ __forceinline__ uint32_t pack2_bf16(float x, float y) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r;
+    r[0] = (__bf16)x;
+    r[1] = (__bf16)y;
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // Remainder of x after rounding it to bf16: x = bf16(x) + bf_lo(x) up to the
@@ -144,6 +154,57 @@ __device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t lane
         :
         : "v"(lane_byte_off), "s"(base), "s"(lds)
         : "memory");
+}
+// The copies above with the LDS destination given as a 32-bit LDS address (no
+// generic-to-LDS pointer conversion per copy); copy4_to_lds_a copies 4 bytes per
+// lane (global_load_lds_dword): lane i's word lands at lds_addr + 4 i.
+__device__ __forceinline__ void copy16_to_lds_sa(const void* sbase, uint32_t lane_byte_off, uint32_t lds_addr) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr);
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t base = ((uint64_t)hi << 32) | lo;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(lane_byte_off), "s"(base), "s"(lds)
+        : "memory");
+}
+__device__ __forceinline__ void copy16_to_lds_a(const void* gsrc, uint32_t lds_addr) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gsrc), "s"(lds)
+        : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds_a(const void* gsrc, uint32_t lds_addr) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, off"
+        :
+        : "v"(gsrc), "s"(lds)
+        : "memory");
+}
+// 32-bit LDS address of an LDS object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return (uint32_t)(uintptr_t)(ATTN_LDS const void*)p;
+}
+// s_waitcnt immediate that waits on the vector-memory counter alone: at most n of
+// this wave's vector-memory operations (the copies above among them) in flight.
+constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// Workgroup barrier ordering LDS accesses only: it waits for this wave's LDS
+// operations, not for its copies in flight (those are waited for by count).
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 // Wait until every copy this wave issued has landed in LDS (s_waitcnt 0). The
 // compiler sees this wait, so it also knows that every vector-memory load it

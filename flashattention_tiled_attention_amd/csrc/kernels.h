@@ -30,7 +30,10 @@ struct BwdArgs {
     float* dq;
     float* dk;
     float* dv;
-    float* delta;        // workspace: [B][Hq][S], the exact delta_i = sum_j P_ij dP_ij
+    float* rowstat;      // workspace: [B][Hq][ceil(S/32)][64]: per block of 32 query rows, the
+                         // rows' lse_i * log2(e), then their -delta_i (delta_i = sum_j P_ij
+                         // dP_ij); rows past S hold +inf and -0, so that whole blocks can be
+                         // copied
     int* peak;           // workspace: [B][Hq][ceil(S/32)], 1 where a row of the 32-row block has
                          // a probability above kPeakP (written by the dQ stage)
     int B, Hq, Hkv, S, G;

@@ -81,12 +81,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int S, int D, int causal, float scale, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes: the per-row
- * delta_i = sum_j P_ij dP_ij (fp32, [B][Hq][S]) and one int32 flag per block of
- * 32 query rows ([B][Hq][ceil(S/32)]: 1 where a row of the block has a
- * probability above 1/8, whose gradient terms then take the exact path), each
- * part 256-byte aligned. Returns 0 when the sizes are invalid (attn_bwd would
- * reject them).
+ * Bytes of device workspace attn_bwd needs for these sizes: the row statistics,
+ * per block of 32 query rows their lse_i * log2(e) then their -delta_i (delta_i =
+ * sum_j P_ij dP_ij), fp32 ([B][Hq][ceil(S/32)][64]; rows past S hold +inf and
+ * -0), and one int32 flag per block of 32 query rows ([B][Hq][ceil(S/32)]: 1
+ * where a row of the block has a probability above 1/8, whose gradient terms
+ * then take the exact path), each part 256-byte aligned. Returns 0 when the sizes
+ * are invalid (attn_bwd would reject them).
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 
@@ -115,7 +116,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * attn_bwd for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * computation, arguments and results as attn_bwd, without the workspace
- * arguments. Its workspace is a static device array of the library, 8 MiB per
+ * arguments. Its workspace is a static device array of the library, 16 MiB per
  * GPU (attn_bwd_noalloc_max_workspace_bytes()), held from the first call on a
  * device until the process ends; the call itself allocates nothing. Sizes with
  * attn_bwd_workspace_bytes() above that limit return ATTN_ERR_SCRATCH before
@@ -134,10 +135,11 @@ size_t attn_bwd_noalloc_max_workspace_bytes(void);
  * The two stages attn_bwd runs, for callers that schedule them separately
  * (attn_bwd is exactly attn_bwd_dq followed by attn_bwd_dkdv on one stream).
  * Arguments and errors are those of attn_bwd.
- *   attn_bwd_dq    writes delta_i = sum_j P_ij dP_ij and the per-block flags into
- *                  the workspace, and dq = scale * dS K (section 2.1, Table 3,
- *                  query gradient row). dk and dv are not touched.
- *   attn_bwd_dkdv  reads delta and the flags from the workspace (it must hold
+ *   attn_bwd_dq    writes the row statistics (lse_i * log2(e), delta_i =
+ *                  sum_j P_ij dP_ij) and the per-block flags into the workspace,
+ *                  and dq = scale * dS K (section 2.1, Table 3, query gradient
+ *                  row). dk and dv are not touched.
+ *   attn_bwd_dkdv  reads the row statistics and the flags from the workspace (it must hold
  *                  attn_bwd_dq's result for the same inputs) and writes
  *                  dk = scale * dS^T Q
  *                  (Table 3, key gradient row) and dv = P^T dO, each summed over
@@ -183,7 +185,7 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
  * window; window >= 1 needs causal != 0 (else, or for window < 0,
  * ATTN_ERR_WINDOW). Scores are q . k over D columns, so the usual scale is
  * 1/sqrt(D). attn_bwd_vdim's workspace is attn_bwd_workspace_bytes(B, Hq, Hkv,
- * S, D) bytes (delta has one value per query row whatever Dv is), and it
+ * S, D) bytes (its row statistics do not depend on Dv), and it
  * needs o and lse from attn_fwd_vdim with the same arguments. With Dv == D these
  * are attn_fwd / attn_bwd (window = 0) and attn_fwd_window / attn_bwd_window.
  * Every other rule, layout and error is that of attn_fwd and attn_bwd, with

@@ -266,7 +266,7 @@ def test_noalloc_validates_before_any_call():
     workspace exceeds its static scratch, before touching the GPU."""
     lib = fa.load_library()
     limit = lib.attn_bwd_noalloc_max_workspace_bytes()
-    assert limit == 8 << 20
+    assert limit == 16 << 20
     assert bwd_noalloc(ptrs={"dq": None}) == fa.ATTN_ERR_NULL
     assert bwd_noalloc(ptrs={"dv": MIS}) == fa.ATTN_ERR_ALIGN
     assert bwd_noalloc(Hq=6, Hkv=4) == fa.ATTN_ERR_GQA

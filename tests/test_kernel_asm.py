@@ -27,7 +27,7 @@ HOT = {
     "attn_fwd.hip": ["fwd_kernelILi128ELi128ELb1E", "fwd_kernelILi64ELi64ELb0E", "fwd_kernelILi64ELi64ELb1E",
                      "fwd_kernelILi128ELi64ELb1E", "fwd_win_kernelILi128ELi128E"],
     "attn_bwd.hip": ["dq_kernelILi128ELi128ELb1E", "dq_kernelILi128ELi128ELb0E", "dkv_kernelILi128ELi128ELb1E",
-                     "dkv_kernelILi128ELi128ELb0E", "dq_kernelILi64ELi64ELb0E", "dkv_kernelILi64ELi64ELb0E",
+                     "dkv_kernelILi128ELi128ELb0E", "dq_kernelILi64ELi64ELb0E", "dkv1_kernelILi64ELi64ELb0E",
                      "dq_kernelILi128ELi64ELb1E", "dkv_kernelILi128ELi64ELb1E", "dq_win_kernelILi128ELi128E"],
     "attn_sparse.hip": ["sparse_fwd_kernelILi128E", "sparse_dq_kernelILi128E"],
 }
@@ -135,12 +135,15 @@ def dims(name):
     return int(m.group(1)), int(m.group(2))
 
 
-def is_plain_loop(name, mfmas):
-    """Whether a tile loop with this many MFMAs belongs to a plain (not exact-path) body.
-    The dQ kernels' plain loop runs one or two key tiles per iteration, each with
-    D/16 + Dv/16 score and dP MFMAs and 2 D/32 dQ MFMAs per 32-key half; their exact
-    bodies have a pass without the dQ MFMAs and one with twice as many, so the counts
-    never coincide."""
+def is_plain_loop(name, mfmas, seg=()):
+    """Whether a tile loop with this many MFMAs (and these lines) belongs to a plain
+    (not exact-path) body. The dQ kernels' plain loop runs one or two key tiles per
+    iteration, each with D/16 + Dv/16 score and dP MFMAs and 2 D/32 dQ MFMAs per
+    32-key half; their exact bodies have a pass without the dQ MFMAs and one with
+    twice as many, so the counts never coincide. The dK/dV kernels' exact loop is the
+    one that reads the dQ stage's per-tile flag with a scalar load."""
+    if "dkv" in name:
+        return not any(x.strip().startswith("s_load") for x in seg)
     if "dq_" in name and "sparse" not in name:
         D, Dv = dims(name)
         per_tile = 2 * (D // 16 + Dv // 16 + 2 * (D // 32))
@@ -169,7 +172,7 @@ def test_no_spill_reload_in_tile_loops(asm):
             # run on the few rows that see at most 128 keys
             mfmas = sum("v_mfma" in body[k] for k in range(a, b + 1))
             reloads = [body[k].strip() for k in range(a, b + 1) if "scratch_load" in body[k]]
-            assert not reloads or not is_plain_loop(name, mfmas), \
+            assert not reloads or not is_plain_loop(name, mfmas, body[a:b + 1]), \
                 "%s: spill reload in a plain tile loop (%d MFMAs): %s" % (name, mfmas, reloads[:3])
 
 
@@ -180,15 +183,21 @@ def test_vmcnt_waits_only_before_barriers(asm):
         for a, b in tile_loops(body):
             parents = [(c, d) for c, d in all_loops if c <= a and d >= b and (c, d) != (a, b)]
             parent = min(parents, key=lambda cd: cd[1] - cd[0]) if parents else None
-            if not is_plain_loop(name, mfmas(a, b)) or (parent and not is_plain_loop(name, mfmas(*parent))):
+            if not is_plain_loop(name, mfmas(a, b), body[a:b + 1]) or \
+                    (parent and not is_plain_loop(name, mfmas(*parent), body[parent[0]:parent[1] + 1])):
                 continue  # an exact-path body (split operands; its spills are allowed)
             for k in range(a, b + 1):
-                if "vmcnt" not in body[k] or "s_waitcnt" not in body[k]:
+                m = re.search(r"s_waitcnt.*vmcnt\((\d+)\)", body[k])
+                if not m:
+                    continue
+                if int(m.group(1)) > 0:
+                    # a wait by count (the dK/dV stage ring: later copies stay in
+                    # flight); only a full wait could stall on the prefetch
                     continue
                 nxt = [body[j].strip() for j in range(k + 1, min(k + 12, len(body)))
                        if body[j].strip() and not body[j].strip().startswith(";")]
                 ok = any(x.startswith("s_barrier") for x in nxt[:3]) or \
-                    any(x.startswith(("ds_write", "v_mul_f32")) for x in nxt[:2])  # dK/dV row statistics
+                    any(x.startswith(("ds_write", "v_mul_f32", "v_xor_b32")) for x in nxt[:3])  # row statistics
                 assert ok, "%s: vector-memory wait inside a tile loop not before a barrier: %s -> %s" % (
                     name, body[k].strip(), nxt[:3])
 
@@ -202,7 +211,8 @@ def test_m0_written_only_by_tile_copies(asm):
                 assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", l.strip()), \
                     "%s: unexpected M0 use: %s" % (src, l.strip())
                 nxt = [x.strip() for x in lines[k + 1:k + 3]]
-                assert nxt[0] == "s_nop 0" and nxt[1].startswith("global_load_lds_dwordx4"), (src, nxt)
+                assert nxt[0] == "s_nop 0" and nxt[1].startswith(("global_load_lds_dwordx4", "global_load_lds_dword ")), \
+                    (src, nxt)
 
 
 def test_scalar_copy_bases_are_not_sign_extended(asm):
