@@ -85,7 +85,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * per block of 32 query rows their lse_i * log2(e) then their -delta_i (delta_i =
  * sum_j P_ij dP_ij), fp32 ([B][Hq][ceil(S/32)][64]; rows past S hold +inf and
  * -0), and one int32 flag per block of 32 query rows ([B][Hq][ceil(S/32)]: 1
- * where a row of the block has a probability above 1/8, whose gradient terms
+ * where a row of the block has a probability above 1/4, whose gradient terms
  * then take the exact path), each part 256-byte aligned. Returns 0 when the sizes
  * are invalid (attn_bwd would reject them).
  */
