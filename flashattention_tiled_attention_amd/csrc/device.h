@@ -114,6 +114,15 @@ struct CopyPlan {
     static_assert(N >= 1 && N * ROWS_PER_COPY * WAVES == ROWS, "copy split");
 };
 
+// 32-bit LDS address of an LDS object named by a generic pointer: the generic
+// address of LDS is the aperture base (zero in its low 32 bits) plus the LDS
+// offset, so the low half is the LDS address. (An address-space cast would give
+// the same value but tests the pointer for null first, which costs a 64-bit
+// compare and a select in scalar registers for every copy.)
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
 // Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
 // lane i's 16 bytes land at lds_wave_base + 16 i. lds_wave_base must be the same
 // for every lane of the wave. Completion is tracked by vmcnt only: the caller
@@ -126,7 +135,7 @@ struct CopyPlan {
 // across the copy. M0 (the LDS address of the copy) cannot be named as a clobber
 // (the compiler reserves it); these kernels keep no value of their own in M0.
 __device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_base) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS void*)lds_wave_base);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_wave_base));
     asm volatile(
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
@@ -140,7 +149,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_b
 // per-lane offsets are fixed then needs no vector address arithmetic per step.
 // sbase must be the same for every lane of the wave.
 __device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t lane_byte_off, void* lds_wave_base) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS void*)lds_wave_base);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_wave_base));
     // (readfirstlane returns a signed int: each half is taken back to 32 unsigned
     // bits before widening, or a low half with bit 31 set would fill the high half)
     const uint64_t b = (uint64_t)(uintptr_t)sbase;
@@ -191,10 +200,6 @@ __device__ __forceinline__ void copy4_to_lds_a(const void* gsrc, uint32_t lds_ad
         :
         : "v"(gsrc), "s"(lds)
         : "memory");
-}
-// 32-bit LDS address of an LDS object.
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-    return (uint32_t)(uintptr_t)(ATTN_LDS const void*)p;
 }
 // s_waitcnt immediate that waits on the vector-memory counter alone: at most n of
 // this wave's vector-memory operations (the copies above among them) in flight.
