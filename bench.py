@@ -331,6 +331,8 @@ def main():
                     help="run only the LDS-to-register transpose microbenchmark (one JSON line)")
     ap.add_argument("--mfma-rate", action="store_true",
                     help="run only the matrix-core rate microbenchmark (one JSON line)")
+    ap.add_argument("--issue-rates", action="store_true",
+                    help="run only the vector-issue and copy-issue microbenchmark (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path; use --gpus 1",
@@ -351,6 +353,13 @@ def main():
         print(json.dumps({"metric": "v_mfma_f32_32x32x16_bf16 rate with operands in registers, whole chip",
                           "unit": "TFLOP/s", "device": "MI355X (gfx950)", "peak": PEAK_BF16_TFLOPS,
                           "runs": mfma_rate.table()}), flush=True)
+        return
+
+    if args.issue_rates:
+        from flashattention_tiled_attention_amd import issue_rate
+        print(json.dumps({"metric": "cycles a wave spends issuing vector instructions and tile copies",
+                          "unit": "shader cycles", "device": "MI355X (gfx950)", "runs": issue_rate.table()}),
+              flush=True)
         return
 
     import torch

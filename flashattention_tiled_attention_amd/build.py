@@ -1,6 +1,6 @@
-"""Build the HIP attention library (libattn.so) and the two microbenchmarks, the
-LDS transpose one (liblds_transpose.so) and the matrix-core rate one
-(libmfma_rate.so), in-tree for gfx950 with hipcc."""
+"""Build the HIP attention library (libattn.so) and the three microbenchmarks, the
+LDS transpose one (liblds_transpose.so), the matrix-core rate one (libmfma_rate.so)
+and the instruction-issue one (libissue_rate.so), in-tree for gfx950 with hipcc."""
 import os
 import subprocess
 import sys
@@ -16,6 +16,8 @@ LDS_LIB = os.path.join(HERE, "liblds_transpose.so")
 LDS_SOURCES = ["lds_transpose.hip"]
 MFMA_LIB = os.path.join(HERE, "libmfma_rate.so")
 MFMA_SOURCES = ["mfma_rate.hip"]
+ISSUE_LIB = os.path.join(HERE, "libissue_rate.so")
+ISSUE_SOURCES = ["issue_rate.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -32,12 +34,12 @@ def _compile(src, obj, extra):
 
 
 def build(extra=None, verbose=False):
-    """Compile every source and link libattn.so, liblds_transpose.so and libmfma_rate.so;
+    """Compile every source and link libattn.so and the three microbenchmark libraries;
     raises on any compiler error. Returns the path of libattn.so."""
     extra = list(extra or [])
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    srcs = SOURCES + LDS_SOURCES + MFMA_SOURCES
+    srcs = SOURCES + LDS_SOURCES + MFMA_SOURCES + ISSUE_SOURCES
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in srcs]
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
         results = list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(srcs, objs)))
@@ -46,8 +48,10 @@ def build(extra=None, verbose=False):
             sys.stderr.write(err + "\n")
         if rc:
             raise RuntimeError("hipcc failed: " + " ".join(cmd))
-    n1, n2 = len(SOURCES), len(SOURCES) + len(LDS_SOURCES)
-    for lib, members in ((LIB, objs[:n1]), (LDS_LIB, objs[n1:n2]), (MFMA_LIB, objs[n2:])):
+    n1 = len(SOURCES)
+    n2 = n1 + len(LDS_SOURCES)
+    n3 = n2 + len(MFMA_SOURCES)
+    for lib, members in ((LIB, objs[:n1]), (LDS_LIB, objs[n1:n2]), (MFMA_LIB, objs[n2:n3]), (ISSUE_LIB, objs[n3:])):
         tmp = lib + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + members
         subprocess.run(cmd, check=True)

@@ -63,6 +63,24 @@ def test_mfma_rate_library_exports_its_header():
     assert lib.mfma_rate_bench(MIS, 1, 1, ctypes.byref(ms), P, P, None) == 2
 
 
+def test_issue_rate_library_exports_its_header():
+    from flashattention_tiled_attention_amd import issue_rate
+    text = open(os.path.join(ROOT, "include", "issue_rate.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b([a-z]+_issue_bench)\s*\(", text)))
+    assert names == ["copy_issue_bench", "valu_issue_bench"]
+    lib = issue_rate.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    # argument checks happen before any HIP call
+    assert lib.valu_issue_bench(4, 1, 1, 0.5, P, P, None) == 2        # no such mode
+    assert lib.valu_issue_bench(0, 0, 1, 0.5, P, P, None) == 2        # no workgroups
+    assert lib.valu_issue_bench(0, 1, 1, 0.5, None, P, None) == 2
+    assert lib.copy_issue_bench(P, 1, 9, 1, 1, P, P, None) == 2       # more than 8 copies
+    assert lib.copy_issue_bench(P, 1, 1, 0, 1, P, P, None) == 2       # no issuing wave
+    assert lib.copy_issue_bench(MIS, 1, 1, 1, 1, P, P, None) == 2     # misaligned source
+
+
 def test_status_strings():
     for code in range(0, 13):
         s = fa.attn_status_str(code)
