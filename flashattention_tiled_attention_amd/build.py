@@ -23,10 +23,17 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
+# Per-source flags. fwd1_kernel runs one wave per SIMD, so it may use 512 registers;
+# for such kernels the compiler otherwise puts every MFMA accumulator in AGPRs, and
+# the softmax then reads each score out of them with an extra instruction. This flag
+# makes it keep MFMA results in VGPRs (spilling cold values to AGPRs). It changes
+# no other kernel of that file: kernels with two waves per SIMD (256 registers)
+# already get that form.
+SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src, obj, extra):
-    cmd = [HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only target feature; that warning is harmless
     noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]

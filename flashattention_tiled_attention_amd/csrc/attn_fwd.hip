@@ -10,7 +10,10 @@
 //
 // One workgroup = 8 waves = one tile of 256 query rows of one (batch, head);
 // each wave owns 32 rows (with a sliding window, fwd_win_kernel gives the 8
-// waves several query heads of one kv head instead, see there). Per key tile j
+// waves several query heads of one kv head instead, see there). When queries,
+// keys and values are all 128 wide, the running-maximum slack is on and S is a
+// multiple of 256, fwd1_kernel (further down) takes the same tiles with 4 waves
+// of 64 rows each instead. Per key tile j
 // (64 keys; 128 when queries, keys and values are all 64 wide), a wave does
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in registers (B)
 //                      -> every lane holds one query column and 32 of its keys,
@@ -554,6 +557,494 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_win_kernel(FwdArgs a) {
         fwd_body<D, DV, true, false>(a, smem, b, hq, q0, q0 + BQ - 1, row0);
 }
 
+// ---------------------------------------------------------------------------
+// fwd1_kernel: queries, keys and values 128 wide, with the running-maximum slack
+// on (max_slack >= 1) and S a multiple of 256. Four waves, one per SIMD, take
+// the same 256 query rows per workgroup as fwd_kernel, each wave 64 of them in two
+// 32-row blocks (rows q0 + 32 w + 128 r, r = 0, 1). Every K and V^T operand a
+// wave reads from LDS then feeds two MFMAs, one per row block, which halves the
+// LDS operand traffic per MFMA against 32 rows per wave; the 512 registers of a
+// SIMD hold both blocks' scores, probabilities and O accumulators.
+//
+// With one wave per SIMD there is no partner wave whose MFMAs could cover the
+// softmax, so the wave interleaves the two itself, a 32-key block at a time. Each
+// step handles key tile j + 1's scores and tile j's P V product in two regions:
+//   region 0: S^T of block 0 of tile j+1 and P V of block 0 of tile j, under the
+//             softmax of block 1 of tile j;
+//   region 1: S^T of block 1 of tile j+1 and P V of block 1 of tile j, under the
+//             softmax of block 0 of tile j+1;
+// a region's 16 score and 16 P V MFMAs (both row blocks) go out over 8 slots,
+// each with its share of the exponentials and bf16 packing, and the step's tile
+// copies go out one per slot of region 0.
+//
+// The loop never rescales O. Each row's reference maximum m is taken exactly
+// from the first key tile, and the probabilities exp2(s c - m) of the later
+// tiles are only summed. After the loop each lane's sum is checked against
+// 2^(slack-1) times the number of 32-key blocks: it passes whenever every block
+// would have passed fwd_body's per-tile test (each lane's sum of a block at most
+// 2^(slack-1)), and passing bounds every probability by the lane's sum, so P
+// stays exact in bf16 and l and O stay far from overflow. Where a sum fails (a
+// score far above m, an overflow, a NaN) the wave raises a flag in LDS and the
+// whole workgroup recomputes its rows in fwd1_careful, which moves the maximum as
+// fwd_body does and splits P into a bf16 high part and remainder. Keeping the
+// conditional rescale of all 128 O registers out of the loop is what keeps the
+// loop free of register copies and spills. The first query tile of a causal
+// problem (rows that see at most 256 keys) always takes fwd1_careful, as it takes
+// fwd_body's exact instance in fwd_kernel.
+//
+// The build compiles this file with MFMA results in VGPRs (build.py): a kernel
+// that may use 512 registers otherwise gets every accumulator in AGPRs, and the
+// softmax would need an extra instruction to read each score out.
+// ---------------------------------------------------------------------------
+constexpr int kF1Waves = 4;
+constexpr int kF1Threads = 64 * kF1Waves;
+constexpr int kF1BK = 64;  // keys per LDS tile
+
+struct F1Tile {
+    static constexpr int D = 128, DV = 128;
+    static constexpr int KTILE = kF1BK * D;  // elements
+    static constexpr int VTILE = kF1BK * DV;
+    static constexpr int RING_BYTES = 2 * (KTILE + VTILE) * 2;  // 2 K slots + 2 V slots
+    static constexpr int LDS_BYTES = RING_BYTES + 16;           // + the workgroup's flag word
+    using KCopy = CopyPlan<D, kF1BK, kF1Waves>;
+    using VCopy = CopyPlan<DV, kF1BK, kF1Waves>;
+};
+
+// Per-lane offsets shared by both bodies: copy source offsets (bytes within a
+// tile) and LDS read offsets (elements within a slot), as in fwd_body.
+struct F1Lane {
+    static constexpr int D = F1Tile::D, DV = F1Tile::DV, DK = D / 16, DB = DV / 32;
+    using KC = F1Tile::KCopy;
+    using VC = F1Tile::VCopy;
+    uint32_t kcoff[KC::N], vcoff[VC::N];
+    int koff[DK], voff[2][DB];
+    __device__ __forceinline__ F1Lane(int wave, int lane) {
+        const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int n = 0; n < KC::N; ++n) {
+            const int row = (wave * KC::N + n) * KC::ROWS_PER_COPY + lane / KC::CH;
+            kcoff[n] = (uint32_t)(row * D + ((lane % KC::CH) ^ swz_f<D>(row)) * 8) * 2u;
+        }
+#pragma unroll
+        for (int n = 0; n < VC::N; ++n) {
+            const int row = (wave * VC::N + n) * VC::ROWS_PER_COPY + lane / VC::CH;
+            vcoff[n] = (uint32_t)(row * DV + ((lane % VC::CH) ^ swz_f<DV>(row)) * 8) * 2u;
+        }
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) koff[dk] = swz<D>(l32, dk * 16 + 8 * h);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                voff[hf][db] = swz<DV>(4 * h + ((lane & 15) >> 2) + 8 * hf,
+                                       db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    }
+};
+
+// Adds -inf to the scores of keys past this lane's query row: element e of a
+// 32-key block starting at key k0 holds key k0 + 8 (e / 4) + 4 h + e % 4.
+__device__ __forceinline__ void f1_mask(f32x16& s, int k0, int qrow, int h) {
+    const int lim = qrow - k0 - 4 * h;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int off = 8 * (e >> 2) + (e & 3);
+        s[e] += __int_as_float(((lim - off) >> 31) & (int)0xff800000u);
+    }
+}
+
+// Exact body: each wave takes its two row blocks one after the other, 32 rows at
+// a time. Per key tile all waves copy K and V into slot 0 of the ring; then the
+// scores, the row maximum moved as fwd_body moves it, the probabilities split
+// into bf16 high parts and remainders, and the P V product on both.
+template <bool CAUSAL>
+__device__ __forceinline__ void fwd1_careful(const FwdArgs& a, __bf16* smem, int b, int hq, int q0) {
+    using T = F1Tile;
+    constexpr int D = T::D, DV = T::DV, BK = kF1BK, DK = D / 16, DB = DV / 32, NT = BK / 16;
+    using KC = T::KCopy;
+    using VC = T::VCopy;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int S = a.S;
+    const size_t qrows = ((size_t)b * a.Hq + hq) * (size_t)S;
+    const size_t kvrows = ((size_t)b * a.Hkv + hq / a.G) * (size_t)S;
+    const uint16_t* Kp = a.k + kvrows * D;
+    const uint16_t* Vp = a.v + kvrows * DV;
+    const float c = a.scale_log2;
+    const F1Lane ln(wave, lane);
+    const __bf16* Ks = smem;
+    const __bf16* Vs = smem + T::KTILE;
+    const uint32_t kdst = lds_addr_of(smem) + wave * KC::N * 1024;
+    const uint32_t vdst = lds_addr_of(smem + T::KTILE) + wave * VC::N * 1024;
+    for (int r = 0; r < 2; ++r) {
+        const int row0 = q0 + 128 * r + 32 * wave;
+        const int qrow = row0 + l32;
+        bf16x8 qf[DK];
+        const u32x4* src = (const u32x4*)(a.q + (qrows + qrow) * D + 8 * h);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            u32x4 t = src[2 * dk];
+            t ^= a.q_sign;
+            qf[dk] = __builtin_bit_cast(bf16x8, t);
+        }
+        // tiles the workgroup's rows of this pass see, and this wave's rows
+        const int jend = CAUSAL ? (q0 + 128 * r + 127) / BK + 1 : S / BK;
+        const int wjend = CAUSAL ? (row0 + 31) / BK + 1 : jend;
+        f32x16 oacc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = zero16();
+        float m = -1e30f, l = 0.0f;
+        for (int j = 0; j < jend; ++j) {
+            barrier_lds();  // every wave is done with the previous tile
+            const uint16_t* kb = Kp + (size_t)j * BK * D;
+            const uint16_t* vb = Vp + (size_t)j * BK * DV;
+#pragma unroll
+            for (int n = 0; n < KC::N; ++n) copy16_to_lds_sa(kb, ln.kcoff[n], kdst + n * 1024);
+#pragma unroll
+            for (int n = 0; n < VC::N; ++n) copy16_to_lds_sa(vb, ln.vcoff[n], vdst + n * 1024);
+            wait_copies();
+            barrier_lds();
+            if (j >= wjend) continue;  // past this wave's diagonal (wave-uniform)
+            f32x16 sc[2] = {zero16(), zero16()};
+#pragma unroll
+            for (int dk = 0; dk < DK; ++dk)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+                    sc[kb2] = mfma32(lds_read8(Ks + ln.koff[dk] + kb2 * 32 * D), qf[dk], sc[kb2]);
+            if (CAUSAL && j == wjend - 1) {
+                f1_mask(sc[0], j * BK, qrow, h);
+                f1_mask(sc[1], j * BK + 32, qrow, h);
+            }
+            float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
+            const float mt = halves_max(mx) * c;
+            if (__any(mt > m + a.max_slack)) {
+                const float mnew = fmaxf(m, mt);
+                const float alpha = fast_exp2(m - mnew);
+                m = mnew;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            }
+            bf16x8 pk[NT], pl[NT];
+            float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = fast_exp2(fmaf(sc[t >> 1][8 * (t & 1) + e], c, -m));
+                    rs[e & 3] += p[e];
+                }
+                pk[t] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+                pl[t] = pack8(bf_lo(p[0]), bf_lo(p[1]), bf_lo(p[2]), bf_lo(p[3]), bf_lo(p[4]), bf_lo(p[5]),
+                              bf_lo(p[6]), bf_lo(p[7]));
+            }
+            l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const bf16x8 vt = concat(lds_read_tr(Vs + ln.voff[0][db] + 16 * t * DV),
+                                             lds_read_tr(Vs + ln.voff[1][db] + 16 * t * DV));
+                    oacc[db] = mfma32(vt, pk[t], oacc[db]);
+                    oacc[db] = mfma32(vt, pl[t], oacc[db]);
+                }
+        }
+        const float lt = halves_sum(l);
+        const float inv = 1.0f / lt;
+        uint16_t* op = a.o + (qrows + qrow) * DV;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = db * 32 + 8 * g4 + 4 * h;
+                *(bf16x4*)(op + d) = pack4(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
+                                           oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+            }
+        if (h == 0) a.lse[qrows + qrow] = (m + log2f(lt)) * 0.69314718055994531f;
+    }
+}
+
+// Pipelined body; returns false (workgroup-uniform, nothing written) when some
+// wave's probabilities left the bound, true once O and lse are written.
+template <bool CAUSAL>
+__device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b, int hq, int q0) {
+    using T = F1Tile;
+    constexpr int D = T::D, DV = T::DV, BK = kF1BK;
+    constexpr int DK = D / 16;    // k-steps of a block's S^T
+    constexpr int DB = DV / 32;   // 32-column blocks of O^T
+    constexpr int NT = BK / 16;   // 16-key P V steps of a tile
+    constexpr int NPV = 2 * DB;   // P V MFMAs of a key block per row block
+    constexpr int NSL = DK > NPV ? DK : NPV;  // slots of a region
+    constexpr int EPS = 16 / NSL; // softmax elements per row block per slot
+    using KC = T::KCopy;
+    using VC = T::VCopy;
+    constexpr int NCP = KC::N + VC::N;  // copies per wave per step
+    static_assert(16 % NSL == 0 && EPS % 2 == 0 && NCP <= NSL, "region slots");
+    static_assert(DK == NSL && NPV == NSL, "every slot has one k-step and one P V step");
+    const int S = a.S;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const size_t qrows = ((size_t)b * a.Hq + hq) * (size_t)S;
+    const size_t kvrows = ((size_t)b * a.Hkv + hq / a.G) * (size_t)S;
+    const uint16_t* Kp = a.k + kvrows * D;
+    const uint16_t* Vp = a.v + kvrows * DV;
+    const int qrow0 = q0 + 32 * wave + l32;  // row of block r: qrow0 + 128 r
+    const float c = a.scale_log2;
+    int* const flag = (int*)((char*)smem + T::RING_BYTES);
+
+    bf16x8 qf[2][DK];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const u32x4* src = (const u32x4*)(a.q + (qrows + qrow0 + 128 * r) * D + 8 * h);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            u32x4 t = src[2 * dk];
+            t ^= a.q_sign;
+            qf[r][dk] = __builtin_bit_cast(bf16x8, t);
+        }
+    }
+    // Tiles of the workgroup; a causal one masks tiles from q0 / BK on (its
+    // first row's tile; earlier tiles are visible to all of its rows).
+    const int nK = CAUSAL ? q0 / BK + kFwdBQ / BK : S / BK;
+    __bf16* const Kring = smem;
+    __bf16* const Vring = smem + 2 * T::KTILE;
+    const uint32_t kbase = lds_addr_of(Kring) + wave * KC::N * 1024;
+    const uint32_t vbase = lds_addr_of(Vring) + wave * VC::N * 1024;
+    const F1Lane ln(wave, lane);
+    // copy k of the step's NCP: K_jk into K slot ks, V_jv into V slot vs
+    auto copy_one = [&](int k, int ks, int jk, int vs, int jv) {
+        if (k < KC::N)
+            copy16_to_lds_sa(Kp + (size_t)jk * BK * D, ln.kcoff[k], kbase + (uint32_t)(ks * T::KTILE * 2 + k * 1024));
+        else
+            copy16_to_lds_sa(Vp + (size_t)jv * BK * DV, ln.vcoff[k - KC::N],
+                             vbase + (uint32_t)(vs * T::VTILE * 2 + (k - KC::N) * 1024));
+    };
+
+    f32x16 oacc[2][DB];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[r][db] = zero16();
+    // m: each row's reference maximum; l4: four partial sums of this lane's share
+    // of its probabilities, carried through the loop
+    float m[2], l4[2][4];
+
+    // Sb[r][kb]: scores of key block kb of the current tile for row block r;
+    // Pb[r][t]: the bf16 probabilities of its 16-key step t.
+    f32x16 Sb[2][2];
+    bf16x8 Pb[2][NT];
+    auto qk_op = [&](const __bf16* Ks, int kb, int dk) { return lds_read8(Ks + ln.koff[dk] + kb * 32 * D); };
+    auto pv_op = [&](const __bf16* Vs, int t, int db) {
+        return concat(lds_read_tr(Vs + ln.voff[0][db] + 16 * t * DV), lds_read_tr(Vs + ln.voff[1][db] + 16 * t * DV));
+    };
+    // One region: the DK k-steps of S^T of key block kb of the tile in Ks (when
+    // WITH_QK) and the NPV P V MFMAs of key block pb (V tile in Vs), both row
+    // blocks, one k-step or P V step per slot, with the softmax of key block sb
+    // (of tile jt, masked when MASK) spread over the slots and copies k0 .. of the
+    // step issued one per slot.
+    auto region = [&](auto with_qk, auto mask, const __bf16* Ks, int kb, const __bf16* Vs, int pb, int sb, int jt,
+                      auto&& copy, int k0) __attribute__((always_inline)) {
+        constexpr bool WITH_QK = decltype(with_qk)::value;
+        constexpr bool MASK = decltype(mask)::value;
+        if (MASK) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) f1_mask(Sb[r][sb], jt * BK + 32 * sb, qrow0 + 128 * r, h);
+        }
+        float pe[2][16];
+        uint32_t pw[2][8];
+        bf16x8 kr[DK], vr[NPV];
+        if (WITH_QK) {
+            Sb[0][kb] = zero16();
+            Sb[1][kb] = zero16();
+            kr[0] = qk_op(Ks, kb, 0);
+        }
+        vr[0] = pv_op(Vs, 2 * pb, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+            if (WITH_QK && i + 1 < DK) kr[i + 1] = qk_op(Ks, kb, i + 1);
+            if (i + 1 < NPV) vr[i + 1] = pv_op(Vs, 2 * pb + (i + 1) / DB, (i + 1) % DB);
+            copy(k0 + i);
+            // the P V product first: its operand was read after the K operand, so
+            // the one wait for it covers both
+            if (i < NPV) {
+                oacc[0][i % DB] = mfma32(vr[i], Pb[0][2 * pb + i / DB], oacc[0][i % DB]);
+                oacc[1][i % DB] = mfma32(vr[i], Pb[1][2 * pb + i / DB], oacc[1][i % DB]);
+            }
+            if (WITH_QK && i < DK) {
+                Sb[0][kb] = mfma32(kr[i], qf[0][i], Sb[0][kb]);
+                Sb[1][kb] = mfma32(kr[i], qf[1][i], Sb[1][kb]);
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+#pragma unroll
+                for (int u = 0; u < EPS; ++u) {
+                    const int e = EPS * i + u;
+                    pe[r][e] = fast_exp2(fmaf(Sb[r][sb][e], c, -m[r]));
+                    l4[r][e & 3] += pe[r][e];
+                    asm volatile("" ::"v"(pe[r][e]), "v"(l4[r][e & 3]));
+                }
+#pragma unroll
+                for (int u = 0; u < EPS; u += 2) {
+                    const int e = EPS * i + u;
+                    pw[r][e >> 1] = pack2_bf16(pe[r][e], pe[r][e + 1]);
+                    asm volatile("" ::"v"(pw[r][e >> 1]));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+                Pb[r][2 * sb + t2] = __builtin_bit_cast(
+                    bf16x8, u32x4{pw[r][4 * t2], pw[r][4 * t2 + 1], pw[r][4 * t2 + 2], pw[r][4 * t2 + 3]});
+    };
+    auto no_copy = [&](int) {};
+    using False = std::integral_constant<bool, false>;
+    using True = std::integral_constant<bool, true>;
+
+    // prologue: K_0, K_1 and V_0; tile 0's scores; m from its 64 keys; block 0's
+    // probabilities
+    if (tid == 0) *flag = 0;
+#pragma unroll
+    for (int k = 0; k < NCP; ++k) copy_one(k, 0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < KC::N; ++k) copy_one(k, 1, 1, 0, 0);
+    wait_copies();
+    barrier_lds();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        Sb[r][0] = zero16();
+        Sb[r][1] = zero16();
+    }
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 kf = qk_op(Kring, kb, dk);
+            Sb[0][kb] = mfma32(kf, qf[0][dk], Sb[0][kb]);
+            Sb[1][kb] = mfma32(kf, qf[1][dk], Sb[1][kb]);
+        }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        float mx = fmaxf(Sb[r][0][0], Sb[r][1][0]);
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(Sb[r][0][e], Sb[r][1][e]));
+        m[r] = halves_max(mx) * c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l4[r][e] = 0.0f;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(fmaf(Sb[r][0][8 * t2 + e], c, -m[r]));
+                l4[r][e & 3] += p[e];
+            }
+            Pb[r][t2] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        }
+    }
+    barrier_lds();  // every wave is done with K slot 0 before K_2 goes there
+
+    // Step j (0 <= j <= nK-2): copies of K_{j+2} (past the end the last tile
+    // again, into a slot no later step reads) and V_{j+1} into the slots of K_j and
+    // V_{j-1}; tile j's P V and block-1 softmax, tile j+1's scores and block-0
+    // softmax. The slot parity is a template constant.
+    auto step = [&](int j, auto par, auto mask) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;  // j & 1
+        const int jk = min(j + 2, nK - 1), jv = j + 1;
+        auto copy = [&](int k) {
+            if (k < NCP) copy_one(k, P, jk, P ^ 1, jv);
+        };
+        const __bf16* Ks = Kring + (P ^ 1) * T::KTILE;
+        const __bf16* Vs = Vring + P * T::VTILE;
+        region(True{}, mask, Ks, 0, Vs, 0, 1, j, copy, 0);
+        region(True{}, mask, Ks, 1, Vs, 1, 0, j + 1, copy, NSL);
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        barrier_lds();
+    };
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    // Unmasked steps 0 .. jm-1; a causal workgroup's last four steps (from
+    // q0 / BK - 1, an odd step, on) handle its diagonal tiles and mask.
+    const int jm = CAUSAL ? q0 / BK - 1 : nK - 1;
+    int j = 0;
+    for (; j + 2 <= jm; j += 2) {
+        step(j, Even{}, False{});
+        step(j + 1, Odd{}, False{});
+    }
+    if (j < jm) step(j++, Even{}, False{});
+    if constexpr (CAUSAL) {
+        step(j, Odd{}, True{});
+        step(j + 1, Even{}, True{});
+        step(j + 2, Odd{}, True{});
+        step(j + 3, Even{}, True{});
+    }
+    // tail: tile nK-1's P V and its block-1 softmax
+    {
+        const __bf16* Vs = Vring + ((nK - 1) & 1) * T::VTILE;
+        region(False{}, std::integral_constant<bool, CAUSAL>{}, Kring, 0, Vs, 0, 1, nK - 1, no_copy, 0);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const bf16x8 vt = pv_op(Vs, 2 + i / DB, i % DB);
+            oacc[0][i % DB] = mfma32(vt, Pb[0][2 + i / DB], oacc[0][i % DB]);
+            oacc[1][i % DB] = mfma32(vt, Pb[1][2 + i / DB], oacc[1][i % DB]);
+        }
+    }
+    // Every probability is at most its lane's sum. The sum of 2 nK blocks passes
+    // whenever each block's sum is at most 2^(slack-1), the bound fwd_body tests
+    // per tile, and passing caps every probability at 2^(slack-1) * 2 nK: P stays
+    // exact in bf16 and O and l far from overflow.
+    float l[2];
+    bool bad = false;
+    const float bound = exp2f(a.max_slack - 1.0f) * (float)(2 * nK);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        l[r] = (l4[r][0] + l4[r][1]) + (l4[r][2] + l4[r][3]);
+        bad |= !(l[r] <= bound);  // also a NaN or an infinity
+    }
+    if (__any(bad) && lane == 0) *(volatile int*)flag = 1;
+    barrier_lds();
+    if (*(volatile int*)flag) return false;
+
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int qrow = qrow0 + 128 * r;
+        const float lt = halves_sum(l[r]);
+        const float inv = 1.0f / lt;
+        uint16_t* op = a.o + (qrows + qrow) * DV;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = db * 32 + 8 * g4 + 4 * h;
+                *(bf16x4*)(op + d) = pack4(oacc[r][db][4 * g4] * inv, oacc[r][db][4 * g4 + 1] * inv,
+                                           oacc[r][db][4 * g4 + 2] * inv, oacc[r][db][4 * g4 + 3] * inv);
+            }
+        if (h == 0) a.lse[qrows + qrow] = (m[r] + log2f(lt)) * 0.69314718055994531f;
+    }
+    return true;
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(kF1Threads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fwd1_kernel(FwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+    const int nQ = a.S / kFwdBQ;
+    int b, hq, qt;
+    decode_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
+    const int q0 = qt * kFwdBQ;
+    if (qt >= a.precise_tiles && fwd1_fast<CAUSAL>(a, smem, b, hq, q0)) return;
+    fwd1_careful<CAUSAL>(a, smem, b, hq, q0);
+}
+
 template <int D, int DV, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
     // Rows that see at most 128 keys take the exact P V product: tile 0 of a
@@ -570,6 +1061,15 @@ hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
         return hipGetLastError();
     }
     a.precise_tiles = (CAUSAL || a.S <= 128) ? 1 : 0;
+    // 128-wide heads with the slack on and whole 256-row tiles: fwd1_kernel (its
+    // own exact body covers the first causal tile). Otherwise fwd_kernel.
+    if constexpr (D == 128 && DV == 128) {
+        if (a.max_slack >= 1.0f && a.S % kFwdBQ == 0 && a.S > 128) {
+            hipLaunchKernelGGL((fwd1_kernel<CAUSAL>), dim3((unsigned)((long long)a.B * a.Hq * nQ)), dim3(kF1Threads),
+                               F1Tile::LDS_BYTES, stream, a);
+            return hipGetLastError();
+        }
+    }
     const long long blocks = (long long)a.B * a.Hq * nQ;
     hipLaunchKernelGGL((fwd_kernel<D, DV, CAUSAL>), dim3((unsigned)blocks), dim3(kFwdThreads), lds, stream, a);
     return hipGetLastError();
@@ -584,6 +1084,8 @@ template <int D, int DV>
 hipError_t setup_pair() {
     hipError_t e = set_lds(fwd_kernel<D, DV, false>, fwd_lds_bytes<D, DV>());
     if (!e) e = set_lds(fwd_kernel<D, DV, true>, fwd_lds_bytes<D, DV>());
+    if (!e && D == 128 && DV == 128) e = set_lds(fwd1_kernel<false>, F1Tile::LDS_BYTES);
+    if (!e && D == 128 && DV == 128) e = set_lds(fwd1_kernel<true>, F1Tile::LDS_BYTES);
     return e ? e : set_lds(fwd_win_kernel<D, DV>, fwd_lds_bytes<D, DV>());
 }
 

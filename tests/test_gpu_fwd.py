@@ -130,6 +130,34 @@ def test_zero_query_gives_prefix_mean():
                  tol_max=TOL_LSE, tol_mean=TOL_LSE)
 
 
+@pytest.mark.parametrize("mode", ["mild", "spike", "ramp"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_maximum_of_the_first_tile(mode, causal):
+    """128-wide heads with S a multiple of 256 take the kernel whose loop keeps each
+    row's maximum from its first key tile and never rescales O. Later keys far above
+    it (spike: about 40 log2 units; ramp: key norms growing fourfold) push a lane's
+    probability sum past its bound, and the workgroup recomputes its rows on the exact
+    path; a mild spike (5 to 8 units) stays on the loop with probabilities up to
+    about 2^8. Both must match the definition."""
+    from flashattention_tiled_attention_amd.inputs import bf16_bits, bf16_to_f32
+    B, Hq, Hkv, S, D = 1, 4, 2, 768, 128
+    print("case mode=%s causal=%d S=%d" % (mode, causal, S), flush=True)
+    q, k, v = qkv(B, Hq, Hkv, S, D, 13)
+    qf, kf = bf16_to_f32(q), bf16_to_f32(k)
+    if mode == "ramp":
+        kf = kf * (1.0 + 3.0 * np.arange(S, dtype=np.float32) / S)[None, None, :, None]
+    else:
+        qf = qf + 1.0
+        for t in (300, 650):
+            kf[:, :, t, :] = 2.5 if mode == "spike" else 0.6
+    q, k, v = bf16_bits(qf), bf16_bits(kf), bf16_bits(bf16_to_f32(v) * 0.5)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal, scale)
+    assert_close(o, o_ref, "O")
+    assert_close(lse, lse_ref, "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)
+
+
 @pytest.mark.parametrize("mode", ["ramp", "spike"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 100), (True, 300)])
