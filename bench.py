@@ -139,7 +139,8 @@ def side_configs(n_rep):
             mean, med, mn = time_calls(fn, n_rep, stream)
             ms[kname] = mean
             tf = pf[kname] * pairs / (mean * 1e-3) / 1e12
-            entry[kname] = {"ms": round(mean, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+            entry[kname] = {"kernel": launched_kernel(kname, D, D, S, causal, 0, scale),
+                            "ms": round(mean, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
                             "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         entry["fwd"] = {k: entry["fwd_kernel"][k] for k in ("ms", "tflops", "frac_of_peak")}
         if with_bwd:
@@ -269,9 +270,32 @@ def cpu_baseline_sparse(q, k, v, dout, idx, cfg, target_s, with_bwd):
 _CSRC = "flashattention_tiled_attention_amd/csrc/"
 KERNEL_SOURCES = {   # every source a kernel's machine code depends on
     "fwd_kernel": [_CSRC + "attn_fwd.hip", _CSRC + "device.h", _CSRC + "kernels.h"],
+    "fwd1_kernel": [_CSRC + "attn_fwd.hip", _CSRC + "device.h", _CSRC + "kernels.h"],
     "dq_kernel": [_CSRC + "attn_bwd.hip", _CSRC + "device.h", _CSRC + "kernels.h"],
     "dkv_kernel": [_CSRC + "attn_bwd.hip", _CSRC + "device.h", _CSRC + "kernels.h"],
 }
+
+
+def launched_kernel(role, D, Dv, S, causal, window, scale, sparse=False):
+    """Name of the kernel an entry point launches for a dense workload, by the launchers'
+    rules: the forward takes fwd1_kernel for 128-wide heads with the running-maximum
+    slack on (|scale| sqrt(D) <= 2) and S a multiple of 256; a window takes the window
+    kernels; dK/dV takes dkv1_kernel when all heads are 64 wide. role is the timing
+    label (fwd_kernel, dq_kernel or dkv_kernel; bwd_kernels for a backward entry point
+    timed as a whole, which launches several)."""
+    if sparse:
+        return "sparse_fwd_kernel" if role == "fwd_kernel" else role
+    if role == "fwd_kernel":
+        if window:
+            return "fwd_win_kernel"
+        if D == 128 and Dv == 128 and abs(scale) * math.sqrt(D) <= 2.0 and S % 256 == 0 and S > 128:
+            return "fwd1_kernel"
+        return "fwd_kernel"
+    if role == "dq_kernel":
+        return "dq_win_kernel" if window else "dq_kernel"
+    if role == "dkv_kernel":
+        return "dkv1_kernel" if D == 64 and Dv == 64 else "dkv_kernel"
+    return role
 
 
 def source_sha(kernel):
@@ -289,7 +313,7 @@ def hbm_traffic(kernel):
     WRITE_SIZE, each scaled by the factor a plain copy of known size gives), or None when
     the record is missing or was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_llama8b_s4096.txt" % kernel)
-    if not os.path.exists(path):
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
@@ -479,21 +503,22 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     dominant = max(kernel_ms, key=kernel_ms.get)
+    launched = {k: launched_kernel(k, D, Dv, S, causal, W, scale, sparse) for k in kernel_ms}
     dom_flops = pf[dominant] * pairs
     achieved = dom_flops / (kernel_ms[dominant] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+    roofline = {"bound": "mfma", "kernel": launched[dominant], "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": hbm_traffic(dominant) if headline else None,
+                "traffic": hbm_traffic(launched[dominant]) if headline else None,
                 "flop_per_launch": dom_flops, "launch_ms": round(kernel_ms[dominant], 4)}
 
     kernels = {}
     apf = algorithmic_pair_flops(D, Dv)
     for kname, ms in kernel_ms.items():
         fl = pf[kname] * pairs
-        kernels[kname] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+        kernels[kname] = {"kernel": launched[kname], "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                           "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                           "ms_median": round(kernel_stats[kname][1], 4), "ms_min": round(kernel_stats[kname][2], 4),
-                          "calls": n_rep, "hbm_bytes": hbm_traffic(kname) if headline else None}
+                          "calls": n_rep, "hbm_bytes": hbm_traffic(launched[kname]) if headline else None}
         if not sparse and kname in apf:
             # the kernel's share of the algorithmic work: below its executed work only
             # where it recomputes products another launch also computes (dQ's S and dP)

@@ -1,5 +1,6 @@
 """Host logic of bench.py, without a GPU: the one-GPU refusal, the FLOP convention and
 the HBM traffic records it attaches to the roofline."""
+import math
 import os
 import shutil
 import subprocess
@@ -62,7 +63,7 @@ def _copy_tree(tmp_path, kernel):
     return tmp_path / ("profiles/hbm_traffic_%s_llama8b_s4096.txt" % kernel)
 
 
-@pytest.mark.parametrize("kernel", ["fwd_kernel", "dq_kernel", "dkv_kernel"])
+@pytest.mark.parametrize("kernel", ["fwd1_kernel", "dq_kernel", "dkv_kernel"])
 def test_traffic_record_follows_the_source_hash(tmp_path, monkeypatch, kernel):
     rec = _copy_tree(tmp_path, kernel)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
@@ -106,3 +107,24 @@ def test_cpu_baseline_counts_whole_groups(causal, window):
     expect = B * Hq * pairs * pf["fwd"] + B * Hkv * (Hq // Hkv) * pairs * (pf["fwd"] + pf["dkv_kernel"])
     assert r["flop"] == pytest.approx(expect, rel=1e-12)
     assert r["kind"] == "oracle" and r["cores"] >= 1
+
+
+def test_launched_kernel_follows_the_launchers():
+    """The kernel names bench.py reports per entry point follow the launchers' rules
+    (attn_fwd.hip launch_fwd_t, attn_bwd.hip): 128-wide heads with the slack on and
+    whole 256-row tiles take fwd1_kernel; peaked scales, ragged S and 64-wide heads
+    take fwd_kernel; windows take the window kernels."""
+    import bench
+    s128 = 1 / math.sqrt(128)
+    assert bench.launched_kernel("fwd_kernel", 128, 128, 4096, True, 0, s128) == "fwd1_kernel"
+    assert bench.launched_kernel("fwd_kernel", 128, 128, 4096, False, 0, s128) == "fwd1_kernel"
+    assert bench.launched_kernel("fwd_kernel", 128, 128, 4000, True, 0, s128) == "fwd_kernel"
+    assert bench.launched_kernel("fwd_kernel", 128, 128, 128, False, 0, s128) == "fwd_kernel"
+    assert bench.launched_kernel("fwd_kernel", 128, 128, 4096, True, 0, 0.5) == "fwd_kernel"
+    assert bench.launched_kernel("fwd_kernel", 128, 64, 4096, True, 0, s128) == "fwd_kernel"
+    assert bench.launched_kernel("fwd_kernel", 64, 64, 2048, False, 0, 0.125) == "fwd_kernel"
+    assert bench.launched_kernel("fwd_kernel", 128, 128, 4096, True, 512, s128) == "fwd_win_kernel"
+    assert bench.launched_kernel("dq_kernel", 128, 128, 4096, True, 512, s128) == "dq_win_kernel"
+    assert bench.launched_kernel("dkv_kernel", 64, 64, 2048, False, 0, 0.125) == "dkv1_kernel"
+    assert bench.launched_kernel("dkv_kernel", 128, 128, 4096, True, 0, s128) == "dkv_kernel"
+    assert bench.launched_kernel("fwd_kernel", 128, 128, 4096, True, 4, s128, sparse=True) == "sparse_fwd_kernel"
