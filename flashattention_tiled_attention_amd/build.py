@@ -23,13 +23,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
-# Per-source flags. fwd1_kernel runs one wave per SIMD, so it may use 512 registers;
-# for such kernels the compiler otherwise puts every MFMA accumulator in AGPRs, and
-# the softmax then reads each score out of them with an extra instruction. This flag
-# makes it keep MFMA results in VGPRs (spilling cold values to AGPRs). It changes
-# no other kernel of that file: kernels with two waves per SIMD (256 registers)
-# already get that form.
-SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# Per-source flags. fwd1_kernel and dkv1_kernel run one wave per SIMD, so they may use
+# 512 registers; for such kernels the compiler otherwise puts every MFMA accumulator in
+# AGPRs, and the vector code then moves each value it reads or writes in and out of
+# them with extra instructions. This flag makes it keep MFMA results in VGPRs (spilling
+# cold values to AGPRs). It changes no other kernel of those files: kernels with two
+# waves per SIMD (256 registers) already get that form.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+SOURCE_FLAGS = {"attn_fwd.hip": _VGPR_FORM, "attn_bwd.hip": _VGPR_FORM}
 
 
 def _compile(src, obj, extra):
