@@ -64,6 +64,26 @@ def test_scales(scale):
     check_full(1, 2, 2, 130, 64, False, seed=4, scale=scale)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [0.0, -0.0884, 0.0884])
+def test_scales_one_wave_forward(scale, causal):
+    """Scales the 64-rows-per-wave forward takes (128-wide heads, S a multiple of 256,
+    |scale| sqrt(D) <= 2): zero (every probability equal) and negative (Q's sign flipped
+    on load)."""
+    check_full(1, 4, 2, 512, 128, causal, seed=5, scale=scale)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,causal", [
+    (1, 2, 1, 256, False),    # one query tile, four key tiles
+    (1, 2, 1, 256, True),     # only the first causal tile: the exact body alone
+    (2, 8, 2, 768, False),    # (B*Hkv) % 8 != 0: one group after another on each XCD
+    (1, 16, 8, 512, False),   # groups dealt round-robin over the 8 XCDs
+    (3, 4, 1, 1280, True),    # five query tiles, G = 4
+])
+def test_one_wave_forward_shapes(B, Hq, Hkv, S, causal):
+    check_full(B, Hq, Hkv, S, 128, causal, seed=B * 7 + S)
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_seeds_small(seed):
     check_full(1, 8, 2, 512, 128, True, seed=seed)
