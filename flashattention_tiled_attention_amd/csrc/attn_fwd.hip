@@ -599,6 +599,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_win_kernel(FwdArgs a) {
 constexpr int kF1Waves = 4;
 constexpr int kF1Threads = 64 * kF1Waves;
 constexpr int kF1BK = 64;  // keys per LDS tile
+constexpr int kF1Rows = 2; // 32-row blocks per wave
 
 struct F1Tile {
     static constexpr int D = 128, DV = 128;
@@ -656,7 +657,7 @@ __device__ __forceinline__ void f1_mask(f32x16& s, int k0, int qrow, int h) {
 // a time. Per key tile all waves copy K and V into slot 0 of the ring; then the
 // scores, the row maximum moved as fwd_body moves it, the probabilities split
 // into bf16 high parts and remainders, and the P V product on both.
-template <bool CAUSAL>
+template <bool CAUSAL, int NR>
 __device__ __forceinline__ void fwd1_careful(const FwdArgs& a, __bf16* smem, int b, int hq, int q0) {
     using T = F1Tile;
     constexpr int D = T::D, DV = T::DV, BK = kF1BK, DK = D / 16, DB = DV / 32, NT = BK / 16;
@@ -676,7 +677,7 @@ __device__ __forceinline__ void fwd1_careful(const FwdArgs& a, __bf16* smem, int
     const __bf16* Vs = smem + T::KTILE;
     const uint32_t kdst = lds_addr_of(smem) + wave * KC::N * 1024;
     const uint32_t vdst = lds_addr_of(smem + T::KTILE) + wave * VC::N * 1024;
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NR; ++r) {
         const int row0 = q0 + 128 * r + 32 * wave;
         const int qrow = row0 + l32;
         bf16x8 qf[DK];
@@ -771,7 +772,7 @@ __device__ __forceinline__ void fwd1_careful(const FwdArgs& a, __bf16* smem, int
 
 // Pipelined body; returns false (workgroup-uniform, nothing written) when some
 // wave's probabilities left the bound, true once O and lse are written.
-template <bool CAUSAL>
+template <bool CAUSAL, int NR>
 __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b, int hq, int q0) {
     using T = F1Tile;
     constexpr int D = T::D, DV = T::DV, BK = kF1BK;
@@ -798,9 +799,9 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
     const float c = a.scale_log2;
     int* const flag = (int*)((char*)smem + T::RING_BYTES);
 
-    bf16x8 qf[2][DK];
+    bf16x8 qf[NR][DK];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NR; ++r) {
         const u32x4* src = (const u32x4*)(a.q + (qrows + qrow0 + 128 * r) * D + 8 * h);
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
@@ -811,7 +812,7 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
     }
     // Tiles of the workgroup; a causal one masks tiles from q0 / BK on (its
     // first row's tile; earlier tiles are visible to all of its rows).
-    const int nK = CAUSAL ? q0 / BK + kFwdBQ / BK : S / BK;
+    const int nK = CAUSAL ? q0 / BK + 128 * NR / BK : S / BK;
     __bf16* const Kring = smem;
     __bf16* const Vring = smem + 2 * T::KTILE;
     const uint32_t kbase = lds_addr_of(Kring) + wave * KC::N * 1024;
@@ -826,19 +827,19 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
                              vbase + (uint32_t)(vs * T::VTILE * 2 + (k - KC::N) * 1024));
     };
 
-    f32x16 oacc[2][DB];
+    f32x16 oacc[NR][DB];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[r][db] = zero16();
     // m: each row's reference maximum; l4: four partial sums of this lane's share
     // of its probabilities, carried through the loop
-    float m[2], l4[2][4];
+    float m[NR], l4[NR][4];
 
     // Sb[r][kb]: scores of key block kb of the current tile for row block r;
     // Pb[r][t]: the bf16 probabilities of its 16-key step t.
-    f32x16 Sb[2][2];
-    bf16x8 Pb[2][NT];
+    f32x16 Sb[NR][2];
+    bf16x8 Pb[NR][NT];
     auto qk_op = [&](const __bf16* Ks, int kb, int dk) { return lds_read8(Ks + ln.koff[dk] + kb * 32 * D); };
     auto pv_op = [&](const __bf16* Vs, int t, int db) {
         return concat(lds_read_tr(Vs + ln.voff[0][db] + 16 * t * DV), lds_read_tr(Vs + ln.voff[1][db] + 16 * t * DV));
@@ -854,14 +855,14 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
         constexpr bool MASK = decltype(mask)::value;
         if (MASK) {
 #pragma unroll
-            for (int r = 0; r < 2; ++r) f1_mask(Sb[r][sb], jt * BK + 32 * sb, qrow0 + 128 * r, h);
+            for (int r = 0; r < NR; ++r) f1_mask(Sb[r][sb], jt * BK + 32 * sb, qrow0 + 128 * r, h);
         }
-        float pe[2][16];
-        uint32_t pw[2][8];
+        float pe[NR][16];
+        uint32_t pw[NR][8];
         bf16x8 kr[DK], vr[NPV];
         if (WITH_QK) {
-            Sb[0][kb] = zero16();
-            Sb[1][kb] = zero16();
+#pragma unroll
+            for (int r = 0; r < NR; ++r) Sb[r][kb] = zero16();
             kr[0] = qk_op(Ks, kb, 0);
         }
         vr[0] = pv_op(Vs, 2 * pb, 0);
@@ -874,15 +875,16 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
             // the P V product first: its operand was read after the K operand, so
             // the one wait for it covers both
             if (i < NPV) {
-                oacc[0][i % DB] = mfma32(vr[i], Pb[0][2 * pb + i / DB], oacc[0][i % DB]);
-                oacc[1][i % DB] = mfma32(vr[i], Pb[1][2 * pb + i / DB], oacc[1][i % DB]);
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    oacc[r][i % DB] = mfma32(vr[i], Pb[r][2 * pb + i / DB], oacc[r][i % DB]);
             }
             if (WITH_QK && i < DK) {
-                Sb[0][kb] = mfma32(kr[i], qf[0][i], Sb[0][kb]);
-                Sb[1][kb] = mfma32(kr[i], qf[1][i], Sb[1][kb]);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) Sb[r][kb] = mfma32(kr[i], qf[r][i], Sb[r][kb]);
             }
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
+            for (int r = 0; r < NR; ++r) {
 #pragma unroll
                 for (int u = 0; u < EPS; ++u) {
                     const int e = EPS * i + u;
@@ -900,7 +902,7 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2)
                 Pb[r][2 * sb + t2] = __builtin_bit_cast(
@@ -920,7 +922,7 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
     wait_copies();
     barrier_lds();
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NR; ++r) {
         Sb[r][0] = zero16();
         Sb[r][1] = zero16();
     }
@@ -929,11 +931,11 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const bf16x8 kf = qk_op(Kring, kb, dk);
-            Sb[0][kb] = mfma32(kf, qf[0][dk], Sb[0][kb]);
-            Sb[1][kb] = mfma32(kf, qf[1][dk], Sb[1][kb]);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) Sb[r][kb] = mfma32(kf, qf[r][dk], Sb[r][kb]);
         }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NR; ++r) {
         float mx = fmaxf(Sb[r][0][0], Sb[r][1][0]);
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(Sb[r][0][e], Sb[r][1][e]));
@@ -982,10 +984,11 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
     }
     if (j < jm) step(j++, Even{}, False{});
     if constexpr (CAUSAL) {
-        step(j, Odd{}, True{});
-        step(j + 1, Even{}, True{});
-        step(j + 2, Odd{}, True{});
-        step(j + 3, Even{}, True{});
+#pragma unroll
+        for (int t = 0; t < NR; ++t, j += 2) {
+            step(j, Odd{}, True{});
+            step(j + 1, Even{}, True{});
+        }
     }
     // tail: tile nK-1's P V and its block-1 softmax
     {
@@ -994,19 +997,19 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             const bf16x8 vt = pv_op(Vs, 2 + i / DB, i % DB);
-            oacc[0][i % DB] = mfma32(vt, Pb[0][2 + i / DB], oacc[0][i % DB]);
-            oacc[1][i % DB] = mfma32(vt, Pb[1][2 + i / DB], oacc[1][i % DB]);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) oacc[r][i % DB] = mfma32(vt, Pb[r][2 + i / DB], oacc[r][i % DB]);
         }
     }
     // Every probability is at most its lane's sum. The sum of 2 nK blocks passes
     // whenever each block's sum is at most 2^(slack-1), the bound fwd_body tests
     // per tile, and passing caps every probability at 2^(slack-1) * 2 nK: P stays
     // exact in bf16 and O and l far from overflow.
-    float l[2];
+    float l[NR];
     bool bad = false;
     const float bound = exp2f(a.max_slack - 1.0f) * (float)(2 * nK);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NR; ++r) {
         l[r] = (l4[r][0] + l4[r][1]) + (l4[r][2] + l4[r][3]);
         bad |= !(l[r] <= bound);  // also a NaN or an infinity
     }
@@ -1015,7 +1018,7 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
     if (*(volatile int*)flag) return false;
 
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NR; ++r) {
         const int qrow = qrow0 + 128 * r;
         const float lt = halves_sum(l[r]);
         const float inv = 1.0f / lt;
@@ -1033,16 +1036,20 @@ __device__ __forceinline__ bool fwd1_fast(const FwdArgs& a, __bf16* smem, int b,
     return true;
 }
 
-template <bool CAUSAL>
-__global__ void __launch_bounds__(kF1Threads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NR row blocks per wave: 2 (one wave per SIMD, 256 rows per workgroup) or 1 (two
+// workgroups of 128 rows per CU, two waves per SIMD).
+template <bool CAUSAL, int NR>
+__global__ void __launch_bounds__(kF1Threads, 3 - NR) __attribute__((amdgpu_waves_per_eu(3 - NR, 3 - NR)))
 fwd1_kernel(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
-    const int nQ = a.S / kFwdBQ;
+    constexpr int BQ = 128 * NR;
+    const int nQ = a.S / BQ;
     int b, hq, qt;
     decode_item(blockIdx.x, nQ, CAUSAL ? nQ - 1 : 0, a.B, a.Hkv, a.G, CAUSAL, b, hq, qt);
-    const int q0 = qt * kFwdBQ;
-    if (qt >= a.precise_tiles && fwd1_fast<CAUSAL>(a, smem, b, hq, q0)) return;
-    fwd1_careful<CAUSAL>(a, smem, b, hq, q0);
+    const int q0 = qt * BQ;
+    // rows below precise_tiles * 256 (the first 256 rows of a causal problem) take the exact body
+    if (q0 >= a.precise_tiles * kFwdBQ && fwd1_fast<CAUSAL, NR>(a, smem, b, hq, q0)) return;
+    fwd1_careful<CAUSAL, NR>(a, smem, b, hq, q0);
 }
 
 template <int D, int DV, bool CAUSAL>
@@ -1065,8 +1072,9 @@ hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
     // own exact body covers the first causal tile). Otherwise fwd_kernel.
     if constexpr (D == 128 && DV == 128) {
         if (a.max_slack >= 1.0f && a.S % kFwdBQ == 0 && a.S > 128) {
-            hipLaunchKernelGGL((fwd1_kernel<CAUSAL>), dim3((unsigned)((long long)a.B * a.Hq * nQ)), dim3(kF1Threads),
-                               F1Tile::LDS_BYTES, stream, a);
+            constexpr int NR = kF1Rows;
+            hipLaunchKernelGGL((fwd1_kernel<CAUSAL, NR>), dim3((unsigned)((long long)a.B * a.Hq * (a.S / (128 * NR)))),
+                               dim3(kF1Threads), F1Tile::LDS_BYTES, stream, a);
             return hipGetLastError();
         }
     }
@@ -1084,8 +1092,8 @@ template <int D, int DV>
 hipError_t setup_pair() {
     hipError_t e = set_lds(fwd_kernel<D, DV, false>, fwd_lds_bytes<D, DV>());
     if (!e) e = set_lds(fwd_kernel<D, DV, true>, fwd_lds_bytes<D, DV>());
-    if (!e && D == 128 && DV == 128) e = set_lds(fwd1_kernel<false>, F1Tile::LDS_BYTES);
-    if (!e && D == 128 && DV == 128) e = set_lds(fwd1_kernel<true>, F1Tile::LDS_BYTES);
+    if (!e && D == 128 && DV == 128) e = set_lds(fwd1_kernel<false, kF1Rows>, F1Tile::LDS_BYTES);
+    if (!e && D == 128 && DV == 128) e = set_lds(fwd1_kernel<true, kF1Rows>, F1Tile::LDS_BYTES);
     return e ? e : set_lds(fwd_win_kernel<D, DV>, fwd_lds_bytes<D, DV>());
 }
 
