@@ -340,16 +340,23 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, __bf16* smem, int b, 
             const int base = j * BK + 4 * h;
             const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - base;
             const int lo = W > 0 ? qrow - W + 1 - base : -(1 << 30);
-            // -inf is added, not selected: adding the bit pattern 0xff800000 (or
-            // +0.0) under a sign-extended mask keeps the 2 * BK/2 comparisons out
-            // of the scalar registers, which a select would fill with lane masks
+            // -inf goes in under a sign-extended mask, not through a compare and
+            // select: that keeps the 2 * BK/2 comparisons out of the scalar
+            // registers, which lane masks would fill. With a causal or window edge
+            // it goes in by a bitwise select (hide_if), which also hides a NaN score
+            // of a key the row must not see; without one the only hidden keys are
+            // the ragged end's, copies of key S-1 that every row sees, and adding
+            // -inf (or +0.0) is enough.
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
                     const int hidden = ((lim - off) | (off - lo)) >> 31;  // all ones iff off > lim or off < lo
-                    sc[kb][r] += __int_as_float(hidden & (int)0xff800000u);
+                    if constexpr (CAUSAL)
+                        sc[kb][r] = hide_if(hidden, sc[kb][r]);
+                    else
+                        sc[kb][r] += __int_as_float(hidden & (int)0xff800000u);
                 }
         }
         // Past a wave's first tile the maximum is usually not needed: if every
@@ -642,14 +649,15 @@ struct F1Lane {
     }
 };
 
-// Adds -inf to the scores of keys past this lane's query row: element e of a
-// 32-key block starting at key k0 holds key k0 + 8 (e / 4) + 4 h + e % 4.
+// Sets the scores of keys past this lane's query row to -inf (a bitwise select, so
+// that a NaN score of a hidden key does not reach the row): element e of a 32-key
+// block starting at key k0 holds key k0 + 8 (e / 4) + 4 h + e % 4.
 __device__ __forceinline__ void f1_mask(f32x16& s, int k0, int qrow, int h) {
     const int lim = qrow - k0 - 4 * h;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int off = 8 * (e >> 2) + (e & 3);
-        s[e] += __int_as_float(((lim - off) >> 31) & (int)0xff800000u);
+        s[e] = hide_if((lim - off) >> 31, s[e]);  // all ones iff off > lim
     }
 }
 

@@ -229,4 +229,14 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// -inf where `mask` is all ones, else s, as one bitwise select (v_bfi_b32); mask is a
+// sign-extended comparison (0 or all ones). The empty asm hides that origin from the
+// compiler, which would otherwise turn the select back into a compare and a lane-mask
+// select and fill the scalar registers with one 64-bit mask per score. Unlike adding
+// -inf, the select also replaces a NaN score.
+__device__ __forceinline__ float hide_if(int mask, float s) {
+    asm("" : "+v"(mask));
+    return __int_as_float((mask & (int)0xff800000u) | (~mask & __float_as_int(s)));
+}
+
 }  // namespace attn

@@ -150,6 +150,34 @@ def test_zero_query_gives_prefix_mean():
                  tol_max=TOL_LSE, tol_mean=TOL_LSE)
 
 
+@pytest.mark.parametrize("D,S", [(128, 512), (64, 300)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_nan_key_reaches_exactly_the_rows_that_see_it(D, S, causal):
+    """A NaN in one key makes every score against it NaN, so softmax gives NaN O and lse
+    on exactly the rows that see that key (all rows; with a causal mask those at or
+    past it) and leaves the other rows as they were. For 128-wide heads the NaN fails
+    the one-wave forward's bound test, and the workgroup's rows are made again on the
+    exact path."""
+    from flashattention_tiled_attention_amd.inputs import bf16_bits, bf16_to_f32
+    B, Hq, Hkv, t = 1, 4, 2, 100
+    print("case nan key D=%d S=%d causal=%d" % (D, S, causal), flush=True)
+    q, k, v = qkv(B, Hq, Hkv, S, D, 17)
+    kf = bf16_to_f32(k)
+    kf[0, 1, t, 5] = np.nan          # key t of kv head 1: query heads 2 and 3 see it
+    k = bf16_bits(kf)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal, scale)
+    rows = np.arange(S)
+    sees = np.zeros((B, Hq, S), bool)
+    sees[0, 2:] = (rows >= t) if causal else True
+    assert np.array_equal(np.isnan(lse_ref), sees), "the oracle's NaN rows"
+    assert np.array_equal(np.isnan(lse), sees), "NaN lse on exactly the rows that see the key"
+    assert np.array_equal(np.isnan(o).all(axis=-1), sees) and not np.isnan(o[~sees]).any(), "NaN O rows"
+    assert_close(o[~sees], o_ref[~sees], "O")
+    assert_close(lse[~sees], lse_ref[~sees], "lse", tol_max=TOL_LSE, tol_mean=TOL_LSE)
+
+
 @pytest.mark.parametrize("mode", ["mild", "spike", "ramp"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_reference_maximum_of_the_first_tile(mode, causal):
